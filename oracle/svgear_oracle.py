@@ -1,0 +1,361 @@
+"""Plain fp64 CPU oracle for the SVG-EAR sparse-attention hot path.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check of the package entry
+point and the CPU-baseline leg of the benchmark may import or run this module.
+It shares no code with the HIP path and never imports it.
+
+Everything is numpy float64, one (batch, head) slice at a time, written for
+reading rather than speed.  The method is an approximation, so the oracle
+follows the pages' steps in order:
+
+  1. ``lloyd``    k-means of Q (C_q clusters) and of K (C_k clusters) from a
+                  given start (SVG2 summary, "Semantic-Aware Permutation via
+                  k-Means Clustering"; centroid cache in "Efficient
+                  System-Algorithm Co-Design").
+  2. ``permute``  cluster-contiguous order, K and V sharing one permutation
+                  (SVG2 summary, "The permutation operation and its
+                  mathematical validity").
+  3. ``means``    per-cluster means of Q, K and V (SVG-EAR task page, "What
+                  the agent has to build": one routine averages each cluster).
+  4. ``route``    the probe error of every (query cluster, key cluster) block,
+                  divided by its cost |Q_i| |K_j|, then a greedy fill to the
+                  density budget (FrontierCS blog on SVG-EAR, the probe formula
+                  and the budget paragraph; Pith review, "What carries the
+                  argument").
+  5. ``attend``   selected blocks exactly, every skipped non-empty key cluster
+                  as one centroid key whose score is raised by ln n_j with the
+                  cluster's mean value (FrontierCS blog, toy example: weight
+                  n e^{s_bar}; SVG-EAR task page, step 3 of the walkthrough),
+                  output in original token order.
+
+Readings taken where the pages are silent (each also listed in the design
+notes): squared L2 distance with ties to the lowest index; empty k-means
+clusters keep their centroid; stable within-cluster order; the probe error is
+stabilised by the row maximum M_i of the probe scores (the per-row ranking is
+unchanged by that common factor); the budget is rho * N_k keys per query
+cluster and the block that crosses it is included; ties in ratio break to the
+lower key-cluster index; compensation uses each query token against the exact
+means of the current assignment; no variance term.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F64 = np.float64
+
+
+# --------------------------------------------------------------------------
+# 1. k-means (Lloyd rounds)
+# --------------------------------------------------------------------------
+def sqdist(X: np.ndarray, C: np.ndarray) -> np.ndarray:
+    """Squared Euclidean distances D[n, c] = ||x_n - c_c||^2 in fp64.
+
+    Euclidean distance on the activation vectors is the clustering metric of
+    the SVG2 summary ("What gets clustered and why")."""
+    X = np.asarray(X, F64)
+    C = np.asarray(C, F64)
+    xx = np.einsum("nd,nd->n", X, X)
+    cc = np.einsum("cd,cd->c", C, C)
+    D = xx[:, None] + cc[None, :] - 2.0 * (X @ C.T)
+    return np.maximum(D, 0.0)
+
+
+def assign(X: np.ndarray, C: np.ndarray) -> np.ndarray:
+    """Label of each row = index of its nearest centroid, ties to the lowest index."""
+    return np.argmin(sqdist(X, C), axis=1).astype(np.int64)
+
+
+def update(X: np.ndarray, labels: np.ndarray, C_old: np.ndarray) -> np.ndarray:
+    """New centroid = mean of its members; an empty cluster keeps its old centroid."""
+    X = np.asarray(X, F64)
+    C = np.array(C_old, F64, copy=True)
+    k = C.shape[0]
+    counts = np.bincount(labels, minlength=k)
+    sums = np.zeros_like(C)
+    np.add.at(sums, labels, X)
+    nz = counts > 0
+    C[nz] = sums[nz] / counts[nz, None]
+    return C
+
+
+def lloyd(X: np.ndarray, C0: np.ndarray, iters: int):
+    """``iters`` rounds of (assign, update) from the start C0.
+
+    Cold starts come from the caller; warm starts are the previous denoising
+    step's centroids (SVG2 summary, centroid cache: 1-3 rounds from the cached
+    centroids instead of 100+ from k-means++).  Returns (centroids after the
+    last update, labels of the last assignment)."""
+    if iters < 1:
+        raise ValueError("iters must be >= 1")
+    C = np.array(C0, F64, copy=True)
+    labels = None
+    for _ in range(iters):
+        labels = assign(X, C)
+        C = update(X, labels, C)
+    return C, labels
+
+
+def inertia(X: np.ndarray, C: np.ndarray, labels: np.ndarray) -> float:
+    X = np.asarray(X, F64)
+    return float(((X - np.asarray(C, F64)[labels]) ** 2).sum())
+
+
+# --------------------------------------------------------------------------
+# 2. permutation
+# --------------------------------------------------------------------------
+def permute(labels: np.ndarray, C: int):
+    """Cluster-contiguous order: perm[p] = source token of slot p.
+
+    Tokens of cluster 0 come first, then cluster 1, and so on; inside a
+    cluster tokens keep their original order.  offsets[c]..offsets[c+1] is
+    cluster c's slot range (SVG2 summary: the permutation groups all tokens
+    of cluster 1 first, then cluster 2, ...)."""
+    labels = np.asarray(labels)
+    counts = np.bincount(labels, minlength=C)
+    offsets = np.zeros(C + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    # stable counting sort written out: each token goes to the next free slot
+    # of its cluster, scanning tokens in original order
+    nxt = offsets[:-1].copy()
+    perm = np.empty(labels.shape[0], dtype=np.int64)
+    for t, c in enumerate(labels):
+        perm[nxt[c]] = t
+        nxt[c] += 1
+    return perm, offsets
+
+
+# --------------------------------------------------------------------------
+# 3. means
+# --------------------------------------------------------------------------
+def means(X: np.ndarray, perm: np.ndarray, offsets: np.ndarray) -> np.ndarray:
+    """Mean of each cluster's rows; an empty cluster's mean is defined as 0."""
+    X = np.asarray(X, F64)
+    C = offsets.shape[0] - 1
+    out = np.zeros((C, X.shape[1]), F64)
+    for c in range(C):
+        lo, hi = int(offsets[c]), int(offsets[c + 1])
+        if hi > lo:
+            out[c] = X[perm[lo:hi]].mean(axis=0)
+    return out
+
+
+# --------------------------------------------------------------------------
+# 4. error-aware routing
+# --------------------------------------------------------------------------
+def probe_errors(qbar, Kp, Vp, kbar, vbar, k_offsets, scale, q_nonempty=None):
+    """Probe error e[i, j] of replacing key cluster j by its centroid, for the
+    probe q_bar_i (the mean query of cluster i).
+
+    FrontierCS blog on SVG-EAR, probe paragraph: with s_k the probe's score for
+    key k and s_bar, v_bar belonging to the key's cluster, the block's error is
+    the sum over its keys of || e^{s_bar} v_bar - e^{s_k} v_k ||^2.  Both
+    exponentials are taken relative to the row maximum M_i = max_k s_ik, which
+    scales a whole row of errors by e^{-2 M_i} and so leaves the per-row
+    ranking unchanged.  Kp, Vp are the keys/values in cluster-contiguous order.
+    Returns (e [Cq, Ck], M [Cq])."""
+    qbar = np.asarray(qbar, F64)
+    Kp = np.asarray(Kp, F64)
+    Vp = np.asarray(Vp, F64)
+    kbar = np.asarray(kbar, F64)
+    vbar = np.asarray(vbar, F64)
+    Cq, Ck = qbar.shape[0], kbar.shape[0]
+    S = scale * (qbar @ Kp.T)              # probe score of every key, [Cq, N]
+    M = S.max(axis=1)
+    sbar = scale * (qbar @ kbar.T)         # centroid score, [Cq, Ck]
+    e = np.zeros((Cq, Ck), F64)
+    for j in range(Ck):
+        lo, hi = int(k_offsets[j]), int(k_offsets[j + 1])
+        if hi == lo:
+            continue
+        a = np.exp(sbar[:, j] - M)                         # estimate weight per key
+        for c0 in range(lo, hi, 2048):                     # chunk keys to bound memory
+            c1 = min(hi, c0 + 2048)
+            b = np.exp(S[:, c0:c1] - M[:, None])           # true weight per key
+            diff = a[:, None, None] * vbar[j][None, None, :] - b[:, :, None] * Vp[c0:c1][None, :, :]
+            e[:, j] += np.einsum("ikd,ikd->i", diff, diff)
+    if q_nonempty is not None:
+        e[~q_nonempty] = 0.0
+        M = np.where(q_nonempty, M, 0.0)
+    return e, M
+
+
+def ratios(e, q_sizes, k_sizes) -> np.ndarray:
+    """Error-to-cost ratio r_ij = e_ij / (|Q_i| |K_j|), as float32.
+
+    The blog divides the error by the number of token pairs in the block; the
+    Pith review calls it the error-to-cost ratio.  Empty clusters get 0.  The
+    selection compares these float32 values."""
+    q_sizes = np.asarray(q_sizes, F64)
+    k_sizes = np.asarray(k_sizes, F64)
+    cost = q_sizes[:, None] * k_sizes[None, :]
+    r = np.zeros_like(np.asarray(e, F64))
+    nz = cost > 0
+    r[nz] = np.asarray(e, F64)[nz] / cost[nz]
+    return r.astype(np.float32)
+
+
+def budget_keys(density: float, Nk: int) -> float:
+    """Key budget per query cluster, rho * N_k, with rho read as a float32."""
+    return float(np.float32(density)) * float(Nk)
+
+
+def select_row(r_row: np.ndarray, k_sizes: np.ndarray, budget: float) -> np.ndarray:
+    """Greedy fill of one query cluster's row (Pith review, "What carries the
+    argument": highest error-to-cost blocks first, under a density budget).
+
+    Order the non-empty key clusters by (ratio descending, index ascending);
+    take a cluster while the keys already taken are below the budget, so the
+    cluster that crosses the budget is included."""
+    k_sizes = np.asarray(k_sizes)
+    cand = [j for j in range(r_row.shape[0]) if k_sizes[j] > 0]
+    cand.sort(key=lambda j: (-float(r_row[j]), j))
+    sel = np.zeros(r_row.shape[0], dtype=np.uint8)
+    taken = 0
+    for j in cand:
+        if taken >= budget:
+            break
+        sel[j] = 1
+        taken += int(k_sizes[j])
+    return sel
+
+
+def select(r: np.ndarray, q_sizes, k_sizes, density: float, Nk: int) -> np.ndarray:
+    """Routing mask [Cq, Ck]; rows of empty query clusters stay all zero."""
+    budget = budget_keys(density, Nk)
+    mask = np.zeros(r.shape, dtype=np.uint8)
+    for i in range(r.shape[0]):
+        if q_sizes[i] > 0:
+            mask[i] = select_row(r[i], k_sizes, budget)
+    return mask
+
+
+def route(qbar, q_offsets, Kp, Vp, kbar, vbar, k_offsets, scale, density):
+    """Full routing step: (float32 ratios [Cq, Ck], mask [Cq, Ck])."""
+    q_sizes = np.diff(np.asarray(q_offsets))
+    k_sizes = np.diff(np.asarray(k_offsets))
+    e, _ = probe_errors(qbar, Kp, Vp, kbar, vbar, k_offsets, scale, q_nonempty=q_sizes > 0)
+    r = ratios(e, q_sizes, k_sizes)
+    return r, select(r, q_sizes, k_sizes, density, Kp.shape[0])
+
+
+# --------------------------------------------------------------------------
+# 5. sparse attention with centroid compensation
+# --------------------------------------------------------------------------
+def attend_rows(q_rows, K, V, k_perm, k_offsets, kbar, vbar, sel_row, scale):
+    """Outputs and log-sum-exp for query rows that share one routing row.
+
+    Keys of selected clusters are attended exactly.  Each skipped non-empty
+    key cluster j enters as one key k_bar_j with score q.k_bar_j * scale +
+    ln n_j and value v_bar_j, i.e. weight n_j e^{q.k_bar_j scale} (FrontierCS
+    blog toy example; SVG-EAR task page walkthrough step 3)."""
+    q_rows = np.asarray(q_rows, F64)
+    K = np.asarray(K, F64)
+    V = np.asarray(V, F64)
+    kbar = np.asarray(kbar, F64)
+    vbar = np.asarray(vbar, F64)
+    Ck = kbar.shape[0]
+    sizes = np.diff(np.asarray(k_offsets))
+    exact_idx = [k_perm[int(k_offsets[j]):int(k_offsets[j + 1])] for j in range(Ck) if sel_row[j]]
+    exact_idx = np.concatenate(exact_idx) if exact_idx else np.zeros(0, np.int64)
+    comp = [j for j in range(Ck) if (not sel_row[j]) and sizes[j] > 0]
+    logits = [scale * (q_rows @ K[exact_idx].T)]
+    values = [V[exact_idx]]
+    if comp:
+        comp = np.asarray(comp)
+        logits.append(scale * (q_rows @ kbar[comp].T) + np.log(sizes[comp].astype(F64))[None, :])
+        values.append(vbar[comp])
+    L = np.concatenate(logits, axis=1)
+    Vall = np.concatenate(values, axis=0)
+    m = L.max(axis=1, keepdims=True)
+    w = np.exp(L - m)
+    den = w.sum(axis=1, keepdims=True)
+    out = (w @ Vall) / den
+    lse = (m + np.log(den))[:, 0]
+    return out, lse
+
+
+def attend(Q, K, V, q_perm, q_offsets, k_perm, k_offsets, kbar, vbar, mask, scale, rows=None):
+    """O [N, D] and LSE [N] in original token order (SVG2 summary: the output
+    is un-permuted back to the original order).
+
+    ``rows`` optionally restricts the work to some original token indices;
+    other outputs are left as NaN."""
+    Q = np.asarray(Q, F64)
+    N, D = Q.shape
+    O = np.full((N, D), np.nan)
+    LSE = np.full(N, np.nan)
+    want = None if rows is None else set(int(t) for t in rows)
+    Cq = q_offsets.shape[0] - 1
+    for i in range(Cq):
+        toks = q_perm[int(q_offsets[i]):int(q_offsets[i + 1])]
+        if want is not None:
+            toks = np.asarray([t for t in toks if int(t) in want], dtype=np.int64)
+        if toks.size == 0:
+            continue
+        o, l = attend_rows(Q[toks], K, V, k_perm, k_offsets, kbar, vbar, mask[i], scale)
+        O[toks] = o
+        LSE[toks] = l
+    return O, LSE
+
+
+def attend_bruteforce(Q, K, V, q_labels, k_labels, kbar, vbar, mask, scale):
+    """Tiny-N cross-check of ``attend`` with explicit loops: one logit per
+    (query, key) pair in a selected block, one per (query, skipped non-empty
+    cluster), then a plain softmax-weighted average."""
+    Q = np.asarray(Q, F64)
+    K = np.asarray(K, F64)
+    V = np.asarray(V, F64)
+    N, D = Q.shape
+    Ck = kbar.shape[0]
+    sizes = np.bincount(np.asarray(k_labels), minlength=Ck)
+    O = np.zeros((N, D))
+    for t in range(N):
+        i = int(q_labels[t])
+        logits, vals = [], []
+        for u in range(K.shape[0]):
+            if mask[i, int(k_labels[u])]:
+                logits.append(scale * float(np.dot(Q[t], K[u])))
+                vals.append(V[u])
+        for j in range(Ck):
+            if not mask[i, j] and sizes[j] > 0:
+                logits.append(scale * float(np.dot(Q[t], kbar[j])) + np.log(float(sizes[j])))
+                vals.append(np.asarray(vbar[j], F64))
+        mx = max(logits)
+        w = np.array([np.exp(s - mx) for s in logits])
+        O[t] = (w[:, None] * np.array(vals)).sum(0) / w.sum()
+    return O
+
+
+# --------------------------------------------------------------------------
+# whole layer, one head
+# --------------------------------------------------------------------------
+def layer(q, k, v, cq0, ck0, iters, density, scale=None):
+    """All steps for one head; returns a dict of every intermediate."""
+    q = np.asarray(q, F64)
+    k = np.asarray(k, F64)
+    v = np.asarray(v, F64)
+    N, D = q.shape
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    Cq, Ck = cq0.shape[0], ck0.shape[0]
+    cq, lq = lloyd(q, cq0, iters)
+    ck, lk = lloyd(k, ck0, iters)
+    pq, oq = permute(lq, Cq)
+    pk, ok = permute(lk, Ck)
+    qbar = means(q, pq, oq)
+    kbar = means(k, pk, ok)
+    vbar = means(v, pk, ok)
+    r, mask = route(qbar, oq, k[pk], v[pk], kbar, vbar, ok, scale, density)
+    O, LSE = attend(q, k, v, pq, oq, pk, ok, kbar, vbar, mask, scale)
+    return dict(cq=cq, ck=ck, lq=lq, lk=lk, pq=pq, oq=oq, pk=pk, ok=ok, qbar=qbar, kbar=kbar,
+                vbar=vbar, ratio=r, mask=mask, O=O, LSE=LSE, scale=scale)
+
+
+def full_attention(q, k, v, scale):
+    """Dense softmax attention, o = sum_j e^{s_j} v_j / sum_j e^{s_j} (FrontierCS
+    blog, the one-query example's formula)."""
+    q = np.asarray(q, F64)
+    L = scale * (q @ np.asarray(k, F64).T)
+    L -= L.max(axis=1, keepdims=True)
+    w = np.exp(L)
+    return (w @ np.asarray(v, F64)) / w.sum(axis=1, keepdims=True)

@@ -1,0 +1,304 @@
+"""Pins of the fp64 oracle to facts that do not come from the oracle itself:
+values the pages print, closed forms, library special cases, invariants and
+brute force on tiny inputs.  CPU only."""
+import json
+import os
+import warnings
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import svgear_oracle as orc
+from synth.gen import WORKLOADS, head_inputs, scaled
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def sdpa64(q, k, v, scale):
+    """Library dense attention in fp64 on the CPU (torch)."""
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v), scale=scale)[0, 0].numpy()
+
+
+def small_head(seed=0, N=192, D=16, comps=6, Cq=5, Ck=9, sigma=0.3):
+    w = scaled(WORKLOADS["tiny"], N=N, D=D, comps=comps, Cq=Cq, Ck=Ck, seed=seed, sigma=sigma)
+    return head_inputs(w, 0)
+
+
+# ---------------------------------------------------------------- the pages' worked example
+def toy():
+    with open(os.path.join(GOLDEN, "toy_example.json")) as f:
+        g = json.load(f)
+    s = g["setup"]
+    K = np.array(s["keys"], dtype=np.float64)[:, None]
+    V = np.array(g["values_fixture"]["values"], dtype=np.float64)[:, None]
+    q = np.array([s["q"]], dtype=np.float64)
+    lab = np.array(s["key_cluster"])
+    return g, q, K, V, lab
+
+
+def lse_of(q, K, V, lab, mask_row, members=None):
+    """Total (estimated) weight exp(LSE) when attending only to the clusters in ``members``."""
+    keep = np.arange(K.shape[0]) if members is None else np.flatnonzero(np.isin(lab, members))
+    Ks, Vs, ls = K[keep], V[keep], lab[keep]
+    C = int(lab.max()) + 1
+    perm, off = orc.permute(ls, C)
+    kbar = orc.means(Ks, perm, off)
+    vbar = orc.means(Vs, perm, off)
+    _, lse = orc.attend_rows(q, Ks, Vs, perm, off, kbar, vbar, np.asarray(mask_row), 1.0)
+    return float(np.exp(lse[0]))
+
+
+def test_toy_weights_and_estimates_match_printed_values():
+    g, q, K, V, lab = toy()
+    p, tol = g["printed"], g["printed_abs_tolerance"]
+    wA = lse_of(q, K, V, lab, [1, 0], members=[0])
+    wB = lse_of(q, K, V, lab, [0, 1], members=[1])
+    tot = lse_of(q, K, V, lab, [1, 1])
+    estA = lse_of(q, K, V, lab, [0, 0], members=[0])
+    estB = lse_of(q, K, V, lab, [0, 0], members=[1])
+    assert abs(wA - p["weight_A"]) < tol and abs(wB - p["weight_B"]) < tol
+    assert abs(tot - p["weight_total"]) < tol
+    assert abs(estA - p["estimate_A"]) < tol and abs(estB - p["estimate_B"]) < tol
+    assert abs((wB - estB) - p["shortfall_B"]) < tol
+    # closed forms of the same example: 2e, 1 + e^2, and n e^{s_bar} = 2e for both estimates
+    e = np.e
+    assert wA == pytest.approx(2 * e, rel=1e-14) and wB == pytest.approx(1 + e * e, rel=1e-14)
+    assert estA == pytest.approx(2 * e, rel=1e-14) and estB == pytest.approx(2 * e, rel=1e-14)
+
+
+def test_toy_error_aware_choice_makes_query_exact():
+    g, q, K, V, lab = toy()
+    perm, off = orc.permute(lab, 2)
+    kbar, vbar = orc.means(K, perm, off), orc.means(V, perm, off)
+    q_off = np.array([0, 1])
+    # room to compute one cluster of the two: a budget of 2 of the 4 keys
+    r, mask = orc.route(q, q_off, K[perm], V[perm], kbar, vbar, off, 1.0, 0.5)
+    assert g["printed"]["choice_with_room_for_one_cluster"] == "B"
+    assert mask.tolist() == [[0, 1]]
+    assert r[0, 0] == 0.0 and r[0, 1] > 0.0
+    O, _ = orc.attend(q, K, V, np.array([0]), q_off, perm, off, kbar, vbar, mask, 1.0)
+    assert g["printed"]["output_after_error_aware_choice"] == "exact"
+    np.testing.assert_allclose(O, sdpa64(q, K, V, 1.0), rtol=0, atol=1e-14)
+    # the score-ranked alternative (compute A, estimate B) is not exact
+    O2, _ = orc.attend(q, K, V, np.array([0]), q_off, perm, off, kbar, vbar, np.array([[1, 0]], np.uint8), 1.0)
+    assert abs(O2[0, 0] - O[0, 0]) > 1e-2
+
+
+# ---------------------------------------------------------------- P1: rho = 1 is full attention
+@pytest.mark.parametrize("seed", [0, 1])
+def test_density_one_equals_full_attention(seed):
+    h = small_head(seed)
+    out = orc.layer(h["q"], h["k"], h["v"], h["cq0"], h["ck0"], iters=3, density=1.0)
+    assert out["mask"][np.diff(out["oq"]) > 0].sum() == ((np.diff(out["oq"]) > 0).sum() * (np.diff(out["ok"]) > 0).sum())
+    ref = sdpa64(h["q"], h["k"], h["v"], out["scale"])
+    np.testing.assert_allclose(out["O"], ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(orc.full_attention(h["q"], h["k"], h["v"], out["scale"]), ref, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- P2: singleton clusters
+@pytest.mark.parametrize("density", [0.1, 0.3])
+def test_singleton_key_clusters_make_compensation_exact(density):
+    h = small_head(2, N=96)
+    q, k, v = h["q"], h["k"], h["v"]
+    out = orc.layer(q, k, v, h["cq0"], k.copy(), iters=2, density=density)
+    assert (np.diff(out["ok"]) == 1).all()
+    assert out["mask"].sum(axis=1).max() < k.shape[0]       # blocks really are skipped
+    np.testing.assert_allclose(out["O"], sdpa64(q, k, v, out["scale"]), rtol=0, atol=1e-12)
+    # every probe error vanishes: one key per cluster equals its centroid
+    assert np.abs(out["ratio"]).max() == 0.0
+
+
+# ---------------------------------------------------------------- P3: permutation equivariance
+def test_token_permutation_equivariance():
+    h = small_head(3)
+    q, k, v = h["q"], h["k"], h["v"]
+    a = orc.layer(q, k, v, h["cq0"], h["ck0"], iters=4, density=0.3)
+    s = np.random.default_rng(7).permutation(q.shape[0])
+    b = orc.layer(q[s], k[s], v[s], h["cq0"], h["ck0"], iters=4, density=0.3)
+    np.testing.assert_array_equal(b["lq"], a["lq"][s])
+    np.testing.assert_array_equal(b["mask"], a["mask"])
+    np.testing.assert_allclose(b["O"], a["O"][s], rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- P4 extras: hand-worked small cases
+def test_permute_hand_example():
+    perm, off = orc.permute(np.array([2, 0, 2, 1, 0]), 4)
+    assert perm.tolist() == [1, 4, 3, 0, 2]
+    assert off.tolist() == [0, 2, 3, 5, 5]
+
+
+def test_means_hand_example_and_empty_cluster():
+    X = np.array([[1.0, 10.0], [2.0, 20.0], [3.0, 30.0], [4.0, 40.0]])
+    perm, off = orc.permute(np.array([0, 2, 0, 2]), 3)
+    m = orc.means(X, perm, off)
+    assert m.tolist() == [[2.0, 20.0], [0.0, 0.0], [3.0, 30.0]]
+
+
+def test_greedy_select_hand_example():
+    sizes = np.array([3, 1, 4, 0, 2])
+    r = np.array([0.5, 0.9, 0.5, 0.0, 0.1], dtype=np.float32)
+    # budget 0.5 * 10 = 5 keys: order 1 (0.9), 0 and 2 (tie at 0.5, lower index first), 4;
+    # taken 0 -> take 1 (1 key), 1 -> take 0 (4), 4 -> take 2 (8), 8 >= 5 stop
+    assert orc.select_row(r, sizes, orc.budget_keys(0.5, 10)).tolist() == [1, 1, 1, 0, 0]
+    # a budget of exactly 1 key takes only the top cluster
+    assert orc.select_row(r, sizes, 1.0).tolist() == [0, 1, 0, 0, 0]
+    # density 1 takes every non-empty cluster, never the empty one
+    assert orc.select_row(r, sizes, 10.0).tolist() == [1, 1, 1, 0, 1]
+
+
+# ---------------------------------------------------------------- P5: linearity and Jensen
+def test_centroid_score_is_mean_score_and_never_overestimates():
+    h = small_head(4, N=256, D=32)
+    q, k, v = h["q"], h["k"], h["v"]
+    ck, lk = orc.lloyd(k, h["ck0"], 3)
+    perm, off = orc.permute(lk, ck.shape[0])
+    kbar = orc.means(k, perm, off)
+    sc = 1 / np.sqrt(32)
+    for j in range(kbar.shape[0]):
+        idx = perm[off[j]:off[j + 1]]
+        if idx.size == 0:
+            continue
+        s = sc * (np.asarray(q, np.float64) @ np.asarray(k, np.float64)[idx].T)
+        sbar = sc * (np.asarray(q, np.float64) @ kbar[j])
+        np.testing.assert_allclose(sbar, s.mean(axis=1), rtol=0, atol=1e-12)
+        assert (idx.size * np.exp(sbar) <= np.exp(s).sum(axis=1) * (1 + 1e-12)).all()
+
+
+# ---------------------------------------------------------------- P6: Lloyd
+def test_lloyd_matches_scipy_kmeans2_and_invariants():
+    from scipy.cluster.vq import kmeans2
+    h = small_head(5, N=600, D=16, comps=8, Ck=12)
+    X = np.asarray(h["k"], np.float64)
+    for T in (1, 2, 5):
+        C, lab = orc.lloyd(X, h["ck0"], T)
+        with warnings.catch_warnings():
+            warnings.simplefilter("ignore")
+            Cs, labs = kmeans2(X, np.asarray(h["ck0"], np.float64), iter=T, minit="matrix")
+        np.testing.assert_array_equal(lab, labs)
+        np.testing.assert_allclose(C, Cs, rtol=0, atol=1e-12)
+    prev = np.inf
+    C = np.asarray(h["ck0"], np.float64)
+    for _ in range(6):
+        C, lab = orc.lloyd(X, C, 1)
+        cur = orc.inertia(X, C, lab)
+        assert cur <= prev * (1 + 1e-12)
+        prev = cur
+    perm, off = orc.permute(lab, C.shape[0])
+    assert sorted(perm.tolist()) == list(range(X.shape[0]))
+    assert (np.diff(lab[perm]) >= 0).all() and off[-1] == X.shape[0]
+    for c in range(C.shape[0]):
+        seg = perm[off[c]:off[c + 1]]
+        assert (np.diff(seg) > 0).all()
+
+
+def test_lloyd_empty_cluster_keeps_centroid():
+    X = np.array([[0.0], [0.1], [10.0]])
+    C0 = np.array([[0.0], [10.0], [100.0]])
+    C, lab = orc.lloyd(X, C0, 1)
+    assert lab.tolist() == [0, 0, 1]
+    np.testing.assert_allclose(C, [[0.05], [10.0], [100.0]], rtol=0, atol=1e-15)
+
+
+def test_assign_ties_go_to_lowest_index():
+    X = np.array([[1.0, 0.0]])
+    C = np.array([[0.0, 0.0], [2.0, 0.0], [1.0, 1.0]])
+    assert orc.assign(X, C).tolist() == [0]
+
+
+# ---------------------------------------------------------------- P7: brute force
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_attend_matches_bruteforce(seed):
+    h = small_head(seed, N=128, D=8, comps=5, Cq=4, Ck=7)
+    q, k, v = (np.asarray(h[x], np.float64) for x in ("q", "k", "v"))
+    _, lq = orc.lloyd(q, h["cq0"], 2)
+    _, lk = orc.lloyd(k, h["ck0"], 2)
+    pq, oq = orc.permute(lq, 4)
+    pk, ok = orc.permute(lk, 7)
+    kbar, vbar = orc.means(k, pk, ok), orc.means(v, pk, ok)
+    mask = (np.random.default_rng(seed).random((4, 7)) < 0.4).astype(np.uint8)
+    sc = 1 / np.sqrt(8)
+    O, _ = orc.attend(q, k, v, pq, oq, pk, ok, kbar, vbar, mask, sc)
+    Ob = orc.attend_bruteforce(q, k, v, lq, lk, kbar, vbar, mask, sc)
+    np.testing.assert_allclose(O, Ob, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- P8: routing invariants
+def test_routing_density_bounds_and_nesting():
+    h = small_head(6, N=512, D=16, comps=10, Cq=6, Ck=20)
+    q, k, v = h["q"], h["k"], h["v"]
+    cq, lq = orc.lloyd(q, h["cq0"], 3)
+    ck, lk = orc.lloyd(k, h["ck0"], 3)
+    pq, oq = orc.permute(lq, 6)
+    pk, ok = orc.permute(lk, 20)
+    qbar, kbar, vbar = orc.means(q, pq, oq), orc.means(k, pk, ok), orc.means(v, pk, ok)
+    sizes = np.diff(ok)
+    N = q.shape[0]
+    prev = None
+    for rho in (0.05, 0.1, 0.25, 0.5, 0.9, 1.0):
+        r, mask = orc.route(qbar, oq, k[pk], v[pk], kbar, vbar, ok, 1 / 4.0, rho)
+        for i in range(6):
+            keys = (mask[i].astype(int) * sizes).sum()
+            budget = float(np.float32(rho)) * N
+            assert budget <= keys < budget + sizes.max()
+            sel, uns = r[i][mask[i] == 1], r[i][(mask[i] == 0) & (sizes > 0)]
+            if uns.size:
+                assert sel.min() >= uns.max()
+        if prev is not None:
+            assert (mask >= prev).all()
+        prev = mask
+    assert (prev[:, sizes > 0] == 1).all() and (prev[:, sizes == 0] == 0).all()
+
+
+# ---------------------------------------------------------------- P9: error sanity and closed forms
+def test_probe_error_closed_forms():
+    rng = np.random.default_rng(11)
+    D, sc = 6, 0.5
+    qbar = rng.standard_normal((3, D))
+    # cluster 0: identical keys, spread values -> e = a^2 * sum_k ||v_bar - v_k||^2 = a^2 * n * sum_d var_d
+    # cluster 1: spread keys, identical values -> e = ||v_bar||^2 * sum_k (a - b_k)^2
+    # cluster 2: identical keys and values -> e = 0
+    k0 = np.repeat(rng.standard_normal((1, D)), 5, axis=0)
+    v0 = rng.standard_normal((5, D))
+    k1 = rng.standard_normal((4, D))
+    v1 = np.repeat(rng.standard_normal((1, D)), 4, axis=0)
+    k2 = np.repeat(rng.standard_normal((1, D)), 3, axis=0)
+    v2 = np.repeat(rng.standard_normal((1, D)), 3, axis=0)
+    Kp, Vp = np.vstack([k0, k1, k2]), np.vstack([v0, v1, v2])
+    off = np.array([0, 5, 9, 12])
+    perm = np.arange(12)
+    kbar, vbar = orc.means(Kp, perm, off), orc.means(Vp, perm, off)
+    e, M = orc.probe_errors(qbar, Kp, Vp, kbar, vbar, off, sc)
+    s_all = sc * qbar @ Kp.T
+    np.testing.assert_allclose(M, s_all.max(axis=1), rtol=1e-15)
+    a0 = np.exp(sc * qbar @ kbar[0] - M)
+    np.testing.assert_allclose(e[:, 0], a0 ** 2 * 5 * np.var(v0, axis=0).sum(), rtol=1e-12)
+    a1 = np.exp(sc * qbar @ kbar[1] - M)
+    b1 = np.exp(s_all[:, 5:9] - M[:, None])
+    np.testing.assert_allclose(e[:, 1], np.dot(v1[0], v1[0]) * ((a1[:, None] - b1) ** 2).sum(1), rtol=1e-12)
+    assert np.abs(e[:, 2]).max() < 1e-28
+    assert (e >= 0).all()
+
+
+def test_ratio_divides_by_block_pairs_and_zero_for_empty():
+    e = np.array([[6.0, 0.0, 8.0], [1.0, 1.0, 1.0]])
+    r = orc.ratios(e, [2, 0], [3, 0, 4])
+    assert r.dtype == np.float32
+    assert r.tolist() == [[1.0, 0.0, 1.0], [0.0, 0.0, 0.0]]
+
+
+# ---------------------------------------------------------------- identical members: estimate is exact
+@pytest.mark.parametrize("density", [0.05, 0.3])
+def test_clusters_of_identical_members_make_compensation_exact(density):
+    """Each key cluster holds 3 copies of one (key, value): n_j e^{q.k_bar} v_bar equals the
+    block's exact contribution, so any mask gives full attention.  Fails if ln n_j is dropped
+    or the wrong value mean is used."""
+    h = small_head(8, N=60, D=8)
+    k = np.repeat(h["k"][:20], 3, axis=0)
+    v = np.repeat(h["v"][:20], 3, axis=0)
+    q = h["q"]
+    out = orc.layer(q, k, v, h["cq0"], h["k"][:20].copy(), iters=2, density=density)
+    assert (np.diff(out["ok"]) == 3).all()
+    assert out["mask"].sum(axis=1).max() < 20
+    np.testing.assert_allclose(out["O"], sdpa64(q, k, v, out["scale"]), rtol=0, atol=1e-12)
