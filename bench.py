@@ -1,0 +1,242 @@
+"""Benchmark: ms per SVG-EAR attention layer on one GPU.
+
+One step = one whole layer on resident inputs: cold k-means of Q (C_q) and K
+(C_k) from the caller's start, permuted copies and means of Q/K/V, error-aware
+routing and the sparse attention pass.  Workload (default): the Wan 2.1 720p
+layer shape, 1 x 40 heads x 75,600 tokens x 128, bf16 Gaussian-mixture inputs
+(400 components, Zipf 1.1 sizes), C_q = 100, C_k = 500, 20 cold k-means
+rounds, density 0.25.
+
+Prints ONE JSON line.  `roofline` is for the dominant kernel (the attention
+pass): algorithmic FLOPs per launch = 4 d (selected query-key pairs +
+query x skipped-cluster pseudo-key pairs), divided by the kernel's average
+duration timed with events on the stream it runs on.  `cpu_baseline` times
+the fp64 oracle on a bounded sample on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import concurrent.futures
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ms per attention layer (cluster+route+sparse attn), 75.6k tok, 25% density; MFMA %"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_F32_TFLOPS = 157.3
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="wan", choices=["wan", "hunyuan", "tiny"])
+    ap.add_argument("--heads", type=int, default=0, help="limit heads (0 = all); changes the workload")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--attn-only", action="store_true", help="after one layer, time only the attention pass")
+    ap.add_argument("--attn-reps", type=int, default=5)
+    return ap.parse_args()
+
+
+def gen_inputs(w, heads):
+    from synth.gen import head_inputs
+    with concurrent.futures.ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
+        hs = list(ex.map(lambda h: head_inputs(w, h), range(heads)))
+    return hs
+
+
+def to_device(hs, key, dtype, dev):
+    import torch
+    from synth.gen import bf16_bits
+    arr = np.stack([h[key] for h in hs])[None]
+    if dtype == "bf16":
+        return torch.from_numpy(bf16_bits(arr).view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(dev)
+
+
+def algorithmic_flops(mask, qoff, koff, D):
+    """4 d per (query, selected key) pair and per (query, skipped non-empty cluster)."""
+    mask = mask.reshape(-1, mask.shape[-2], mask.shape[-1]).astype(np.int64)
+    qs = np.diff(qoff.reshape(-1, qoff.shape[-1]), axis=1).astype(np.int64)
+    ks = np.diff(koff.reshape(-1, koff.shape[-1]), axis=1).astype(np.int64)
+    sel_keys = np.einsum("hij,hj->hi", mask, ks)
+    comp = np.einsum("hij,hj->hi", 1 - mask, (ks > 0).astype(np.int64))
+    pairs_sel = int((qs * sel_keys).sum())
+    pairs_comp = int((qs * comp).sum())
+    return 4 * D * (pairs_sel + pairs_comp), pairs_sel, pairs_comp
+
+
+def cpu_baseline(w, h0, scale):
+    """The fp64 oracle on one head, on bounded samples, scaled to ms per layer."""
+    from oracle import svgear_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    q, k, v = (np.asarray(h0[x], np.float64) for x in ("q", "k", "v"))
+    t = {}
+    s = time.perf_counter()
+    orc.lloyd(q, h0["cq0"], 1)
+    t["kmeans_q_round"] = time.perf_counter() - s
+    s = time.perf_counter()
+    ck, lk = orc.lloyd(k, h0["ck0"], 1)
+    t["kmeans_k_round"] = time.perf_counter() - s
+    cq, lq = orc.lloyd(q, h0["cq0"], 1)
+    s = time.perf_counter()
+    pq, oq = orc.permute(lq, w.Cq)
+    pk, ok = orc.permute(lk, w.Ck)
+    qbar, kbar, vbar = orc.means(q, pq, oq), orc.means(k, pk, ok), orc.means(v, pk, ok)
+    Kp, Vp = k[pk], v[pk]
+    t["permute_means"] = time.perf_counter() - s
+    s = time.perf_counter()
+    r, mask = orc.route(qbar, oq, Kp, Vp, kbar, vbar, ok, scale, w.density)
+    t["route"] = time.perf_counter() - s
+    # attention on a sample of query clusters, scaled by the rows covered
+    sizes = np.diff(oq)
+    pick = [i for i in np.argsort(-sizes) if sizes[i] > 0][::12][:4]
+    rows = int(sum(sizes[i] for i in pick))
+    s = time.perf_counter()
+    for i in pick:
+        toks = pq[oq[i]:oq[i + 1]]
+        orc.attend_rows(q[toks], k, v, pk, ok, kbar, vbar, mask[i], scale)
+    t["attend_sample"] = time.perf_counter() - s
+    per_head = (w.iters * (t["kmeans_q_round"] + t["kmeans_k_round"]) + t["permute_means"] + t["route"]
+                + t["attend_sample"] * (w.N / max(rows, 1)))
+    ms = per_head * w.B * w.H * 1e3
+    sample = (f"1 of {w.B * w.H} heads: one Lloyd round of Q and of K (x{w.iters}), permute+means, route, "
+              f"attention for {rows} of {w.N} query rows (x{w.N / max(rows, 1):.1f}); scaled x{w.B * w.H} heads")
+    return {"value": round(ms, 1), "unit": "ms", "cores": int(cores), "kind": "oracle", "sample": sample,
+            "measured_s": round(sum(t.values()), 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1 "
+                                   "(the path shards by head across GPUs with no collective, see the design notes)"}))
+        sys.exit(2)
+    import torch
+    import sparse_attention_video_amd as sv
+    from synth.gen import WORKLOADS, scaled
+
+    w = WORKLOADS[args.workload]
+    if args.heads:
+        w = scaled(w, H=args.heads)
+    dev = torch.device("cuda:0")
+    sv.load()
+    BH = w.B * w.H
+    t0 = time.time()
+    hs = gen_inputs(w, BH)
+    print(f"# inputs generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    q, k, v = (to_device(hs, x, w.dtype, dev) for x in ("q", "k", "v"))
+    cq0 = to_device(hs, "cq0", "f32", dev)
+    ck0 = to_device(hs, "ck0", "f32", dev)
+    h0 = hs[0]
+    del hs
+    scale = 1.0 / math.sqrt(w.D)
+    L = sv.Layer(w.B, w.H, w.N, w.D, w.Cq, w.Ck, dtype=tdt, device=dev)
+    cq, ck = cq0.clone(), ck0.clone()
+
+    def step():
+        cq.copy_(cq0)
+        ck.copy_(ck0)
+        L.forward(q, k, v, cq, ck, w.iters, w.density, scale)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print("# warmup done", file=sys.stderr, flush=True)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    ms = None
+    if not args.attn_only:
+        a, b = ev(), ev()
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(args.steps):
+            step()
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / args.steps
+        print(f"# timed {args.steps} steps: {ms:.3f} ms/step", file=sys.stderr, flush=True)
+
+    # per-stage breakdown of one instrumented step
+    stages = {}
+    if not args.attn_only:
+        e = [ev() for _ in range(8)]
+        cq.copy_(cq0)
+        ck.copy_(ck0)
+        e[0].record()
+        sv.kmeans(q, cq, w.iters, L.lq, L.pq, L.oq, ws=L.ws)
+        e[1].record()
+        sv.kmeans(k, ck, w.iters, L.lk, L.pk, L.ok, ws=L.ws)
+        e[2].record()
+        sv.centroids(q, L.pq, L.oq, x_perm=L.qp, means=L.qm, ws=L.ws)
+        sv.centroids(k, L.pk, L.ok, x_perm=L.kp, means=L.km, ws=L.ws)
+        sv.centroids(v, L.pk, L.ok, x_perm=L.vp, means=L.vm, ws=L.ws)
+        e[3].record()
+        sv.route(L.qm, L.oq, L.kp, L.vp, L.km, L.vm, L.ok, scale, w.density, mask=L.mask, scores=L.scores, ws=L.ws)
+        e[4].record()
+        sv.sparse_attn(L.qp, L.kp, L.vp, L.pq, L.oq, L.ok, L.km, L.vm, L.mask, scale, out=L.out, ws=L.ws)
+        e[5].record()
+        torch.cuda.synchronize()
+        names = ["kmeans_q", "kmeans_k", "centroids_qkv", "route", "sparse_attn"]
+        stages = {n: round(e[i].elapsed_time(e[i + 1]), 3) for i, n in enumerate(names)}
+
+    # the attention pass alone, repeated (dominant kernel)
+    a, b = ev(), ev()
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(args.attn_reps):
+        sv.sparse_attn(L.qp, L.kp, L.vp, L.pq, L.oq, L.ok, L.km, L.vm, L.mask, scale, out=L.out, ws=L.ws)
+    b.record()
+    torch.cuda.synchronize()
+    t_attn = a.elapsed_time(b) / args.attn_reps
+    flops, pairs_sel, pairs_comp = algorithmic_flops(L.mask.cpu().numpy(), L.oq.cpu().numpy(),
+                                                     L.ok.cpu().numpy(), w.D)
+    achieved = flops / (t_attn * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    if ms is None:
+        ms = t_attn
+    res = {
+        "metric": METRIC,
+        "value": round(ms, 3),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 3),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded Gaussian mixture standing in for Wan 2.1 720p activations)",
+        "config": {"workload": f"{w.name}: {w.B}x{w.H}x{w.N}x{w.D} {w.dtype}, Cq={w.Cq}, Ck={w.Ck}, "
+                               f"{w.iters} cold k-means rounds, density {w.density}",
+                   "B": w.B, "H": w.H, "N": w.N, "D": w.D, "Cq": w.Cq, "Ck": w.Ck, "kmeans_iters": w.iters,
+                   "density": w.density},
+        "roofline": {"kernel": "attn_kernel (svgear_sparse_attn)", "bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+                     "launch_ms": round(t_attn, 3), "flops_per_launch": flops},
+        "stages_ms": stages,
+        "realized_density": round(pairs_sel / (BH * float(w.N) ** 2), 4),
+        "pseudo_pair_fraction": round(pairs_comp / max(1, pairs_sel + pairs_comp), 4),
+    }
+    if not args.no_cpu_baseline and not args.attn_only:
+        print("# timing the oracle on the host", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(w, h0, scale)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,200 @@
+/*
+ * svgear.h -- C ABI of the SVG-EAR sparse-attention hot path on AMD MI355X (gfx950).
+ *
+ * The method: SVG-EAR, "Parameter-Free Linear Compensation for Sparse Video
+ * Generation via Error-aware Routing" (arXiv 2603.08982), built on Sparse
+ * VideoGen2's semantic-aware permutation (arXiv 2505.18875).  The pages this
+ * library follows describe its interface as routines that cluster the tokens
+ * and return the sorted order, average each cluster, pick which cluster pairs
+ * to compute, and compute them while estimating the rest (SVG-EAR task page,
+ * "What the agent has to build" and the walkthrough's steps 1-3).
+ *
+ * Conventions shared by every call
+ *   - Tensors are dense, row-major [B, H, N, D] (or [B, H, C, D] for
+ *     centroids/means, [B, H, N] for per-token integers, [B, H, C+1] for
+ *     offsets, [B, H, Cq, Ck] for routing tables).  B*H independent
+ *     (batch, head) slices are processed in one launch.
+ *   - Self-attention only: queries and keys share N.
+ *   - D is 64 or 128.  Element types: SVGEAR_BF16 (bfloat16) or SVGEAR_F32.
+ *     Centroids, means, scores and LSE are always float32.
+ *   - All pointers are DEVICE pointers (hipMalloc'd or equivalent), owned by
+ *     the caller, and must stay valid until the work queued on `stream`
+ *     finishes.  The library never allocates, frees or retains memory; the
+ *     scratch it needs is the caller's `ws` buffer of at least the size the
+ *     matching *_workspace() query returns (256-byte aligned).
+ *   - Every call is asynchronous on `stream` and never synchronises.  Calls
+ *     that share a workspace or outputs must be ordered on one stream.
+ *   - Arguments are validated before anything is queued.  On any non-OK
+ *     status nothing was queued and outputs are untouched, except
+ *     SVGEAR_ERR_HIP (a launch failed; outputs are undefined).
+ *     svgear_last_error() returns a message for the calling thread's last
+ *     non-OK status.  No call aborts or throws.
+ *   - Results are bitwise deterministic run to run (no float atomics).
+ *   - Setting the environment variable SVGEAR_FAULT to one of kmeans,
+ *     centroids, route, attn makes that call return SVGEAR_ERR_INJECTED
+ *     without queuing work (for testing a caller's dense fallback).
+ */
+#ifndef SVGEAR_H
+#define SVGEAR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SVGEAR_OK = 0,
+    SVGEAR_ERR_INVALID_ARG = 1,   /* a pointer is null, a size is out of range, ... */
+    SVGEAR_ERR_UNSUPPORTED = 2,   /* a valid request this build does not implement */
+    SVGEAR_ERR_WORKSPACE = 3,     /* ws is null, misaligned or smaller than required */
+    SVGEAR_ERR_HIP = 4,           /* a HIP launch failed */
+    SVGEAR_ERR_INJECTED = 5       /* SVGEAR_FAULT named this call */
+} svgear_status;
+
+typedef enum { SVGEAR_BF16 = 0, SVGEAR_F32 = 1 } svgear_dtype;
+
+/* Library version string, e.g. "svgear 0.1.0 gfx950". */
+const char* svgear_version(void);
+
+/* Message for the calling thread's last non-OK status ("" if none). */
+const char* svgear_last_error(void);
+
+/* Largest cluster count any call accepts (C, Cq, Ck). */
+#define SVGEAR_MAX_CLUSTERS 4096
+
+/* ------------------------------------------------------------------------
+ * svgear_kmeans -- Lloyd k-means of one tensor (Q or K), per (batch, head),
+ * emitting the cluster-contiguous permutation.
+ *
+ * SVG2 summary, "Semantic-Aware Permutation via k-Means Clustering": Q and K
+ * are clustered independently per head on their activation vectors (C_q and
+ * C_k clusters, Euclidean distance); "Efficient System-Algorithm
+ * Co-Design": centroids cached from the previous denoising step warm-start
+ * the next one (1-3 rounds instead of 100+).  SVG-EAR task page, walkthrough
+ * step 1: the clustering also returns the sorted order.
+ *
+ *   x          [B,H,N,D] dtype dt, the tokens.
+ *   centroids  [B,H,C,D] float32, IN: start (cold init or the cached
+ *              centroids); OUT: centroids after the last update.
+ *   iters      rounds of (assign, update), >= 1.  Assign: each token to
+ *              its nearest centroid by squared L2 distance; ties go to the
+ *              lowest index (distances within 1e-5 relative of the minimum
+ *              may resolve either way).  Update: each non-empty cluster's
+ *              centroid becomes the mean of its members; an empty cluster
+ *              keeps its centroid.
+ *   labels     [B,H,N] int32 OUT, the last assignment.
+ *   perm       [B,H,N] int32 OUT, perm[p] = source token of permuted slot p:
+ *              tokens grouped by label, original order inside a cluster.
+ *   offsets    [B,H,C+1] int32 OUT, cluster c occupies [offsets[c], offsets[c+1]).
+ *   Limits: 1 <= C <= min(N, SVGEAR_MAX_CLUSTERS), 1 <= N < 2^24.
+ * ---------------------------------------------------------------------- */
+size_t svgear_kmeans_workspace(int B, int H, int N, int D, int C);
+svgear_status svgear_kmeans(const void* x, svgear_dtype dt, int B, int H, int N, int D, int C,
+                            int iters, float* centroids, int32_t* labels, int32_t* perm,
+                            int32_t* offsets, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * svgear_centroids -- gather into cluster-contiguous order and average each
+ * cluster in one pass.
+ *
+ * SVG-EAR task page, "What the agent has to build": one routine averages each
+ * cluster; walkthrough step 1: a small kernel averages each cluster's values
+ * in one pass.  SVG2 summary: Q' = pi_q Q, K' = pi_k K, V' = pi_k V, with K
+ * and V sharing pi_k.
+ *
+ *   x          [B,H,N,D] dtype dt.
+ *   perm, offsets as produced by svgear_kmeans (any valid permutation whose
+ *              clusters are the offsets' ranges is accepted).
+ *   x_perm     [B,H,N,D] dtype dt OUT (nullable): x_perm[p] = x[perm[p]].
+ *   means      [B,H,C,D] float32 OUT (nullable): mean of each cluster's
+ *              rows; an empty cluster gets 0.
+ * ---------------------------------------------------------------------- */
+size_t svgear_centroids_workspace(int B, int H, int N, int D, int C);
+svgear_status svgear_centroids(const void* x, svgear_dtype dt, int B, int H, int N, int D, int C,
+                               const int32_t* perm, const int32_t* offsets, void* x_perm,
+                               float* means, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * svgear_route -- error-aware routing: probe error / block cost, greedy
+ * fill to the density budget.
+ *
+ * FrontierCS blog on SVG-EAR, probe paragraph: the query cluster's mean
+ * q_bar_i is scored against every key k of a block, s_k = q_bar_i.k / sqrt(d)
+ * (here: times `scale`), and the block's error is the sum over its keys of
+ * || e^{s_bar} v_bar - e^{s_k} v_k ||^2 with s_bar, v_bar belonging to the
+ * key's cluster; the error is divided by the block's token pairs.  Pith
+ * review, "What carries the argument": blocks are taken greedily by highest
+ * error-to-cost ratio under a density budget.
+ *
+ * Readings fixed here: both exponentials are taken relative to the row
+ * maximum M_i = max_k s_ik (leaves each row's ranking unchanged); the ratio
+ * is r_ij = e_ij / (|Q_i| |K_j|) rounded to float32 (0 for an empty cluster);
+ * per query cluster the non-empty key clusters are ordered by (r desc, j asc)
+ * and taken while the keys already taken are < density * N (as a double), so
+ * the block that crosses the budget is included; empty key clusters are
+ * never taken; rows of empty query clusters are all zero.
+ *
+ *   q_means    [B,H,Cq,D] float32, the probes (query-cluster means).
+ *   q_offsets  [B,H,Cq+1] int32 (only the sizes |Q_i| are used).
+ *   k_perm, v_perm  [B,H,N,D] dtype dt, keys/values in cluster order.
+ *   k_means, v_means [B,H,Ck,D] float32, the key-cluster means.
+ *   k_offsets  [B,H,Ck+1] int32.
+ *   scale      > 0 (normally 1/sqrt(D)).   density in (0, 1].
+ *   scores_in  nullable [B,H,Cq,Ck] float32: when given, the probe is skipped
+ *              and the selection runs on these ratios (the key, value and
+ *              query-mean pointers may then be null).
+ *   scores_out nullable [B,H,Cq,Ck] float32 OUT: the ratios used.
+ *   mask       [B,H,Cq,Ck] uint8 OUT: 1 = compute the block exactly.
+ * ---------------------------------------------------------------------- */
+size_t svgear_route_workspace(int B, int H, int N, int D, int Cq, int Ck);
+svgear_status svgear_route(const float* q_means, const int32_t* q_offsets, int Cq,
+                           const void* k_perm, const void* v_perm, svgear_dtype dt,
+                           const float* k_means, const float* v_means, const int32_t* k_offsets,
+                           int Ck, int B, int H, int N, int D, float scale, float density,
+                           const float* scores_in, float* scores_out, uint8_t* mask, void* ws,
+                           size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * svgear_sparse_attn -- dynamic-block-size sparse attention with centroid
+ * compensation, output in original token order.
+ *
+ * SVG2 summary, "Custom dynamic block-size sparse attention kernel": blocks
+ * are the (query cluster, key cluster) rectangles of the permuted layout,
+ * of any size.  SVG-EAR: each skipped non-empty key cluster j enters the same
+ * softmax as one key k_bar_j with value v_bar_j and score q.k_bar_j * scale +
+ * ln n_j, i.e. weight n_j e^{q.k_bar_j scale} (FrontierCS blog toy example;
+ * task page walkthrough step 3).  For query token t of cluster i:
+ *   o_t = [sum_{j sel} sum_{u in K_j} e^{s_tu} v_u + sum_{j skipped, n_j>0} n_j e^{q_t.k_bar_j scale} v_bar_j]
+ *         / [the same sums without the values],   s_tu = q_t.k_u * scale.
+ * The output row goes back to the token's original position (SVG2 summary,
+ * inverse permutation of O).
+ *
+ *   q_perm, k_perm, v_perm  [B,H,N,D] dtype dt, cluster-contiguous copies.
+ *   q_perm_idx [B,H,N] int32: original index of each permuted query slot
+ *              (the perm output of svgear_kmeans for Q).
+ *   q_offsets  [B,H,Cq+1], k_offsets [B,H,Ck+1] int32.
+ *   k_means, v_means [B,H,Ck,D] float32.
+ *   mask       [B,H,Cq,Ck] uint8 from svgear_route (any 0/1 table works).
+ *   out        [B,H,N,D] dtype dt OUT, original token order.
+ *   lse        nullable [B,H,N] float32 OUT: natural-log sum of the weights.
+ * A query cluster with nothing selected and every key cluster empty cannot
+ * occur (the key clusters partition N >= 1 keys).
+ * ---------------------------------------------------------------------- */
+size_t svgear_sparse_attn_workspace(int B, int H, int N, int D, int Cq, int Ck);
+svgear_status svgear_sparse_attn(const void* q_perm, const void* k_perm, const void* v_perm,
+                                 svgear_dtype dt, const int32_t* q_perm_idx,
+                                 const int32_t* q_offsets, int Cq, const int32_t* k_offsets,
+                                 int Ck, const float* k_means, const float* v_means,
+                                 const uint8_t* mask, int B, int H, int N, int D, float scale,
+                                 void* out, float* lse, void* ws, size_t ws_bytes,
+                                 hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVGEAR_H */

@@ -1,0 +1,469 @@
+// Dynamic-block-size sparse attention with centroid compensation:
+// svgear_sparse_attn.
+//
+// SVG2 summary, "Custom dynamic block-size sparse attention kernel": after the
+// permutation every (query cluster, key cluster) block is a dense rectangle of
+// any size, computed on the matrix cores without padding each block.  Here a
+// workgroup takes up to 128 rows of one query cluster and streams the union of
+// its selected key clusters as one packed sequence of 64-key tiles (clusters
+// are contiguous in K'/V', so only the last tile of the whole stream is
+// ragged), then the skipped non-empty clusters as pseudo-keys: key k_bar_j,
+// value v_bar_j and a score raised by ln n_j (SVG-EAR: the skipped block's
+// weight becomes n_j e^{q.k_bar_j / sqrt d}; FrontierCS blog toy example, task
+// page walkthrough step 3).  Both parts share one online softmax (running max
+// and sum in fp32), and each row is written back to its original position.
+//
+// MFMA formulation: S^T = K Q^T (keys x queries) and O^T = V^T P^T, so that a
+// lane owns one query column of both, making the softmax statistics and the
+// rescale of O lane-local.  bf16: QK^T and PV on v_mfma_f32_32x32x16_bf16,
+// P rounded to bf16; the pseudo-keys' k_bar and v_bar (fp32) enter as bf16
+// hi + lo pairs.  fp32: v_mfma_f32_32x32x2f32 throughout.
+#include <float.h>
+
+#include "common.h"
+#include "host.h"
+#include "scan.h"
+
+namespace svg {
+
+constexpr int AT_BM = 128;  // query rows per workgroup (4 waves x 32)
+constexpr int AT_BN = 64;   // keys per tile
+
+template <typename T, int D>
+struct AttnLds {
+  static constexpr bool F32 = sizeof(T) == 4;
+  // bf16: K tiles [2][64][SK] (hi, lo) and V^T tiles [2][D][SV] (hi, lo)
+  static constexpr int SK = F32 ? D + 1 : D + 8;
+  static constexpr int SV = F32 ? D + 4 : AT_BN + 8;
+  static constexpr size_t k_bytes = F32 ? (size_t)AT_BN * SK * 4 : (size_t)2 * AT_BN * SK * 2;
+  static constexpr size_t v_bytes = F32 ? (size_t)AT_BN * SV * 4 : (size_t)2 * D * SV * 2;
+  static constexpr size_t fixed = k_bytes + v_bytes + AT_BN * 4 /*bias*/ + 2 * AT_BN * 4 /*src*/;
+};
+
+template <typename T, int D>
+__global__ void __launch_bounds__(256) attn_kernel(const T* __restrict__ qp, const T* __restrict__ kp,
+                                                   const T* __restrict__ vp, const int32_t* __restrict__ qidx,
+                                                   const int32_t* __restrict__ qoff, const int32_t* __restrict__ tstart,
+                                                   int Cq, const int32_t* __restrict__ koff, int Ck,
+                                                   const float* __restrict__ kmeans, const float* __restrict__ vmeans,
+                                                   const uint8_t* __restrict__ mask, int N, float sl2,
+                                                   T* __restrict__ out, float* __restrict__ lse) {
+  using L = AttnLds<T, D>;
+  constexpr bool F32 = L::F32;
+  constexpr int SK = L::SK, SV = L::SV;
+  constexpr int KS = F32 ? D / 2 : D / 16;  // MFMA K-steps over the head dim
+  constexpr int DT = D / 32;                // 32-wide output tiles over the head dim
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  char* sK = smem;
+  char* sV = smem + L::k_bytes;
+  float* sBias = reinterpret_cast<float*>(sV + L::v_bytes);
+  int* sSrc = reinterpret_cast<int*>(sBias + AT_BN);  // [2][64]
+  int* sSelStart = sSrc + 2 * AT_BN;                  // [Ck]
+  int* sSelPre = sSelStart + Ck;                      // [Ck + 1]
+  int* sComp = sSelPre + Ck + 1;                      // [Ck]
+  __shared__ int sScan[16];
+  __shared__ int sInfo[4];
+
+  const int bh = blockIdx.y, tid = threadIdx.x, lane = lane_id(), w = wave_id();
+  const int half = lane >> 5, col = lane & 31;
+  const int32_t* ts = tstart + (size_t)bh * (Cq + 1);
+  if ((int)blockIdx.x >= ts[Cq]) return;
+  if (tid == 0) sInfo[0] = upper_index(ts, Cq, blockIdx.x);
+  __syncthreads();
+  const int ci = sInfo[0];
+  const int32_t* qo = qoff + (size_t)bh * (Cq + 1);
+  const int32_t* ko = koff + (size_t)bh * (Ck + 1);
+  const int row0 = qo[ci] + ((int)blockIdx.x - ts[ci]) * AT_BM;
+  const int rowEnd = qo[ci + 1];
+  const uint8_t* mrow = mask + ((size_t)bh * Cq + ci) * Ck;
+
+  // ---- compact the selected clusters (with key prefix) and the skipped non-empty ones
+  {
+    const int per = (Ck + 255) / 256;
+    const int j0 = tid * per, j1 = min(Ck, j0 + per);
+    int nsel = 0, ncomp = 0, nkeys = 0;
+    for (int j = j0; j < j1; ++j) {
+      const int nj = ko[j + 1] - ko[j];
+      if (nj > 0) {
+        if (mrow[j]) { ++nsel; nkeys += nj; } else { ++ncomp; }
+      }
+    }
+    int tsel, tcomp, tkeys;
+    int psel = block_exscan(nsel, sScan, &tsel);
+    int pcomp = block_exscan(ncomp, sScan, &tcomp);
+    int pkeys = block_exscan(nkeys, sScan, &tkeys);
+    for (int j = j0; j < j1; ++j) {
+      const int nj = ko[j + 1] - ko[j];
+      if (nj > 0) {
+        if (mrow[j]) {
+          sSelStart[psel] = ko[j];
+          sSelPre[psel] = pkeys;
+          ++psel;
+          pkeys += nj;
+        } else {
+          sComp[pcomp++] = j;
+        }
+      }
+    }
+    if (tid == 0) {
+      sSelPre[tsel] = tkeys;
+      sInfo[1] = tsel;
+      sInfo[2] = tcomp;
+      sInfo[3] = tkeys;
+    }
+    __syncthreads();
+  }
+  const int nsel = sInfo[1], ncomp = sInfo[2], nkeys = sInfo[3];
+  const int nreal = (nkeys + AT_BN - 1) / AT_BN;
+  const int ntiles = nreal + (ncomp + AT_BN - 1) / AT_BN;
+
+  // ---- this wave's 32 query rows as MFMA B fragments (query = column)
+  const T* qb = qp + (size_t)bh * N * D;
+  const T* kb = kp + (size_t)bh * N * D;
+  const T* vb = vp + (size_t)bh * N * D;
+  const int qrow = row0 + 32 * w + col;
+  const bool qok = qrow < rowEnd;
+  bf16x8 bq[F32 ? 1 : KS];
+  float bqf[F32 ? KS : 1];
+  if constexpr (!F32) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 v = {};
+      if (qok) v = *reinterpret_cast<const bf16x8*>(qb + (size_t)qrow * D + 16 * ks + 8 * half);
+      bq[ks] = v;
+    }
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) bqf[ks] = qok ? to_f32(qb[(size_t)qrow * D + 2 * ks + half]) : 0.f;
+  }
+
+  f32x16 o[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) o[t] = f32x16{};
+  float m_run = -1e30f, l_run = 0.f;
+
+  // source row (in K'/V') of stream position p of the selected keys
+  auto src_of = [&](int p) -> int {
+    if (p >= nkeys) return -1;
+    const int s = upper_index(sSelPre, nsel, p);
+    return sSelStart[s] + (p - sSelPre[s]);
+  };
+  if (tid < AT_BN && nreal > 0) sSrc[tid] = src_of(tid);
+  __syncthreads();
+
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const bool pseudo = kt >= nreal;
+    // ---- stage the tile: unit = (4 consecutive keys, 8 consecutive dims)
+    {
+      constexpr int UNITS = (AT_BN / 4) * (D / 8);
+      for (int u = tid; u < UNITS; u += 256) {
+        const int g4 = u / (D / 8), dc = u - g4 * (D / 8);
+        const int d0 = dc * 8;
+        float kf[4][8], vf[4][8];
+        bool valid[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = 4 * g4 + r;
+          if (!pseudo) {
+            const int src = sSrc[(kt & 1) * AT_BN + key];
+            valid[r] = src >= 0;
+            if constexpr (!F32) {
+              bf16x8 kv = {}, vv = {};
+              if (valid[r]) {
+                kv = *reinterpret_cast<const bf16x8*>(kb + (size_t)src * D + d0);
+                vv = *reinterpret_cast<const bf16x8*>(vb + (size_t)src * D + d0);
+              }
+#pragma unroll
+              for (int e = 0; e < 8; ++e) { kf[r][e] = (float)kv[e]; vf[r][e] = (float)vv[e]; }
+            } else {
+              f32x4 k0 = {}, k1 = {}, v0 = {}, v1 = {};
+              if (valid[r]) {
+                k0 = *reinterpret_cast<const f32x4*>(kb + (size_t)src * D + d0);
+                k1 = *reinterpret_cast<const f32x4*>(kb + (size_t)src * D + d0 + 4);
+                v0 = *reinterpret_cast<const f32x4*>(vb + (size_t)src * D + d0);
+                v1 = *reinterpret_cast<const f32x4*>(vb + (size_t)src * D + d0 + 4);
+              }
+#pragma unroll
+              for (int e = 0; e < 4; ++e) { kf[r][e] = k0[e]; kf[r][e + 4] = k1[e]; vf[r][e] = v0[e]; vf[r][e + 4] = v1[e]; }
+            }
+          } else {
+            const int c = (kt - nreal) * AT_BN + key;
+            valid[r] = c < ncomp;
+            f32x4 k0 = {}, k1 = {}, v0 = {}, v1 = {};
+            if (valid[r]) {
+              const int j = sComp[c];
+              const float* kr = kmeans + ((size_t)bh * Ck + j) * D + d0;
+              const float* vr = vmeans + ((size_t)bh * Ck + j) * D + d0;
+              k0 = *reinterpret_cast<const f32x4*>(kr);
+              k1 = *reinterpret_cast<const f32x4*>(kr + 4);
+              v0 = *reinterpret_cast<const f32x4*>(vr);
+              v1 = *reinterpret_cast<const f32x4*>(vr + 4);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { kf[r][e] = k0[e]; kf[r][e + 4] = k1[e]; vf[r][e] = v0[e]; vf[r][e + 4] = v1[e]; }
+            if (dc == 0) {
+              float b = -INFINITY;
+              if (valid[r]) {
+                const int j = sComp[c];
+                b = log2f((float)(ko[j + 1] - ko[j]));
+              }
+              sBias[key] = b;
+            }
+          }
+          if (!pseudo && dc == 0) sBias[key] = valid[r] ? 0.f : -INFINITY;
+        }
+        if constexpr (!F32) {
+          bf16* kh = reinterpret_cast<bf16*>(sK);
+          bf16* kl = kh + AT_BN * SK;
+          bf16* vh = reinterpret_cast<bf16*>(sV);
+          bf16* vl = vh + D * SV;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            bf16x8 h, l;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              bf16 hh, ll;
+              split_bf16(kf[r][e], hh, ll);
+              h[e] = hh;
+              l[e] = ll;
+            }
+            *reinterpret_cast<bf16x8*>(&kh[(4 * g4 + r) * SK + d0]) = h;
+            if (pseudo) *reinterpret_cast<bf16x8*>(&kl[(4 * g4 + r) * SK + d0]) = l;
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            bf16x4 h, l;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              bf16 hh, ll;
+              split_bf16(vf[r][e], hh, ll);
+              h[r] = hh;
+              l[r] = ll;
+            }
+            *reinterpret_cast<bf16x4*>(&vh[(d0 + e) * SV + 4 * g4]) = h;
+            if (pseudo) *reinterpret_cast<bf16x4*>(&vl[(d0 + e) * SV + 4 * g4]) = l;
+          }
+        } else {
+          float* kf32 = reinterpret_cast<float*>(sK);
+          float* vf32 = reinterpret_cast<float*>(sV);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              kf32[(4 * g4 + r) * SK + d0 + e] = kf[r][e];
+              vf32[(4 * g4 + r) * SV + d0 + e] = vf[r][e];
+            }
+        }
+      }
+      // next tile's sources
+      if (kt + 1 < nreal && tid < AT_BN) sSrc[((kt + 1) & 1) * AT_BN + tid] = src_of((kt + 1) * AT_BN + tid);
+    }
+    __syncthreads();
+
+    // ---- S^T = K Q^T for two 32-key halves
+    f32x16 s[2];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      f32x16 acc = {};
+      const int krow = sub * 32 + col;
+      if constexpr (!F32) {
+        const bf16* kh = reinterpret_cast<const bf16*>(sK);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kh[krow * SK + 16 * ks + 8 * half]);
+          acc = mfma_bf16(a, bq[ks], acc);
+        }
+        if (pseudo) {
+          const bf16* kl = kh + AT_BN * SK;
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(&kl[krow * SK + 16 * ks + 8 * half]);
+            acc = mfma_bf16(a, bq[ks], acc);
+          }
+        }
+      } else {
+        const float* kf32 = reinterpret_cast<const float*>(sK);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) acc = mfma_f32(kf32[krow * SK + 2 * ks + half], bqf[ks], acc);
+      }
+      s[sub] = acc;
+    }
+
+    // ---- online softmax (log2 domain); lane owns query `col`, 32 of the 64 keys
+    float mx = -INFINITY;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float t = fmaf(s[sub][r], sl2, sBias[sub * 32 + c_row(r, half)]);
+        s[sub][r] = t;
+        mx = fmaxf(mx, t);
+      }
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = exp2f(m_run - m_new);
+    m_run = m_new;
+    float lsum = 0.f;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = exp2f(s[sub][r] - m_new);
+        s[sub][r] = p;
+        lsum += p;
+      }
+    l_run = fmaf(l_run, alpha, lsum);
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+
+    // ---- O^T += V^T P^T
+    if constexpr (!F32) {
+      const bf16* vh = reinterpret_cast<const bf16*>(sV);
+      const bf16* vl = vh + D * SV;
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        const int sub = st >> 1, tp = st & 1;
+        bf16x8 pb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[e] = (bf16)s[sub][8 * tp + e];
+        const int k0 = 16 * st + 4 * half;
+#pragma unroll
+        for (int t = 0; t < DT; ++t) {
+          const int d = 32 * t + col;
+          const bf16x4 x0 = *reinterpret_cast<const bf16x4*>(&vh[d * SV + k0]);
+          const bf16x4 x1 = *reinterpret_cast<const bf16x4*>(&vh[d * SV + k0 + 8]);
+          bf16x8 a;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { a[e] = x0[e]; a[e + 4] = x1[e]; }
+          o[t] = mfma_bf16(a, pb, o[t]);
+          if (pseudo) {
+            const bf16x4 y0 = *reinterpret_cast<const bf16x4*>(&vl[d * SV + k0]);
+            const bf16x4 y1 = *reinterpret_cast<const bf16x4*>(&vl[d * SV + k0 + 8]);
+            bf16x8 b;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { b[e] = y0[e]; b[e + 4] = y1[e]; }
+            o[t] = mfma_bf16(b, pb, o[t]);
+          }
+        }
+      }
+    } else {
+      const float* vf32 = reinterpret_cast<const float*>(sV);
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = sub * 32 + c_row(r, half);
+#pragma unroll
+          for (int t = 0; t < DT; ++t) o[t] = mfma_f32(vf32[key * SV + 32 * t + col], s[sub][r], o[t]);
+        }
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: normalise, write rows back to their original positions
+  const float l_tot = l_run + shfl_xor(l_run, 32);
+  if (qok) {
+    const int orig = qidx[(size_t)bh * N + qrow];
+    const float inv = 1.f / l_tot;
+    T* orow = out + ((size_t)bh * N + orig) * D;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d = 32 * t + 8 * g + 4 * half;
+        if constexpr (!F32) {
+          bf16x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (bf16)(o[t][4 * g + e] * inv);
+          *reinterpret_cast<bf16x4*>(orow + d) = v;
+        } else {
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = o[t][4 * g + e] * inv;
+          *reinterpret_cast<f32x4*>(orow + d) = v;
+        }
+      }
+    if (lse && half == 0) lse[(size_t)bh * N + orig] = (m_run + log2f(l_tot)) * 0.69314718055994531f;
+  }
+}
+
+// ---------------------------------------------------------------- host side
+struct AtPlan {
+  int BH, maxt;
+  size_t off_ts, total;
+};
+
+static AtPlan at_plan(int B, int H, int N, int Cq) {
+  AtPlan p;
+  p.BH = B * H;
+  p.maxt = cdiv(N, AT_BM) + Cq;
+  Carver cv(nullptr);
+  p.off_ts = cv.used; cv.take<int32_t>((size_t)p.BH * (Cq + 1));
+  p.total = cv.used;
+  return p;
+}
+
+template <typename T, int D>
+static void launch_attn(const void* q, const void* k, const void* v, const int32_t* qidx, const int32_t* qoff,
+                        const int32_t* ts, int Cq, const int32_t* koff, int Ck, const float* km, const float* vm,
+                        const uint8_t* mask, int BH, int N, float sl2, void* out, float* lse, int maxt,
+                        hipStream_t st) {
+  using L = AttnLds<T, D>;
+  const size_t lds = L::fixed + (size_t)(3 * Ck + 1) * sizeof(int);
+  (void)hipFuncSetAttribute((const void*)attn_kernel<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipLaunchKernelGGL((attn_kernel<T, D>), dim3(maxt, BH), dim3(256), lds, st, (const T*)q, (const T*)k, (const T*)v,
+                     qidx, qoff, ts, Cq, koff, Ck, km, vm, mask, N, sl2, (T*)out, lse);
+}
+
+}  // namespace svg
+
+using namespace svg;
+
+extern "C" size_t svgear_sparse_attn_workspace(int B, int H, int N, int D, int Cq, int Ck) {
+  (void)D;
+  (void)Ck;
+  if (B < 1 || H < 1 || N < 1 || Cq < 1) return 0;
+  return at_plan(B, H, N, Cq).total;
+}
+
+extern "C" svgear_status svgear_sparse_attn(const void* q_perm, const void* k_perm, const void* v_perm,
+                                            svgear_dtype dt, const int32_t* q_perm_idx, const int32_t* q_offsets,
+                                            int Cq, const int32_t* k_offsets, int Ck, const float* k_means,
+                                            const float* v_means, const uint8_t* mask, int B, int H, int N, int D,
+                                            float scale, void* out, float* lse, void* ws, size_t ws_bytes,
+                                            hipStream_t stream) {
+  svgear_status st = check_common("attn", dt, B, H, N, D);
+  if (st != SVGEAR_OK) return st;
+  if (Cq < 1 || Cq > N || Cq > SVGEAR_MAX_CLUSTERS || Ck < 1 || Ck > N || Ck > SVGEAR_MAX_CLUSTERS)
+    return fail(SVGEAR_ERR_INVALID_ARG, "attn: Cq=%d, Ck=%d must be in [1, min(N=%d, %d)]", Cq, Ck, N,
+                SVGEAR_MAX_CLUSTERS);
+  if (!(scale > 0.f) || !(scale < INFINITY)) return fail(SVGEAR_ERR_INVALID_ARG, "attn: scale must be > 0 and finite");
+  if (!q_perm || !k_perm || !v_perm || !q_perm_idx || !q_offsets || !k_offsets || !k_means || !v_means || !mask ||
+      !out)
+    return fail(SVGEAR_ERR_INVALID_ARG, "attn: null pointer");
+  AtPlan p = at_plan(B, H, N, Cq);
+  st = check_ws("attn", ws, ws_bytes, p.total);
+  if (st != SVGEAR_OK) return st;
+  int32_t* ts = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + p.off_ts);
+  const int BH = B * H;
+  const float sl2 = scale * 1.4426950408889634f;
+  hipLaunchKernelGGL(chunk_list_kernel, dim3(BH), dim3(1024), 0, stream, q_offsets, Cq, AT_BM, ts);
+  if (dt == SVGEAR_BF16) {
+    if (D == 128)
+      launch_attn<bf16, 128>(q_perm, k_perm, v_perm, q_perm_idx, q_offsets, ts, Cq, k_offsets, Ck, k_means, v_means,
+                             mask, BH, N, sl2, out, lse, p.maxt, stream);
+    else
+      launch_attn<bf16, 64>(q_perm, k_perm, v_perm, q_perm_idx, q_offsets, ts, Cq, k_offsets, Ck, k_means, v_means,
+                            mask, BH, N, sl2, out, lse, p.maxt, stream);
+  } else {
+    if (D == 128)
+      launch_attn<float, 128>(q_perm, k_perm, v_perm, q_perm_idx, q_offsets, ts, Cq, k_offsets, Ck, k_means, v_means,
+                              mask, BH, N, sl2, out, lse, p.maxt, stream);
+    else
+      launch_attn<float, 64>(q_perm, k_perm, v_perm, q_perm_idx, q_offsets, ts, Cq, k_offsets, Ck, k_means, v_means,
+                             mask, BH, N, sl2, out, lse, p.maxt, stream);
+  }
+  return check_launch("svgear_sparse_attn");
+}

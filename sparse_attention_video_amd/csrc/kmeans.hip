@@ -1,0 +1,649 @@
+// k-means (Lloyd rounds), the cluster-contiguous permutation and the
+// per-cluster means: svgear_kmeans and svgear_centroids.
+//
+// SVG2 summary, "Semantic-Aware Permutation via k-Means Clustering" (Q and K
+// clustered independently per head; permute so each cluster is contiguous)
+// and "Efficient System-Algorithm Co-Design" (centroid cache warm starts);
+// SVG-EAR task page, walkthrough step 1 (k-means on the GPU returning the
+// sorted order; a small kernel averaging each cluster in one pass).
+//
+// One Lloyd round is: prep (centroid MFMA operands) -> assign (MFMA distance
+// tiles + exact refinement of near ties) -> tile histograms -> scan ->
+// stable scatter (perm) -> chunked segment sums -> means.
+#include <float.h>
+
+#include "common.h"
+#include "host.h"
+#include "scan.h"
+
+namespace svg {
+
+constexpr int KM_EXTRA = 16;        // extra K slots of the distance GEMM (norms, offset)
+constexpr int KM_TOK_WG = 256;      // tokens per assign workgroup (4 waves x 64)
+constexpr int SORT_TILE = 4096;     // tokens per histogram / scatter tile
+constexpr int MEAN_ROWS = 256;      // rows per segment-sum chunk
+constexpr float PAD_NORM = 1e30f;   // squared norm given to padding centroids
+
+// --------------------------------------------------------------------------
+// prep: per (batch, head), the bf16 operands of the distance GEMM.
+//   chi[c][0:D]      = hi part of -2 c      chi[c][D:D+16] = (1, 1, 1, n_hi, n_mid, n_lo, 0, ...)
+//   clo[c][0:D]      = lo part of -2 c      with n = ||c||^2 rounded to fp32 and split in three
+// Padding rows (c >= C) get zeros and n = PAD_NORM, so they never win.
+// cmax[bh] = max_c ||c|| (slightly rounded up), used by the error window.
+// --------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(256) km_prep_kernel(const float* __restrict__ cent, int C, int Cpad,
+                                                      bf16* __restrict__ chi, bf16* __restrict__ clo,
+                                                      float* __restrict__ cmax) {
+  constexpr int EPL = D / SV_WAVE;  // elements per lane
+  __shared__ double s_max[4];
+  const int bh = blockIdx.x, lane = lane_id(), w = wave_id();
+  const float* cb = cent + (size_t)bh * C * D;
+  bf16* hb = chi + (size_t)bh * Cpad * (D + KM_EXTRA);
+  bf16* lb = clo + (size_t)bh * Cpad * D;
+  double wmax = 0.0;
+  for (int c = w; c < Cpad; c += 4) {
+    double cc = 0.0;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      int d = lane + e * SV_WAVE;
+      float v = c < C ? cb[(size_t)c * D + d] : 0.f;
+      bf16 hi, lo;
+      split_bf16(-2.f * v, hi, lo);
+      hb[(size_t)c * (D + KM_EXTRA) + d] = hi;
+      lb[(size_t)c * D + d] = lo;
+      cc += (double)v * (double)v;
+    }
+    cc = wave_sum_d(cc);
+    if (c < C) wmax = fmax(wmax, cc);
+    if (lane < KM_EXTRA) {
+      float n = c < C ? (float)cc : PAD_NORM;
+      bf16 n_hi = (bf16)n;
+      float r1 = n - (float)n_hi;
+      bf16 n_mid = (bf16)r1;
+      bf16 n_lo = (bf16)(r1 - (float)n_mid);
+      bf16 val = (bf16)0.f;
+      if (lane < 3) val = (bf16)1.f;
+      else if (lane == 3) val = n_hi;
+      else if (lane == 4) val = c < C ? n_mid : (bf16)0.f;
+      else if (lane == 5) val = c < C ? n_lo : (bf16)0.f;
+      hb[(size_t)c * (D + KM_EXTRA) + D + lane] = val;
+    }
+  }
+  if (lane == 0) s_max[w] = wmax;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double m = fmax(fmax(s_max[0], s_max[1]), fmax(s_max[2], s_max[3]));
+    cmax[bh] = (float)(sqrt(m) * (1.0 + 1e-6));
+  }
+}
+
+// --------------------------------------------------------------------------
+// assign: label[n] = argmin_c ||x_n - c||^2 (ties to the lowest index).
+//
+// Each wave owns 64 tokens as two 32-token MFMA B tiles held in registers;
+// the workgroup streams 32-centroid chunks of the prep operands through LDS.
+// One 32x32 output tile is (centroid m, token n) ->
+//   V = ||x||^2 + off + ||c||^2 - 2 x.c   (the extra K slots add the norms),
+// an fp32 estimate of ||x - c||^2 + off with off >= 1 keeping it positive.
+// The low `ib` bits of V's float pattern are replaced by the centroid index;
+// the result orders like (V, index) and each lane keeps its 4 smallest with
+// min/med3.  A rigorous bound W on the estimate's error (bf16 splitting of c
+// and of fp32 x, fp32 accumulation, truncation of the low bits) decides:
+//   key2 - key1 > W          -> label = index of key1 (provably the argmin)
+//   else, <= 4 keys inside W -> exact fp64 distances of those candidates
+//   else                     -> exact fp64 scan of every centroid
+// The exact distances are summed by a fixed 64-lane butterfly.
+// --------------------------------------------------------------------------
+template <typename T, int D>
+__global__ void __launch_bounds__(256) km_assign_kernel(const T* __restrict__ x, const bf16* __restrict__ chi,
+                                                        const bf16* __restrict__ clo, const float* __restrict__ cmax,
+                                                        const float* __restrict__ cent, int N, int C, int Cpad, int ib,
+                                                        int32_t* __restrict__ labels) {
+  constexpr bool F32 = sizeof(T) == 4;
+  constexpr int KS = D / 16;
+  constexpr int SH = D + KM_EXTRA + 8;  // LDS row strides (bf16 elements): odd multiples of 16 bytes
+  constexpr int SL = D + 8;
+  constexpr int HU = (D + KM_EXTRA) / 8, LU = D / 8;  // 16-byte units per row
+  __shared__ __attribute__((aligned(16))) bf16 s_hi[32 * SH];
+  __shared__ __attribute__((aligned(16))) bf16 s_lo[32 * SL];
+
+  const int bh = blockIdx.y, tid = threadIdx.x, lane = lane_id(), w = wave_id();
+  const int half = lane >> 5, col = lane & 31;
+  const T* xb = x + (size_t)bh * N * D;
+  const bf16* hb = chi + (size_t)bh * Cpad * (D + KM_EXTRA);
+  const bf16* lb = clo + (size_t)bh * Cpad * D;
+  const float* cb = cent + (size_t)bh * C * D;
+  const int tok0 = blockIdx.x * KM_TOK_WG + w * 64;
+  const float u = 5.9604645e-08f;  // 2^-24
+
+  bf16x8 bx[2][KS];
+  bf16x8 bxl[2][F32 ? KS : 1];
+  bf16x8 bext[2];
+  float xx[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int n = tok0 + 32 * t + col;
+    const bool ok = n < N;
+    float part = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int d0 = 16 * ks + 8 * half;
+      if constexpr (!F32) {
+        bf16x8 v = {};
+        if (ok) v = *reinterpret_cast<const bf16x8*>(xb + (size_t)n * D + d0);
+        bx[t][ks] = v;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) part += (float)v[e] * (float)v[e];
+      } else {
+        float f[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) f[e] = 0.f;
+        if (ok) {
+          f32x4 a = *reinterpret_cast<const f32x4*>(xb + (size_t)n * D + d0);
+          f32x4 b = *reinterpret_cast<const f32x4*>(xb + (size_t)n * D + d0 + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { f[e] = a[e]; f[e + 4] = b[e]; }
+        }
+        bf16x8 h, l;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          bf16 hh, ll;
+          split_bf16(f[e], hh, ll);
+          h[e] = hh;
+          l[e] = ll;
+          part += f[e] * f[e];
+        }
+        bx[t][ks] = h;
+        bxl[t][ks % (F32 ? KS : 1)] = l;
+      }
+    }
+    xx[t] = part + shfl_xor(part, 32);
+  }
+
+  // Error window (see above).  s: split error factor; K: products per output.
+  const float cm = cmax[bh];
+  const float s_split = F32 ? 3.01f : 1.0f;
+  const int kprod = D * (F32 ? 3 : 2) + KM_EXTRA;
+  const float gam = (kprod * u) / (1.f - kprod * u);
+  const float q = ldexpf(1.f, ib - 23);
+  float E0[2], off[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const float X = sqrtf(xx[t]) * (1.f + 1e-6f);
+    const float xxb = xx[t] * (1.f + 2e-5f) + 1e-30f;
+    const float pre = u * cm * cm + 4.f * s_split * 3.8146973e-06f * X * cm;  // 2^-18
+    float e0 = 1.25f * (pre + gam * (xxb + 2.f + cm * cm + 2.05f * X * cm));
+    const float o = 1.f + 4.f * e0 + 4e-5f * xxb;
+    E0[t] = 1.25f * (pre + gam * (xxb + o + 2.f + cm * cm + 2.05f * X * cm));
+    off[t] = o;
+    bf16x8 ex = {};
+    if (half == 0) {
+      bf16 xh, xl;
+      split_bf16(xx[t], xh, xl);
+      ex[0] = xh;
+      ex[1] = xl;
+      ex[2] = (bf16)o;
+      ex[3] = (bf16)1.f;
+      ex[4] = (bf16)1.f;
+      ex[5] = (bf16)1.f;
+    }
+    bext[t] = ex;
+  }
+
+  const uint32_t imask = (1u << ib) - 1u;
+  float key[2][4];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) key[t][k] = FLT_MAX;
+
+  for (int c0 = 0; c0 < Cpad; c0 += 32) {
+    __syncthreads();
+    for (int v = tid; v < 32 * HU; v += 256) {
+      const int r = v / HU, cu = v - r * HU;
+      *reinterpret_cast<u32x4*>(&s_hi[r * SH + cu * 8]) =
+          *reinterpret_cast<const u32x4*>(hb + (size_t)(c0 + r) * (D + KM_EXTRA) + cu * 8);
+    }
+    for (int v = tid; v < 32 * LU; v += 256) {
+      const int r = v / LU, cu = v - r * LU;
+      *reinterpret_cast<u32x4*>(&s_lo[r * SL + cu * 8]) =
+          *reinterpret_cast<const u32x4*>(lb + (size_t)(c0 + r) * D + cu * 8);
+    }
+    __syncthreads();
+    f32x16 acc0 = {}, acc1 = {};
+    {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s_hi[col * SH + D + 8 * half]);
+      acc0 = mfma_bf16(a, bext[0], acc0);
+      acc1 = mfma_bf16(a, bext[1], acc1);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s_hi[col * SH + 16 * ks + 8 * half]);
+      acc0 = mfma_bf16(a, bx[0][ks], acc0);
+      acc1 = mfma_bf16(a, bx[1][ks], acc1);
+      if constexpr (F32) {
+        acc0 = mfma_bf16(a, bxl[0][ks % (F32 ? KS : 1)], acc0);
+        acc1 = mfma_bf16(a, bxl[1][ks % (F32 ? KS : 1)], acc1);
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s_lo[col * SL + 16 * ks + 8 * half]);
+      acc0 = mfma_bf16(a, bx[0][ks], acc0);
+      acc1 = mfma_bf16(a, bx[1][ks], acc1);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const uint32_t idx = (uint32_t)(c0 + c_row(r, half));
+      float k0 = __uint_as_float((__float_as_uint(acc0[r]) & ~imask) | idx);
+      float k1 = __uint_as_float((__float_as_uint(acc1[r]) & ~imask) | idx);
+      key[0][3] = med3f(key[0][2], key[0][3], k0);
+      key[0][2] = med3f(key[0][1], key[0][2], k0);
+      key[0][1] = med3f(key[0][0], key[0][1], k0);
+      key[0][0] = fminf(key[0][0], k0);
+      key[1][3] = med3f(key[1][2], key[1][3], k1);
+      key[1][2] = med3f(key[1][1], key[1][2], k1);
+      key[1][1] = med3f(key[1][0], key[1][1], k1);
+      key[1][0] = fminf(key[1][0], k1);
+    }
+  }
+
+  // merge the two halves' lists (they hold different centroids of the same tokens)
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    float o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = shfl_xor(key[t][k], 32);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float kk = o[k];
+      key[t][3] = med3f(key[t][2], key[t][3], kk);
+      key[t][2] = med3f(key[t][1], key[t][2], kk);
+      key[t][1] = med3f(key[t][0], key[t][1], kk);
+      key[t][0] = fminf(key[t][0], kk);
+    }
+  }
+
+  int lab[2], ncand[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const float k1v = key[t][0];
+    const float W = 2.f * E0[t] + q * (2.f * k1v + 2.f * E0[t] + 1.f) * 2.5f;
+    lab[t] = (int)(__float_as_uint(k1v) & imask);
+    int nc = 1;
+#pragma unroll
+    for (int k = 1; k < 4; ++k) nc += (key[t][k] - k1v <= W) ? 1 : 0;
+    ncand[t] = nc;  // 1: decided; 2..3: refine candidates; 4: full scan
+  }
+
+  // exact refinement, one flagged token at a time, all 64 lanes cooperating
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int n_mine = tok0 + 32 * t + col;
+    uint64_t todo = ballot(half == 0 && n_mine < N && ncand[t] > 1);
+    while (todo) {
+      const int src = __builtin_ctzll(todo);
+      todo &= todo - 1;
+      const int n = tok0 + 32 * t + src;
+      const int nc = __shfl(ncand[t], src, SV_WAVE);
+      double xv[D / SV_WAVE];
+#pragma unroll
+      for (int e = 0; e < D / SV_WAVE; ++e) xv[e] = (double)to_f32(xb[(size_t)n * D + lane + e * SV_WAVE]);
+      int cand[3];
+#pragma unroll
+      for (int j = 0; j < 3; ++j) cand[j] = (int)(__float_as_uint(__shfl(key[t][j], src, SV_WAVE)) & imask);
+      double best = 0.0;
+      int bidx = -1;
+      const int count = nc >= 4 ? C : nc;
+      for (int j = 0; j < count; ++j) {
+        const int c = nc >= 4 ? j : (j == 0 ? cand[0] : (j == 1 ? cand[1] : cand[2]));
+        if (c >= C) continue;  // padding centroids never qualify; guard the read anyway
+        double part = 0.0;
+#pragma unroll
+        for (int e = 0; e < D / SV_WAVE; ++e) {
+          const double dv = xv[e] - (double)cb[(size_t)c * D + lane + e * SV_WAVE];
+          part += dv * dv;
+        }
+        const double dist = wave_sum_d(part);
+        if (bidx < 0 || dist < best || (dist == best && c < bidx)) {
+          best = dist;
+          bidx = c;
+        }
+      }
+      if (lane == src) lab[t] = bidx;
+    }
+    if (half == 0 && n_mine < N) labels[(size_t)bh * N + n_mine] = min(lab[t], C - 1);
+  }
+}
+
+// --------------------------------------------------------------------------
+// tile histograms: counts[bh][tile][c] = #tokens of tile with label c
+// --------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) km_hist_kernel(const int32_t* __restrict__ labels, int N, int C, int ntiles,
+                                                      int32_t* __restrict__ counts) {
+  __shared__ int32_t h[SVGEAR_MAX_CLUSTERS];
+  const int bh = blockIdx.y, tile = blockIdx.x;
+  for (int c = threadIdx.x; c < C; c += 256) h[c] = 0;
+  __syncthreads();
+  const int n0 = tile * SORT_TILE, n1 = min(N, n0 + SORT_TILE);
+  const int32_t* lb = labels + (size_t)bh * N;
+  for (int n = n0 + threadIdx.x; n < n1; n += 256) atomicAdd(&h[lb[n]], 1);
+  __syncthreads();
+  int32_t* cnt = counts + ((size_t)bh * ntiles + tile) * C;
+  for (int c = threadIdx.x; c < C; c += 256) cnt[c] = h[c];
+}
+
+// --------------------------------------------------------------------------
+// scan: offsets (cluster starts), per-tile bases (in place over counts) and
+// the segment-sum chunk list.  One block of 1024 threads per (batch, head).
+// --------------------------------------------------------------------------
+__global__ void __launch_bounds__(1024) km_scan_kernel(int32_t* __restrict__ counts, int N, int C, int ntiles,
+                                                       int rows, int32_t* __restrict__ offsets,
+                                                       int32_t* __restrict__ chunk_start) {
+  __shared__ int sm[16];
+  const int bh = blockIdx.x;
+  int32_t* cnt = counts + (size_t)bh * ntiles * C;
+  int tot[4], nch[4];
+  int sum = 0, csum = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int c = threadIdx.x * 4 + e;
+    int s = 0;
+    if (c < C)
+      for (int t = 0; t < ntiles; ++t) s += cnt[(size_t)t * C + c];
+    tot[e] = s;
+    nch[e] = (s + rows - 1) / rows;
+    sum += s;
+    csum += nch[e];
+  }
+  int total, ctotal;
+  int base = block_exscan(sum, sm, &total);
+  int cbase = block_exscan(csum, sm, &ctotal);
+  int32_t* off = offsets + (size_t)bh * (C + 1);
+  int32_t* cs = chunk_start + (size_t)bh * (C + 1);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int c = threadIdx.x * 4 + e;
+    if (c < C) {
+      off[c] = base;
+      cs[c] = cbase;
+      int b = base;
+      for (int t = 0; t < ntiles; ++t) {
+        const int v = cnt[(size_t)t * C + c];
+        cnt[(size_t)t * C + c] = b;
+        b += v;
+      }
+    }
+    base += tot[e];
+    cbase += nch[e];
+  }
+  if (threadIdx.x == 0) {
+    off[C] = total;
+    cs[C] = ctotal;
+  }
+}
+
+// --------------------------------------------------------------------------
+// stable scatter: perm[dest] = token, tokens of one cluster in original order.
+// Each wave owns a contiguous quarter of the tile; equal labels inside a
+// 64-token step are matched with ballots over the label bits, so ranks come
+// out in lane order with no atomics.
+// --------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) km_scatter_kernel(const int32_t* __restrict__ labels,
+                                                         const int32_t* __restrict__ tile_base, int N, int C,
+                                                         int ntiles, int ib, int32_t* __restrict__ perm) {
+  extern __shared__ int32_t hw[];  // [4][C]
+  const int bh = blockIdx.y, tile = blockIdx.x, lane = lane_id(), w = wave_id();
+  const int32_t* lb = labels + (size_t)bh * N;
+  int32_t* pb = perm + (size_t)bh * N;
+  for (int c = threadIdx.x; c < 4 * C; c += 256) hw[c] = 0;
+  __syncthreads();
+  const int q0 = tile * SORT_TILE + w * (SORT_TILE / 4);
+  const int q1 = min(N, q0 + SORT_TILE / 4);
+  int32_t* mine = hw + w * C;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int pass = 0; pass < 2; ++pass) {
+    for (int n0 = q0; n0 < q1; n0 += SV_WAVE) {
+      const int n = n0 + lane;
+      const bool ok = n < q1;
+      const int lab = ok ? lb[n] : 0;
+      uint64_t peers = ballot(ok);
+      for (int b = 0; b < ib; ++b) {
+        const bool bit = (lab >> b) & 1;
+        const uint64_t m = ballot(bit);
+        peers &= bit ? m : ~m;
+      }
+      const int leader = __builtin_ctzll(peers | (1ull << 63));
+      const int cnt = __popcll(peers);
+      if (pass == 1 && ok) pb[mine[lab] + __popcll(peers & lt)] = n;
+      if (ok && lane == leader) mine[lab] += cnt;
+    }
+    if (pass == 0) {
+      __syncthreads();
+      const int32_t* tb = tile_base + ((size_t)bh * ntiles + tile) * C;
+      for (int c = threadIdx.x; c < C; c += 256) {
+        int b = tb[c];
+        for (int ww = 0; ww < 4; ++ww) {
+          const int v = hw[ww * C + c];
+          hw[ww * C + c] = b;
+          b += v;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// segment sums over the permuted order: chunk k of cluster c sums rows
+// [offsets[c] + k' * rows, ...) of x[perm[.]] (k' = k - chunk_start[c]),
+// optionally writing the permuted copy.  Fixed row-to-lane mapping and a
+// fixed reduction order keep the sums deterministic.
+// --------------------------------------------------------------------------
+template <typename T, int D>
+__global__ void __launch_bounds__(256) km_partial_kernel(const T* __restrict__ x, const int32_t* __restrict__ perm,
+                                                         const int32_t* __restrict__ offsets,
+                                                         const int32_t* __restrict__ chunk_start, int N, int C,
+                                                         int rows, int maxch, float* __restrict__ partial,
+                                                         T* __restrict__ x_perm) {
+  constexpr int EPL = 16 / sizeof(T);     // elements per lane (one 16-byte load)
+  constexpr int LPR = D / EPL;            // lanes per row
+  constexpr int RPI = 256 / LPR;          // rows per iteration
+  __shared__ float red[RPI * D];
+  __shared__ int s_c;
+  const int bh = blockIdx.y, k = blockIdx.x;
+  const int32_t* cs = chunk_start + (size_t)bh * (C + 1);
+  if (k >= cs[C]) return;
+  if (threadIdx.x == 0) s_c = upper_index(cs, C, k);
+  __syncthreads();
+  const int c = s_c;
+  const int32_t* off = offsets + (size_t)bh * (C + 1);
+  const int r0 = off[c] + (k - cs[c]) * rows;
+  const int r1 = min(r0 + rows, off[c + 1]);
+  const int g = threadIdx.x / LPR, e0 = (threadIdx.x % LPR) * EPL;
+  const T* xb = x + (size_t)bh * N * D;
+  const int32_t* pb = perm + (size_t)bh * N;
+  T* xpb = x_perm ? x_perm + (size_t)bh * N * D : nullptr;
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  for (int p = r0 + g; p < r1; p += RPI) {
+    const int src = pb[p];
+    const u32x4 v = ld16(xb + (size_t)src * D + e0);
+    if (xpb) st16(xpb + (size_t)p * D + e0, v);
+    const T* tv = reinterpret_cast<const T*>(&v);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] += to_f32(tv[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) red[g * D + e0 + e] = acc[e];
+  __syncthreads();
+  for (int d = threadIdx.x; d < D; d += 256) {
+    float s = 0.f;
+    for (int gg = 0; gg < RPI; ++gg) s += red[gg * D + d];
+    partial[((size_t)bh * maxch + k) * D + d] = s;
+  }
+}
+
+// means[c] = (sum of c's chunks, in order) / |c|.  Empty clusters: keep the
+// old value (k-means update) or write 0 (svgear_centroids).
+__global__ void __launch_bounds__(256) km_finalize_kernel(const float* __restrict__ partial,
+                                                          const int32_t* __restrict__ offsets,
+                                                          const int32_t* __restrict__ chunk_start, int C, int D,
+                                                          int maxch, float* __restrict__ means, int keep_empty) {
+  const int bh = blockIdx.y;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= C * D) return;
+  const int c = i / D, d = i - c * D;
+  const int32_t* off = offsets + (size_t)bh * (C + 1);
+  const int32_t* cs = chunk_start + (size_t)bh * (C + 1);
+  const int n = off[c + 1] - off[c];
+  float* out = means + ((size_t)bh * C + c) * D + d;
+  if (n == 0) {
+    if (!keep_empty) *out = 0.f;
+    return;
+  }
+  float s = 0.f;
+  for (int k = cs[c]; k < cs[c + 1]; ++k) s += partial[((size_t)bh * maxch + k) * D + d];
+  *out = s / (float)n;
+}
+
+// ---------------------------------------------------------------- host side
+struct KmPlan {
+  int BH, Cpad, ib, ntiles, maxch;
+  size_t off_chi, off_clo, off_cmax, off_counts, off_cs, off_partial, total;
+};
+
+static KmPlan km_plan(int B, int H, int N, int D, int C) {
+  KmPlan p;
+  p.BH = B * H;
+  p.Cpad = round_up(C, 32);
+  p.ib = bit_length((unsigned)(p.Cpad - 1));
+  if (p.ib < 1) p.ib = 1;
+  p.ntiles = cdiv(N, SORT_TILE);
+  p.maxch = cdiv(N, MEAN_ROWS) + C;
+  Carver cv(nullptr);
+  p.off_chi = cv.used; cv.take<bf16>((size_t)p.BH * p.Cpad * (D + KM_EXTRA));
+  p.off_clo = cv.used; cv.take<bf16>((size_t)p.BH * p.Cpad * D);
+  p.off_cmax = cv.used; cv.take<float>(p.BH);
+  p.off_counts = cv.used; cv.take<int32_t>((size_t)p.BH * p.ntiles * C);
+  p.off_cs = cv.used; cv.take<int32_t>((size_t)p.BH * (C + 1));
+  p.off_partial = cv.used; cv.take<float>((size_t)p.BH * p.maxch * D);
+  p.total = cv.used;
+  return p;
+}
+
+struct MeanPlan {
+  int BH, maxch;
+  size_t off_cs, off_partial, total;
+};
+
+static MeanPlan mean_plan(int B, int H, int N, int D, int C) {
+  MeanPlan p;
+  p.BH = B * H;
+  p.maxch = cdiv(N, MEAN_ROWS) + C;
+  Carver cv(nullptr);
+  p.off_cs = cv.used; cv.take<int32_t>((size_t)p.BH * (C + 1));
+  p.off_partial = cv.used; cv.take<float>((size_t)p.BH * p.maxch * D);
+  p.total = cv.used;
+  return p;
+}
+
+template <typename T, int D>
+static void launch_partial(const void* x, const int32_t* perm, const int32_t* offsets, const int32_t* cs, int BH,
+                           int N, int C, int maxch, float* partial, void* x_perm, hipStream_t st) {
+  hipLaunchKernelGGL((km_partial_kernel<T, D>), dim3(maxch, BH), dim3(256), 0, st, (const T*)x, perm, offsets, cs, N,
+                     C, MEAN_ROWS, maxch, partial, (T*)x_perm);
+}
+
+template <typename T, int D>
+static svgear_status kmeans_impl(const void* x, int BH, int N, int C, int iters, float* cent, int32_t* labels,
+                                 int32_t* perm, int32_t* offsets, char* ws, const KmPlan& p, hipStream_t st) {
+  bf16* chi = reinterpret_cast<bf16*>(ws + p.off_chi);
+  bf16* clo = reinterpret_cast<bf16*>(ws + p.off_clo);
+  float* cmax = reinterpret_cast<float*>(ws + p.off_cmax);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + p.off_counts);
+  int32_t* cs = reinterpret_cast<int32_t*>(ws + p.off_cs);
+  float* partial = reinterpret_cast<float*>(ws + p.off_partial);
+  for (int it = 0; it < iters; ++it) {
+    hipLaunchKernelGGL((km_prep_kernel<D>), dim3(BH), dim3(256), 0, st, cent, C, p.Cpad, chi, clo, cmax);
+    hipLaunchKernelGGL((km_assign_kernel<T, D>), dim3(cdiv(N, KM_TOK_WG), BH), dim3(256), 0, st, (const T*)x, chi,
+                       clo, cmax, cent, N, C, p.Cpad, p.ib, labels);
+    hipLaunchKernelGGL(km_hist_kernel, dim3(p.ntiles, BH), dim3(256), 0, st, labels, N, C, p.ntiles, counts);
+    hipLaunchKernelGGL(km_scan_kernel, dim3(BH), dim3(1024), 0, st, counts, N, C, p.ntiles, MEAN_ROWS, offsets, cs);
+    (void)hipFuncSetAttribute((const void*)km_scatter_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)(4 * C * sizeof(int32_t)));
+    hipLaunchKernelGGL(km_scatter_kernel, dim3(p.ntiles, BH), dim3(256), 4 * C * sizeof(int32_t), st, labels, counts,
+                       N, C, p.ntiles, p.ib, perm);
+    launch_partial<T, D>(x, perm, offsets, cs, BH, N, C, p.maxch, partial, nullptr, st);
+    hipLaunchKernelGGL(km_finalize_kernel, dim3(cdiv(C * D, 256), BH), dim3(256), 0, st, partial, offsets, cs, C, D,
+                       p.maxch, cent, 1);
+  }
+  return check_launch("svgear_kmeans");
+}
+
+}  // namespace svg
+
+using namespace svg;
+
+extern "C" size_t svgear_kmeans_workspace(int B, int H, int N, int D, int C) {
+  if (B < 1 || H < 1 || N < 1 || C < 1 || (D != 64 && D != 128)) return 0;
+  return km_plan(B, H, N, D, C).total;
+}
+
+extern "C" svgear_status svgear_kmeans(const void* x, svgear_dtype dt, int B, int H, int N, int D, int C, int iters,
+                                       float* centroids, int32_t* labels, int32_t* perm, int32_t* offsets, void* ws,
+                                       size_t ws_bytes, hipStream_t stream) {
+  svgear_status st = check_common("kmeans", dt, B, H, N, D);
+  if (st != SVGEAR_OK) return st;
+  if (C < 1 || C > N || C > SVGEAR_MAX_CLUSTERS)
+    return fail(SVGEAR_ERR_INVALID_ARG, "kmeans: C=%d must be in [1, min(N=%d, %d)]", C, N, SVGEAR_MAX_CLUSTERS);
+  if (iters < 1) return fail(SVGEAR_ERR_INVALID_ARG, "kmeans: iters=%d must be >= 1", iters);
+  if (!x || !centroids || !labels || !perm || !offsets) return fail(SVGEAR_ERR_INVALID_ARG, "kmeans: null pointer");
+  KmPlan p = km_plan(B, H, N, D, C);
+  st = check_ws("kmeans", ws, ws_bytes, p.total);
+  if (st != SVGEAR_OK) return st;
+  char* w = static_cast<char*>(ws);
+  const int BH = B * H;
+  if (dt == SVGEAR_BF16)
+    return D == 128 ? kmeans_impl<bf16, 128>(x, BH, N, C, iters, centroids, labels, perm, offsets, w, p, stream)
+                    : kmeans_impl<bf16, 64>(x, BH, N, C, iters, centroids, labels, perm, offsets, w, p, stream);
+  return D == 128 ? kmeans_impl<float, 128>(x, BH, N, C, iters, centroids, labels, perm, offsets, w, p, stream)
+                  : kmeans_impl<float, 64>(x, BH, N, C, iters, centroids, labels, perm, offsets, w, p, stream);
+}
+
+extern "C" size_t svgear_centroids_workspace(int B, int H, int N, int D, int C) {
+  if (B < 1 || H < 1 || N < 1 || C < 1 || (D != 64 && D != 128)) return 0;
+  return mean_plan(B, H, N, D, C).total;
+}
+
+extern "C" svgear_status svgear_centroids(const void* x, svgear_dtype dt, int B, int H, int N, int D, int C,
+                                          const int32_t* perm, const int32_t* offsets, void* x_perm, float* means,
+                                          void* ws, size_t ws_bytes, hipStream_t stream) {
+  svgear_status st = check_common("centroids", dt, B, H, N, D);
+  if (st != SVGEAR_OK) return st;
+  if (C < 1 || C > N || C > SVGEAR_MAX_CLUSTERS)
+    return fail(SVGEAR_ERR_INVALID_ARG, "centroids: C=%d must be in [1, min(N=%d, %d)]", C, N, SVGEAR_MAX_CLUSTERS);
+  if (!x || !perm || !offsets) return fail(SVGEAR_ERR_INVALID_ARG, "centroids: null pointer");
+  if (!x_perm && !means) return SVGEAR_OK;
+  MeanPlan p = mean_plan(B, H, N, D, C);
+  st = check_ws("centroids", ws, ws_bytes, p.total);
+  if (st != SVGEAR_OK) return st;
+  char* w = static_cast<char*>(ws);
+  int32_t* cs = reinterpret_cast<int32_t*>(w + p.off_cs);
+  float* partial = reinterpret_cast<float*>(w + p.off_partial);
+  const int BH = B * H;
+  hipLaunchKernelGGL(chunk_list_kernel, dim3(BH), dim3(1024), 0, stream, offsets, C, MEAN_ROWS, cs);
+  if (dt == SVGEAR_BF16) {
+    if (D == 128) launch_partial<bf16, 128>(x, perm, offsets, cs, BH, N, C, p.maxch, partial, x_perm, stream);
+    else launch_partial<bf16, 64>(x, perm, offsets, cs, BH, N, C, p.maxch, partial, x_perm, stream);
+  } else {
+    if (D == 128) launch_partial<float, 128>(x, perm, offsets, cs, BH, N, C, p.maxch, partial, x_perm, stream);
+    else launch_partial<float, 64>(x, perm, offsets, cs, BH, N, C, p.maxch, partial, x_perm, stream);
+  }
+  if (means)
+    hipLaunchKernelGGL(km_finalize_kernel, dim3(cdiv(C * D, 256), BH), dim3(256), 0, stream, partial, offsets, cs, C,
+                       D, p.maxch, means, 0);
+  return check_launch("svgear_centroids");
+}

@@ -1,0 +1,248 @@
+"""Thin ctypes binding over libsvgear.so (the C ABI in include/svgear.h).
+
+Only argument marshalling happens here: torch supplies device memory (outputs
+and workspaces) and the current HIP stream; every step of the path runs in the
+library's HIP kernels.  If the library is missing or the tensors are not on a
+GPU, calls raise instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsvgear.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_INJECTED = range(6)
+BF16, F32 = 0, 1
+
+EXPORTS = (
+    "svgear_version", "svgear_last_error",
+    "svgear_kmeans_workspace", "svgear_kmeans",
+    "svgear_centroids_workspace", "svgear_centroids",
+    "svgear_route_workspace", "svgear_route",
+    "svgear_sparse_attn_workspace", "svgear_sparse_attn",
+)
+
+_lib = None
+
+
+class SvgearError(RuntimeError):
+    def __init__(self, call: str, status: int, msg: str):
+        super().__init__(f"{call} failed with status {status}: {msg}")
+        self.status = status
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with sparse_attention_video_amd/build.py")
+    lib = ctypes.CDLL(path)
+    P, I, F, Z, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_double
+    lib.svgear_version.restype = ctypes.c_char_p
+    lib.svgear_last_error.restype = ctypes.c_char_p
+    lib.svgear_kmeans_workspace.argtypes = [I, I, I, I, I]
+    lib.svgear_kmeans_workspace.restype = Z
+    lib.svgear_kmeans.argtypes = [P, I, I, I, I, I, I, I, P, P, P, P, P, Z, P]
+    lib.svgear_kmeans.restype = I
+    lib.svgear_centroids_workspace.argtypes = [I, I, I, I, I]
+    lib.svgear_centroids_workspace.restype = Z
+    lib.svgear_centroids.argtypes = [P, I, I, I, I, I, I, P, P, P, P, P, Z, P]
+    lib.svgear_centroids.restype = I
+    lib.svgear_route_workspace.argtypes = [I, I, I, I, I, I]
+    lib.svgear_route_workspace.restype = Z
+    lib.svgear_route.argtypes = [P, P, I, P, P, I, P, P, P, I, I, I, I, I, F, F, P, P, P, P, Z, P]
+    lib.svgear_route.restype = I
+    lib.svgear_sparse_attn_workspace.argtypes = [I, I, I, I, I, I]
+    lib.svgear_sparse_attn_workspace.restype = Z
+    lib.svgear_sparse_attn.argtypes = [P, P, P, I, P, P, I, P, I, P, P, P, I, I, I, I, F, P, P, P, Z, P]
+    lib.svgear_sparse_attn.restype = I
+    _lib = lib
+    return lib
+
+
+def version() -> str:
+    return load().svgear_version().decode()
+
+
+def _check(call: str, status: int) -> None:
+    if status != OK:
+        raise SvgearError(call, status, load().svgear_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(*ts: torch.Tensor) -> torch.device:
+    dev = ts[0].device
+    for t in ts:
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError("svgear runs on the GPU only: every tensor must be on a HIP device")
+        if t.device != dev:
+            raise ValueError("all tensors must be on the same device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+    return dev
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _workspace(nbytes: int, dev: torch.device) -> torch.Tensor:
+    ws = torch.empty(max(int(nbytes), 1) + 256, dtype=torch.uint8, device=dev)
+    off = (-ws.data_ptr()) % 256
+    return ws[off:off + max(int(nbytes), 1)]
+
+
+# ----------------------------------------------------------------------------
+def kmeans(x: torch.Tensor, centroids: torch.Tensor, iters: int, labels=None, perm=None, offsets=None, ws=None):
+    """Lloyd k-means; ``centroids`` [B,H,C,D] fp32 is updated in place.
+
+    Returns (labels [B,H,N] int32, perm [B,H,N] int32, offsets [B,H,C+1] int32)."""
+    dev = _dev(x, centroids)
+    B, H, N, D = x.shape
+    C = centroids.shape[2]
+    if centroids.dtype != torch.float32 or tuple(centroids.shape) != (B, H, C, D):
+        raise ValueError("centroids must be float32 [B,H,C,D]")
+    labels = labels if labels is not None else torch.empty((B, H, N), dtype=torch.int32, device=dev)
+    perm = perm if perm is not None else torch.empty((B, H, N), dtype=torch.int32, device=dev)
+    offsets = offsets if offsets is not None else torch.empty((B, H, C + 1), dtype=torch.int32, device=dev)
+    lib = load()
+    need = lib.svgear_kmeans_workspace(B, H, N, D, C)
+    ws = ws if ws is not None else _workspace(need, dev)
+    _check("svgear_kmeans", lib.svgear_kmeans(_ptr(x), _dtype(x), B, H, N, D, C, int(iters), _ptr(centroids),
+                                              _ptr(labels), _ptr(perm), _ptr(offsets), _ptr(ws), ws.numel(),
+                                              _stream(dev)))
+    return labels, perm, offsets
+
+
+def centroids(x: torch.Tensor, perm: torch.Tensor, offsets: torch.Tensor, want_perm: bool = True,
+              want_means: bool = True, x_perm=None, means=None, ws=None):
+    """Returns (x_perm [B,H,N,D] or None, means [B,H,C,D] fp32 or None)."""
+    dev = _dev(x, perm, offsets)
+    B, H, N, D = x.shape
+    C = offsets.shape[2] - 1
+    if want_perm and x_perm is None:
+        x_perm = torch.empty_like(x)
+    if want_means and means is None:
+        means = torch.empty((B, H, C, D), dtype=torch.float32, device=dev)
+    lib = load()
+    need = lib.svgear_centroids_workspace(B, H, N, D, C)
+    ws = ws if ws is not None else _workspace(need, dev)
+    _check("svgear_centroids", lib.svgear_centroids(_ptr(x), _dtype(x), B, H, N, D, C, _ptr(perm), _ptr(offsets),
+                                                    _ptr(x_perm if want_perm else None),
+                                                    _ptr(means if want_means else None), _ptr(ws), ws.numel(),
+                                                    _stream(dev)))
+    return (x_perm if want_perm else None), (means if want_means else None)
+
+
+def route(q_means, q_offsets, k_perm, v_perm, k_means, v_means, k_offsets, scale: float, density: float,
+          scores_in: Optional[torch.Tensor] = None, want_scores: bool = True, mask=None, scores=None, ws=None):
+    """Returns (scores [B,H,Cq,Ck] fp32 or None, mask [B,H,Cq,Ck] uint8)."""
+    dev = _dev(q_offsets, k_offsets)
+    B, H, Cq1 = q_offsets.shape
+    Cq, Ck = Cq1 - 1, k_offsets.shape[2] - 1
+    if scores_in is None:
+        _dev(q_means, k_perm, v_perm, k_means, v_means)
+        N, D = k_perm.shape[2], k_perm.shape[3]
+        dt = _dtype(k_perm)
+    else:
+        _dev(scores_in)
+        N = int(k_perm.shape[2]) if k_perm is not None else None
+        D = int(k_perm.shape[3]) if k_perm is not None else 64
+        dt = _dtype(k_perm) if k_perm is not None else F32
+        if N is None:
+            raise ValueError("k_perm (or its shape) is needed for N")
+    mask = mask if mask is not None else torch.empty((B, H, Cq, Ck), dtype=torch.uint8, device=dev)
+    if want_scores and scores is None:
+        scores = torch.empty((B, H, Cq, Ck), dtype=torch.float32, device=dev)
+    lib = load()
+    need = lib.svgear_route_workspace(B, H, N, D, Cq, Ck)
+    ws = ws if ws is not None else _workspace(need, dev)
+    _check("svgear_route", lib.svgear_route(_ptr(q_means), _ptr(q_offsets), Cq, _ptr(k_perm), _ptr(v_perm), dt,
+                                            _ptr(k_means), _ptr(v_means), _ptr(k_offsets), Ck, B, H, N, D,
+                                            float(scale), float(density), _ptr(scores_in),
+                                            _ptr(scores if want_scores else None), _ptr(mask), _ptr(ws), ws.numel(),
+                                            _stream(dev)))
+    return (scores if want_scores else None), mask
+
+
+def sparse_attn(q_perm, k_perm, v_perm, q_perm_idx, q_offsets, k_offsets, k_means, v_means, mask, scale: float,
+                want_lse: bool = False, out=None, lse=None, ws=None):
+    """Returns (out [B,H,N,D] in original token order, lse [B,H,N] fp32 or None)."""
+    dev = _dev(q_perm, k_perm, v_perm, q_perm_idx, q_offsets, k_offsets, k_means, v_means, mask)
+    B, H, N, D = q_perm.shape
+    Cq, Ck = q_offsets.shape[2] - 1, k_offsets.shape[2] - 1
+    out = out if out is not None else torch.empty_like(q_perm)
+    if want_lse and lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    lib = load()
+    need = lib.svgear_sparse_attn_workspace(B, H, N, D, Cq, Ck)
+    ws = ws if ws is not None else _workspace(need, dev)
+    _check("svgear_sparse_attn",
+           lib.svgear_sparse_attn(_ptr(q_perm), _ptr(k_perm), _ptr(v_perm), _dtype(q_perm), _ptr(q_perm_idx),
+                                  _ptr(q_offsets), Cq, _ptr(k_offsets), Ck, _ptr(k_means), _ptr(v_means), _ptr(mask),
+                                  B, H, N, D, float(scale), _ptr(out), _ptr(lse if want_lse else None), _ptr(ws),
+                                  ws.numel(), _stream(dev)))
+    return out, (lse if want_lse else None)
+
+
+# ----------------------------------------------------------------------------
+class Layer:
+    """One SVG-EAR attention layer: k-means of Q and K, permuted copies and
+    means, routing, sparse attention.  Buffers (including workspaces) are
+    allocated once per shape and reused; the centroid tensors are the cache
+    carried across denoising steps."""
+
+    def __init__(self, B, H, N, D, Cq, Ck, dtype=torch.bfloat16, device="cuda"):
+        dev = torch.device(device)
+        self.shape = (B, H, N, D, Cq, Ck)
+        lib = load()
+        e = lambda *s, dt=torch.int32: torch.empty(s, dtype=dt, device=dev)
+        self.lq, self.pq, self.oq = e(B, H, N), e(B, H, N), e(B, H, Cq + 1)
+        self.lk, self.pk, self.ok = e(B, H, N), e(B, H, N), e(B, H, Ck + 1)
+        self.qp, self.kp, self.vp = (e(B, H, N, D, dt=dtype) for _ in range(3))
+        self.qm = e(B, H, Cq, D, dt=torch.float32)
+        self.km = e(B, H, Ck, D, dt=torch.float32)
+        self.vm = e(B, H, Ck, D, dt=torch.float32)
+        self.mask = e(B, H, Cq, Ck, dt=torch.uint8)
+        self.scores = e(B, H, Cq, Ck, dt=torch.float32)
+        self.out = e(B, H, N, D, dt=dtype)
+        need = max(lib.svgear_kmeans_workspace(B, H, N, D, Cq), lib.svgear_kmeans_workspace(B, H, N, D, Ck),
+                   lib.svgear_centroids_workspace(B, H, N, D, max(Cq, Ck)),
+                   lib.svgear_route_workspace(B, H, N, D, Cq, Ck),
+                   lib.svgear_sparse_attn_workspace(B, H, N, D, Cq, Ck))
+        self.ws = _workspace(need, dev)
+
+    def forward(self, q, k, v, cq, ck, iters, density, scale=None):
+        B, H, N, D, Cq, Ck = self.shape
+        scale = 1.0 / math.sqrt(D) if scale is None else scale
+        kmeans(q, cq, iters, self.lq, self.pq, self.oq, ws=self.ws)
+        kmeans(k, ck, iters, self.lk, self.pk, self.ok, ws=self.ws)
+        centroids(q, self.pq, self.oq, x_perm=self.qp, means=self.qm, ws=self.ws)
+        centroids(k, self.pk, self.ok, x_perm=self.kp, means=self.km, ws=self.ws)
+        centroids(v, self.pk, self.ok, x_perm=self.vp, means=self.vm, ws=self.ws)
+        route(self.qm, self.oq, self.kp, self.vp, self.km, self.vm, self.ok, scale, density, mask=self.mask,
+              scores=self.scores, ws=self.ws)
+        sparse_attn(self.qp, self.kp, self.vp, self.pq, self.oq, self.ok, self.km, self.vm, self.mask, scale,
+                    out=self.out, ws=self.ws)
+        return self.out

@@ -1,0 +1,112 @@
+"""The C-ABI library loads, exports every symbol include/svgear.h declares,
+and rejects bad arguments before touching the GPU (no compute calls here)."""
+import ctypes
+import os
+import re
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "svgear.h")
+LIB = os.path.join(ROOT, "sparse_attention_video_amd", "libsvgear.so")
+
+
+def declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(svgear_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libsvgear.so is not built (run __graft_entry__.build())")
+    from sparse_attention_video_amd import svgear
+    return svgear.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared()
+    assert len(names) == 10
+    for n in names:
+        assert hasattr(lib, n), n
+    from sparse_attention_video_amd import svgear
+    assert sorted(svgear.EXPORTS) == names
+
+
+def test_version(lib):
+    assert lib.svgear_version().decode().startswith("svgear ")
+
+
+def test_workspace_queries_are_positive_and_monotone(lib):
+    a = lib.svgear_kmeans_workspace(1, 40, 75600, 128, 500)
+    b = lib.svgear_kmeans_workspace(1, 40, 75600, 128, 100)
+    assert a > b > 0
+    assert lib.svgear_route_workspace(1, 40, 75600, 128, 100, 500) > 0
+    assert lib.svgear_sparse_attn_workspace(1, 40, 75600, 128, 100, 500) > 0
+    assert lib.svgear_centroids_workspace(1, 40, 75600, 128, 500) > 0
+    assert lib.svgear_kmeans_workspace(1, 1, 10, 96, 2) == 0     # bad D
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+
+
+def call_kmeans(lib, **kw):
+    a = dict(x=FAKE, dt=0, B=1, H=1, N=100, D=64, C=4, iters=1, cent=FAKE, lab=FAKE, perm=FAKE, off=FAKE,
+             ws=None, wsb=0)
+    a.update(kw)
+    return lib.svgear_kmeans(a["x"], a["dt"], a["B"], a["H"], a["N"], a["D"], a["C"], a["iters"], a["cent"],
+                             a["lab"], a["perm"], a["off"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=96), 1), (dict(C=0), 1), (dict(C=101), 1), (dict(iters=0), 1), (dict(N=0), 1),
+    (dict(dt=7), 1), (dict(x=None), 1), (dict(B=0), 1), (dict(C=5000, N=6000), 1),
+    (dict(), 3),                                     # valid arguments but no workspace
+    (dict(ws=ctypes.c_void_p(0x1001), wsb=1 << 40), 3),  # misaligned workspace
+])
+def test_kmeans_validation(lib, kw, status):
+    assert call_kmeans(lib, **kw) == status
+    assert lib.svgear_last_error().decode()
+
+
+def test_route_and_attn_validation(lib):
+    F = FAKE
+    # density out of range, scale not positive
+    assert lib.svgear_route(F, F, 4, F, F, 0, F, F, F, 8, 1, 1, 100, 64, ctypes.c_float(0.125),
+                            ctypes.c_float(1.5), None, None, F, None, 0, None) == 1
+    assert lib.svgear_route(F, F, 4, F, F, 0, F, F, F, 8, 1, 1, 100, 64, ctypes.c_float(-1.0),
+                            ctypes.c_float(0.5), None, None, F, None, 0, None) == 1
+    assert lib.svgear_sparse_attn(F, F, F, 0, F, F, 4, F, 8, F, F, F, 1, 1, 100, 64, ctypes.c_float(0.125),
+                                  None, None, None, 0, None) == 1          # out is null
+    assert lib.svgear_sparse_attn(F, F, F, 0, F, F, 4, F, 8, F, F, F, 1, 1, 100, 64, ctypes.c_float(0.125),
+                                  F, None, None, 0, None) == 3             # no workspace
+    assert lib.svgear_centroids(F, 1, 1, 1, 100, 64, 200, F, F, F, F, None, 0, None) == 1
+
+
+def test_fault_injection_returns_injected_without_work():
+    """SVGEAR_FAULT=<call> makes that call report SVGEAR_ERR_INJECTED (a caller's
+    dense fallback can be tested with the oracle standing in)."""
+    code = (
+        "import ctypes, sys\n"
+        f"sys.path.insert(0, {ROOT!r})\n"
+        "from sparse_attention_video_amd import svgear\n"
+        "lib = svgear.load()\n"
+        "F = ctypes.c_void_p(0x1000)\n"
+        "st = lib.svgear_kmeans(F, 0, 1, 1, 100, 64, 4, 1, F, F, F, F, None, 0, None)\n"
+        "st2 = lib.svgear_sparse_attn(F, F, F, 0, F, F, 4, F, 8, F, F, F, 1, 1, 100, 64, ctypes.c_float(0.1), F, None, None, 0, None)\n"
+        "print(st, st2)\n"
+    )
+    env = dict(os.environ, SVGEAR_FAULT="kmeans")
+    out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0, out.stderr
+    assert out.stdout.split() == ["5", "3"]
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    from sparse_attention_video_amd import svgear
+    x = torch.zeros((1, 1, 64, 64))
+    with pytest.raises(ValueError):
+        svgear.kmeans(x, torch.zeros((1, 1, 4, 64)), 1)

@@ -1,0 +1,307 @@
+"""GPU parity: every C-ABI call against the fp64 oracle on the same seeded
+inputs, teacher-forced (the GPU gets the oracle's inputs to that stage),
+at sizes that span several tiles and ragged tails; then end to end.
+
+Tolerances.  Labels: equal except where the GPU's centroid is within
+1e-5 * max(1, D) of the oracle's in squared distance.  Means: the rigorous
+fp32 summation bound (n + 2) u max|x|.  Masks: bit-exact given the same
+float32 ratios.  Attention output vs the fp64 oracle: bf16 inputs max-abs
+<= 2e-2 and mean-abs <= 2e-3; fp32 inputs max-abs <= 1e-4 and mean-abs
+<= 1e-5 (fp32 MFMA products, fp32 softmax, ~1e-6 relative).  Route ratios:
+relative 2e-3 (see the design notes for the derivation)."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import svgear_oracle as orc
+from synth.gen import WORKLOADS, layer_inputs, scaled
+from tests.helpers import check_labels_near_ties, f32, host, i32, mean_bound, to_dev
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # name: (dtype, B, H, N, D, comps, zipf, Cq, Ck)
+    "f32-d64": ("f32", 1, 2, 2500, 64, 12, None, 13, 37),
+    "bf16-d128": ("bf16", 1, 2, 5000, 128, 24, 1.1, 16, 53),
+    "bf16-d64": ("bf16", 2, 1, 4500, 64, 24, 1.1, 11, 41),
+    "f32-d128": ("f32", 1, 1, 3000, 128, 10, None, 9, 40),
+}
+ATOL = {"bf16": (2e-2, 2e-3), "f32": (1e-4, 1e-5)}
+
+
+@pytest.fixture(scope="module")
+def sv():
+    import sparse_attention_video_amd as pkg
+    pkg.load()
+    assert torch.cuda.is_available()
+    return pkg
+
+
+def make(name, seed=11):
+    dt, B, H, N, D, comps, zipf, Cq, Ck = CASES[name]
+    w = scaled(WORKLOADS["tiny"], B=B, H=H, N=N, D=D, dtype=dt, comps=comps, zipf=zipf, Cq=Cq, Ck=Ck,
+               seed=seed, density=0.3)
+    return w, layer_inputs(w)
+
+
+def stack(arrs):
+    return np.stack(arrs)
+
+
+def reshape4(a, w):
+    return a.reshape(w.B, w.H, *a.shape[1:])
+
+
+@pytest.fixture(scope="module")
+def ref_cache():
+    return {}
+
+
+def oracle_layer(name, ref_cache, iters=3, density=0.3):
+    key = (name, iters, density)
+    if key not in ref_cache:
+        w, x = make(name)
+        sc = 1.0 / np.sqrt(w.D)
+        outs = [orc.layer(x["q"][h], x["k"][h], x["v"][h], x["cq0"][h], x["ck0"][h], iters, density, sc)
+                for h in range(w.B * w.H)]
+        ref_cache[key] = (w, x, outs, sc)
+    return ref_cache[key]
+
+
+# ------------------------------------------------------------------ k-means
+@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("which", ["q", "k"])
+def test_kmeans_rounds_teacher_forced(sv, name, which):
+    w, x = make(name)
+    X = x[which]
+    C = w.Cq if which == "q" else w.Ck
+    Cs = x["cq0"] if which == "q" else x["ck0"]
+    xd = to_dev(reshape4(X, w), w.dtype)
+    for rnd in range(3):
+        cent = f32(reshape4(Cs, w))
+        lab, perm, off = sv.kmeans(xd, cent, 1)
+        lab, perm, off, cent = (host(t).reshape(w.B * w.H, -1) for t in (lab, perm, off, cent))
+        cent = cent.reshape(w.B * w.H, C, w.D)
+        nxt = []
+        for h in range(w.B * w.H):
+            lo = orc.assign(X[h], Cs[h])
+            nbad = check_labels_near_ties(X[h], Cs[h], lab[h], lo)
+            if nbad == 0:
+                po, oo = orc.permute(lo, C)
+                np.testing.assert_array_equal(perm[h], po)
+                np.testing.assert_array_equal(off[h], oo)
+                c1 = orc.update(X[h], lo, Cs[h])
+                bound = mean_bound(X[h], po, oo)
+                err = np.abs(cent[h] - c1).max(axis=1)
+                assert np.all(err <= bound + 1e-30), (err.max(), bound.max())
+                empty = np.diff(oo) == 0
+                np.testing.assert_array_equal(cent[h][empty], Cs[h][empty].astype(np.float32))
+            nxt.append(orc.update(X[h], lo, Cs[h]).astype(np.float32))
+        Cs = np.stack(nxt)
+
+
+@pytest.mark.parametrize("name", ["bf16-d128", "f32-d64"])
+def test_kmeans_multi_round_matches_lloyd(sv, name):
+    w, x = make(name)
+    X, C0 = x["k"], x["ck0"]
+    cent = f32(reshape4(C0, w))
+    lab, perm, off = sv.kmeans(to_dev(reshape4(X, w), w.dtype), cent, 6)
+    lab = host(lab).reshape(w.B * w.H, -1)
+    cent = host(cent).reshape(w.B * w.H, w.Ck, w.D)
+    for h in range(w.B * w.H):
+        Co, lo = orc.lloyd(X[h], C0[h], 6)
+        assert (lab[h] != lo).mean() < 1e-3
+        if (lab[h] == lo).all():
+            po, oo = orc.permute(lo, w.Ck)
+            assert (np.abs(cent[h] - Co).max(axis=1) <= mean_bound(X[h], po, oo) + 1e-6).all()
+
+
+def test_kmeans_empty_cluster_keeps_centroid(sv):
+    w, x = make("bf16-d64")
+    X = x["q"]
+    C0 = x["cq0"].copy()
+    C0[:, 3] = 1000.0          # far away: no member
+    C0[:, 5] = C0[:, 4]        # duplicate of centroid 4: ties go to 4, so 5 is empty
+    cent = f32(reshape4(C0, w))
+    lab, perm, off = sv.kmeans(to_dev(reshape4(X, w), w.dtype), cent, 1)
+    lab = host(lab).reshape(w.B * w.H, -1)
+    off = host(off).reshape(w.B * w.H, -1)
+    cent = host(cent).reshape(w.B * w.H, w.Cq, w.D)
+    for h in range(w.B * w.H):
+        lo = orc.assign(X[h], C0[h])
+        assert check_labels_near_ties(X[h], C0[h], lab[h], lo) == 0
+        assert off[h][4] == off[h][3] and off[h][6] == off[h][5]
+        np.testing.assert_array_equal(cent[h][3], C0[h][3])
+        np.testing.assert_array_equal(cent[h][5], C0[h][5])
+
+
+def test_kmeans_singletons_and_single_cluster(sv):
+    w, x = make("f32-d64")
+    X = x["k"][:1, :300]
+    for C0 in (X.copy(), X[:, :1].copy()):
+        C = C0.shape[1]
+        cent = f32(C0[:, None])
+        lab, perm, off = sv.kmeans(f32(X[:, None]), cent, 2)
+        Co, lo = orc.lloyd(X[0], C0[0], 2)
+        np.testing.assert_array_equal(host(lab)[0, 0], lo)
+        np.testing.assert_allclose(host(cent)[0, 0], Co, rtol=0, atol=1e-5)
+
+
+# ------------------------------------------------------------------ centroids
+@pytest.mark.parametrize("name", list(CASES))
+def test_centroids_gather_and_means(sv, name, ref_cache):
+    w, x, outs, sc = oracle_layer(name, ref_cache)
+    for which, perm_key, off_key in (("q", "pq", "oq"), ("k", "pk", "ok"), ("v", "pk", "ok")):
+        X = x[which]
+        perm = np.stack([o[perm_key] for o in outs])
+        off = np.stack([o[off_key] for o in outs])
+        xp, mu = sv.centroids(to_dev(reshape4(X, w), w.dtype), i32(reshape4(perm, w)), i32(reshape4(off, w)))
+        xp = host(xp).reshape(w.B * w.H, w.N, w.D)
+        mu = host(mu).reshape(w.B * w.H, off.shape[1] - 1, w.D)
+        for h in range(w.B * w.H):
+            np.testing.assert_array_equal(xp[h], X[h][perm[h]])
+            ref = orc.means(X[h], perm[h], off[h])
+            err = np.abs(mu[h] - ref).max(axis=1)
+            assert (err <= mean_bound(X[h], perm[h], off[h]) + 1e-30).all()
+
+
+# ------------------------------------------------------------------ route
+@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("density", [0.1, 0.3, 1.0])
+def test_route_teacher_forced(sv, name, density, ref_cache):
+    w, x, outs, sc = oracle_layer(name, ref_cache)
+    BH = w.B * w.H
+    g = lambda key: np.stack([o[key] for o in outs])
+    pk = g("pk")
+    Kp = np.stack([x["k"][h][pk[h]] for h in range(BH)])
+    Vp = np.stack([x["v"][h][pk[h]] for h in range(BH)])
+    qbar, kbar, vbar, oq, ok = g("qbar"), g("kbar"), g("vbar"), g("oq"), g("ok")
+    args = (f32(reshape4(qbar, w)), i32(reshape4(oq, w)), to_dev(reshape4(Kp, w), w.dtype),
+            to_dev(reshape4(Vp, w), w.dtype), f32(reshape4(kbar, w)), f32(reshape4(vbar, w)), i32(reshape4(ok, w)))
+    scores, mask = sv.route(*args, sc, density)
+    scores = host(scores).reshape(BH, w.Cq, w.Ck)
+    mask = host(mask).reshape(BH, w.Cq, w.Ck)
+    for h in range(BH):
+        r_o, m_o = orc.route(qbar[h], oq[h], Kp[h], Vp[h], kbar[h], vbar[h], ok[h], sc, density)
+        rowmax = r_o.max(axis=1, keepdims=True).astype(np.float64)
+        err = np.abs(scores[h].astype(np.float64) - r_o)
+        assert (err <= 2e-3 * r_o + 1e-7 * rowmax + 1e-37).all(), (err / (r_o + 1e-30)).max()
+        # a mask from the GPU's own ratios may differ only at near-ties of the ratios
+        for i in np.flatnonzero((mask[h] != m_o).any(axis=1)):
+            sel_o = m_o[i] == 1
+            thr = r_o[i][sel_o].min()
+            diff = np.flatnonzero(mask[h][i] != m_o[i])
+            assert np.all(np.abs(r_o[i][diff] - thr) <= 4e-3 * thr + 1e-7 * rowmax[i]), (i, diff)
+    # bit-exact selection given the same float32 ratios
+    r_all = np.stack([orc.route(qbar[h], oq[h], Kp[h], Vp[h], kbar[h], vbar[h], ok[h], sc, density)[0]
+                      for h in range(BH)])
+    _, mask2 = sv.route(*args, sc, density, scores_in=f32(reshape4(r_all, w)))
+    mask2 = host(mask2).reshape(BH, w.Cq, w.Ck)
+    for h in range(BH):
+        q_sizes, k_sizes = np.diff(oq[h]), np.diff(ok[h])
+        np.testing.assert_array_equal(mask2[h], orc.select(r_all[h], q_sizes, k_sizes, density, w.N))
+
+
+def test_route_select_ties_and_empty(sv):
+    """Hand-built ratios with ties, an empty key cluster and an empty query cluster."""
+    N, Cq, Ck = 10, 3, 5
+    ok = np.array([[[0, 3, 4, 8, 8, 10]]], dtype=np.int32)        # sizes 3, 1, 4, 0, 2
+    oq = np.array([[[0, 6, 6, 10]]], dtype=np.int32)              # query cluster 1 is empty
+    r = np.array([[[[0.5, 0.9, 0.5, 0.7, 0.1], [1, 1, 1, 1, 1], [0.0, 0.0, 0.0, 0.0, 0.0]]]], dtype=np.float32)
+    kp = torch.zeros((1, 1, N, 64), dtype=torch.float32, device="cuda")
+    _, mask = sv.route(None, i32(oq), kp, None, None, None, i32(ok), 0.125, 0.5, scores_in=f32(r))
+    mask = host(mask)[0, 0]
+    assert mask.tolist() == [[1, 1, 1, 0, 0], [0, 0, 0, 0, 0], [1, 1, 0, 0, 0]]
+
+
+# ------------------------------------------------------------------ attention
+def attn_inputs(w, x, outs, mask=None):
+    BH = w.B * w.H
+    g = lambda key: np.stack([o[key] for o in outs])
+    pq, pk = g("pq"), g("pk")
+    take = lambda a, p: np.stack([a[h][p[h]] for h in range(BH)])
+    Qp, Kp, Vp = take(x["q"], pq), take(x["k"], pk), take(x["v"], pk)
+    m = g("mask") if mask is None else mask
+    dev = (to_dev(reshape4(Qp, w), w.dtype), to_dev(reshape4(Kp, w), w.dtype), to_dev(reshape4(Vp, w), w.dtype),
+           i32(reshape4(pq, w)), i32(reshape4(g("oq"), w)), i32(reshape4(g("ok"), w)),
+           f32(reshape4(g("kbar"), w)), f32(reshape4(g("vbar"), w)),
+           torch.from_numpy(reshape4(m.astype(np.uint8), w)).cuda())
+    return dev, m
+
+
+@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("maskkind", ["routed", "dense", "none", "random"])
+def test_sparse_attn_teacher_forced(sv, name, maskkind, ref_cache):
+    w, x, outs, sc = oracle_layer(name, ref_cache)
+    BH = w.B * w.H
+    m = np.stack([o["mask"] for o in outs])
+    if maskkind == "dense":
+        m = np.ones_like(m)
+    elif maskkind == "none":
+        m = np.zeros_like(m)
+    elif maskkind == "random":
+        m = (np.random.default_rng(5).random(m.shape) < 0.35).astype(np.uint8)
+    dev, m = attn_inputs(w, x, outs, m)
+    out, lse = sv.sparse_attn(*dev, sc, want_lse=True)
+    out = host(out).reshape(BH, w.N, w.D)
+    lse = host(lse).reshape(BH, w.N)
+    amax, amean = ATOL[w.dtype]
+    for h in range(BH):
+        o = outs[h]
+        O, L = orc.attend(x["q"][h], x["k"][h], x["v"][h], o["pq"], o["oq"], o["pk"], o["ok"], o["kbar"], o["vbar"],
+                          m[h], sc)
+        err = np.abs(out[h] - O)
+        assert err.max() <= amax and err.mean() <= amean, (err.max(), err.mean())
+        assert np.abs(lse[h] - L).max() <= (1e-2 if w.dtype == "bf16" else 1e-4)
+
+
+def test_sparse_attn_density_one_is_full_attention(sv, ref_cache):
+    w, x, outs, sc = oracle_layer("bf16-d128", ref_cache)
+    m = np.stack([(np.diff(o["ok"]) > 0)[None, :].repeat(w.Cq, 0) for o in outs]).astype(np.uint8)
+    dev, _ = attn_inputs(w, x, outs, m)
+    out, _ = sv.sparse_attn(*dev, sc)
+    out = host(out).reshape(w.B * w.H, w.N, w.D)
+    for h in range(w.B * w.H):
+        ref = orc.full_attention(x["q"][h], x["k"][h], x["v"][h], sc)
+        err = np.abs(out[h] - ref)
+        assert err.max() <= 2e-2 and err.mean() <= 2e-3
+
+
+# ------------------------------------------------------------------ end to end
+@pytest.mark.parametrize("name", ["f32-d64", "bf16-d128"])
+def test_layer_end_to_end(sv, name, ref_cache):
+    w, x, outs, sc = oracle_layer(name, ref_cache, iters=3, density=0.3)
+    BH = w.B * w.H
+    L = sv.Layer(w.B, w.H, w.N, w.D, w.Cq, w.Ck, dtype=torch.bfloat16 if w.dtype == "bf16" else torch.float32)
+    cq, ck = f32(reshape4(x["cq0"], w)), f32(reshape4(x["ck0"], w))
+    out = L.forward(to_dev(reshape4(x["q"], w), w.dtype), to_dev(reshape4(x["k"], w), w.dtype),
+                    to_dev(reshape4(x["v"], w), w.dtype), cq, ck, 3, 0.3, sc)
+    out = host(out).reshape(BH, w.N, w.D)
+    lq, lk = host(L.lq).reshape(BH, -1), host(L.lk).reshape(BH, -1)
+    mask = host(L.mask).reshape(BH, w.Cq, w.Ck)
+    amax, amean = ATOL[w.dtype]
+    for h in range(BH):
+        o = outs[h]
+        np.testing.assert_array_equal(lq[h], o["lq"])
+        np.testing.assert_array_equal(lk[h], o["lk"])
+        agree = (mask[h] == o["mask"]).mean()
+        assert agree > 0.97
+        if agree == 1.0:
+            err = np.abs(out[h] - o["O"])
+            assert err.max() <= amax and err.mean() <= amean, (err.max(), err.mean())
+
+
+def test_layer_is_deterministic(sv):
+    w, x = make("bf16-d128")
+    sc = 1.0 / np.sqrt(w.D)
+    L = sv.Layer(w.B, w.H, w.N, w.D, w.Cq, w.Ck)
+    res = []
+    for _ in range(2):
+        cq, ck = f32(reshape4(x["cq0"], w)), f32(reshape4(x["ck0"], w))
+        out = L.forward(to_dev(reshape4(x["q"], w), "bf16"), to_dev(reshape4(x["k"], w), "bf16"),
+                        to_dev(reshape4(x["v"], w), "bf16"), cq, ck, 4, 0.25, sc)
+        res.append((out.clone(), L.scores.clone(), cq.clone(), ck.clone()))
+    for a, b in zip(res[0], res[1]):
+        assert torch.equal(a, b)
