@@ -213,7 +213,9 @@ def test_route_select_ties_and_empty(sv):
     kp = torch.zeros((1, 1, N, 64), dtype=torch.float32, device="cuda")
     _, mask = sv.route(None, i32(oq), kp, None, None, None, i32(ok), 0.125, 0.5, scores_in=f32(r))
     mask = host(mask)[0, 0]
-    assert mask.tolist() == [[1, 1, 1, 0, 0], [0, 0, 0, 0, 0], [1, 1, 0, 0, 0]]
+    # row 2: all ratios tie at 0, so clusters go in index order: 0 (3 keys), 1 (4), 2 (8 >= 5, stop)
+    assert mask.tolist() == [[1, 1, 1, 0, 0], [0, 0, 0, 0, 0], [1, 1, 1, 0, 0]]
+    np.testing.assert_array_equal(mask, orc.select(r[0, 0], np.diff(oq[0, 0]), np.diff(ok[0, 0]), 0.5, N))
 
 
 # ------------------------------------------------------------------ attention
