@@ -389,6 +389,339 @@ __global__ void __launch_bounds__(256) attn_kernel(const T* __restrict__ qp, con
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 path.  Same algorithm, arranged for throughput:
+//  * each thread owns one staging unit (4 consecutive keys x 8 dims); the
+//    next tile's K/V rows are loaded into registers while the current tile
+//    computes, then written to the other LDS buffer (one barrier per tile);
+//  * K rows are copied as raw 16-byte vectors; V is transposed to V^T with
+//    byte permutes on the way into LDS;
+//  * the running max is raised only when a tile's max exceeds it by more
+//    than AT_LAZY (log2 units), so O and the sum are rarely rescaled (the
+//    weights stay <= 2^AT_LAZY, and the final normalisation uses the same
+//    max, so the result is unchanged);
+//  * skipped clusters (pseudo-keys, bf16 hi + lo) run in a second loop.
+// ---------------------------------------------------------------------------
+constexpr float AT_LAZY = 8.f;
+
+__device__ __forceinline__ uint32_t perm_b32(uint32_t hi_src, uint32_t lo_src, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi_src, lo_src, sel);
+}
+
+template <int D>
+__global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restrict__ qp, const bf16* __restrict__ kp,
+                                                           const bf16* __restrict__ vp, const int32_t* __restrict__ qidx,
+                                                           const int32_t* __restrict__ qoff,
+                                                           const int32_t* __restrict__ tstart, int Cq,
+                                                           const int32_t* __restrict__ koff, int Ck,
+                                                           const float* __restrict__ kmeans,
+                                                           const float* __restrict__ vmeans,
+                                                           const uint8_t* __restrict__ mask, int N, float sl2,
+                                                           bf16* __restrict__ out, float* __restrict__ lse) {
+  constexpr int KS = D / 16, DT = D / 32;
+  constexpr int SK = D + 8, SV = AT_BN + 8;
+  constexpr int NUNIT = (AT_BN / 4) * (D / 8);
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  bf16* sK = reinterpret_cast<bf16*>(smem);                 // [2][64][SK]
+  bf16* sV = sK + 2 * AT_BN * SK;                           // [2][D][SV]  (V^T)
+  float* sBias = reinterpret_cast<float*>(sV + 2 * D * SV);  // [64]
+  int* sSrc = reinterpret_cast<int*>(sBias + AT_BN);        // [2][64]
+  int* sSelStart = sSrc + 2 * AT_BN;
+  int* sSelPre = sSelStart + Ck;
+  int* sComp = sSelPre + Ck + 1;
+  __shared__ int sScan[16];
+  __shared__ int sInfo[4];
+
+  const int bh = blockIdx.y, tid = threadIdx.x, lane = lane_id(), w = wave_id();
+  const int half = lane >> 5, col = lane & 31;
+  const int32_t* ts = tstart + (size_t)bh * (Cq + 1);
+  if ((int)blockIdx.x >= ts[Cq]) return;
+  if (tid == 0) sInfo[0] = upper_index(ts, Cq, blockIdx.x);
+  __syncthreads();
+  const int ci = sInfo[0];
+  const int32_t* qo = qoff + (size_t)bh * (Cq + 1);
+  const int32_t* ko = koff + (size_t)bh * (Ck + 1);
+  const int row0 = qo[ci] + ((int)blockIdx.x - ts[ci]) * AT_BM;
+  const int rowEnd = qo[ci + 1];
+  const uint8_t* mrow = mask + ((size_t)bh * Cq + ci) * Ck;
+  {
+    const int per = (Ck + 255) / 256;
+    const int j0 = tid * per, j1 = min(Ck, j0 + per);
+    int nsel = 0, ncomp = 0, nkeys = 0;
+    for (int j = j0; j < j1; ++j) {
+      const int nj = ko[j + 1] - ko[j];
+      if (nj > 0) {
+        if (mrow[j]) { ++nsel; nkeys += nj; } else { ++ncomp; }
+      }
+    }
+    int tsel, tcomp, tkeys;
+    int psel = block_exscan(nsel, sScan, &tsel);
+    int pcomp = block_exscan(ncomp, sScan, &tcomp);
+    int pkeys = block_exscan(nkeys, sScan, &tkeys);
+    for (int j = j0; j < j1; ++j) {
+      const int nj = ko[j + 1] - ko[j];
+      if (nj > 0) {
+        if (mrow[j]) { sSelStart[psel] = ko[j]; sSelPre[psel] = pkeys; ++psel; pkeys += nj; }
+        else { sComp[pcomp++] = j; }
+      }
+    }
+    if (tid == 0) { sSelPre[tsel] = tkeys; sInfo[1] = tsel; sInfo[2] = tcomp; sInfo[3] = tkeys; }
+    __syncthreads();
+  }
+  const int nsel = sInfo[1], ncomp = sInfo[2], nkeys = sInfo[3];
+  const int nreal = (nkeys + AT_BN - 1) / AT_BN;
+  const int npseudo = (ncomp + AT_BN - 1) / AT_BN;
+
+  const bf16* qb = qp + (size_t)bh * N * D;
+  const bf16* kb = kp + (size_t)bh * N * D;
+  const bf16* vb = vp + (size_t)bh * N * D;
+  const int qrow = row0 + 32 * w + col;
+  const bool qok = qrow < rowEnd;
+  bf16x8 bq[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    bf16x8 v = {};
+    if (qok) v = *reinterpret_cast<const bf16x8*>(qb + (size_t)qrow * D + 16 * ks + 8 * half);
+    bq[ks] = v;
+  }
+  f32x16 o[DT];
+#pragma unroll
+  for (int t = 0; t < DT; ++t) o[t] = f32x16{};
+  float m_run = -1e30f, l_run = 0.f;
+
+  // staging unit: keys 4*g4 .. 4*g4+3, dims d0 .. d0+7
+  const bool has_unit = tid < NUNIT;
+  const int g4 = tid & 15, d0 = (tid >> 4) * 8;
+  auto src_of = [&](int p) -> int {
+    if (p >= nkeys) return -1;
+    const int s = upper_index(sSelPre, nsel, p);
+    return sSelStart[s] + (p - sSelPre[s]);
+  };
+  u32x4 pk[4], pv[4];
+  auto issue = [&](int kt) {
+    if (has_unit) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int src = sSrc[(kt & 1) * AT_BN + 4 * g4 + r];
+        u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+        if (src >= 0) {
+          a = ld16(kb + (size_t)src * D + d0);
+          b = ld16(vb + (size_t)src * D + d0);
+        }
+        pk[r] = a;
+        pv[r] = b;
+      }
+    }
+  };
+  auto commit = [&](int buf) {
+    if (has_unit) {
+      bf16* K = sK + buf * AT_BN * SK;
+      bf16* V = sV + buf * D * SV;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) st16(&K[(4 * g4 + r) * SK + d0], pk[r]);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        uint2 lo, hi;
+        lo.x = perm_b32(pv[1][m], pv[0][m], 0x05040100u);
+        lo.y = perm_b32(pv[3][m], pv[2][m], 0x05040100u);
+        hi.x = perm_b32(pv[1][m], pv[0][m], 0x07060302u);
+        hi.y = perm_b32(pv[3][m], pv[2][m], 0x07060302u);
+        *reinterpret_cast<uint2*>(&V[(d0 + 2 * m) * SV + 4 * g4]) = lo;
+        *reinterpret_cast<uint2*>(&V[(d0 + 2 * m + 1) * SV + 4 * g4]) = hi;
+      }
+    }
+  };
+
+  // one tile of keys already in LDS buffer `buf`: S^T, online softmax, O^T += V^T P^T
+  auto compute = [&](int buf, int lim, bool pseudo) {
+    const bf16* Kh = pseudo ? sK : sK + buf * AT_BN * SK;
+    const bf16* Vh = pseudo ? sV : sV + buf * D * SV;
+    f32x16 s[2];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      f32x16 acc = {};
+      const int krow = sub * 32 + col;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        acc = mfma_bf16(*reinterpret_cast<const bf16x8*>(&Kh[krow * SK + 16 * ks + 8 * half]), bq[ks], acc);
+      if (pseudo) {
+        const bf16* Kl = sK + AT_BN * SK;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          acc = mfma_bf16(*reinterpret_cast<const bf16x8*>(&Kl[krow * SK + 16 * ks + 8 * half]), bq[ks], acc);
+      }
+      s[sub] = acc;
+    }
+    if (pseudo) {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[sub][r] = fmaf(s[sub][r], sl2, sBias[sub * 32 + c_row(r, half)]);
+    } else {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[sub][r] *= sl2;
+      if (lim < AT_BN) {
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (sub * 32 + c_row(r, half) >= lim) s[sub][r] = -INFINITY;
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
+    mx = fmaxf(mx, shfl_xor(mx, 32));
+    const bool grow = mx > m_run + AT_LAZY;
+    if (ballot(grow)) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int t = 0; t < DT; ++t)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
+    }
+    float lsum = 0.f;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = exp2f(s[sub][r] - m_run);
+        s[sub][r] = p;
+        lsum += p;
+      }
+    l_run += lsum;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+      const int sub = st >> 1, tp = st & 1;
+      bf16x8 pb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[e] = (bf16)s[sub][8 * tp + e];
+      const int k0 = 16 * st + 4 * half;
+#pragma unroll
+      for (int t = 0; t < DT; ++t) {
+        const int d = 32 * t + col;
+        const bf16x4 x0 = *reinterpret_cast<const bf16x4*>(&Vh[d * SV + k0]);
+        const bf16x4 x1 = *reinterpret_cast<const bf16x4*>(&Vh[d * SV + k0 + 8]);
+        bf16x8 a;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { a[e] = x0[e]; a[e + 4] = x1[e]; }
+        o[t] = mfma_bf16(a, pb, o[t]);
+        if (pseudo) {
+          const bf16* Vl = sV + D * SV;
+          const bf16x4 y0 = *reinterpret_cast<const bf16x4*>(&Vl[d * SV + k0]);
+          const bf16x4 y1 = *reinterpret_cast<const bf16x4*>(&Vl[d * SV + k0 + 8]);
+          bf16x8 b;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { b[e] = y0[e]; b[e + 4] = y1[e]; }
+          o[t] = mfma_bf16(b, pb, o[t]);
+        }
+      }
+    }
+  };
+
+  // ---- selected keys: packed 64-key tiles, double buffered
+  if (nreal > 0) {
+    if (tid < AT_BN) sSrc[tid] = src_of(tid);
+    if (tid < AT_BN && nreal > 1) sSrc[AT_BN + tid] = src_of(AT_BN + tid);
+    __syncthreads();
+    issue(0);
+    commit(0);
+    __syncthreads();
+    for (int kt = 0; kt < nreal; ++kt) {
+      const bool more = kt + 1 < nreal;
+      if (more) issue(kt + 1);
+      compute(kt & 1, nkeys - kt * AT_BN, false);
+      if (more) commit((kt + 1) & 1);
+      if (kt + 2 < nreal && tid < AT_BN) sSrc[(kt & 1) * AT_BN + tid] = src_of((kt + 2) * AT_BN + tid);
+      __syncthreads();
+    }
+  }
+
+  // ---- skipped non-empty clusters: pseudo-keys k_bar_j (hi, lo), v_bar_j (hi, lo), bias log2 n_j
+  for (int pt = 0; pt < npseudo; ++pt) {
+    if (has_unit) {
+      float kf[4][8], vf[4][8];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int c = pt * AT_BN + 4 * g4 + r;
+        f32x4 k0 = {}, k1 = {}, v0 = {}, v1 = {};
+        float bias = -INFINITY;
+        if (c < ncomp) {
+          const int j = sComp[c];
+          const float* kr = kmeans + ((size_t)bh * Ck + j) * D + d0;
+          const float* vr = vmeans + ((size_t)bh * Ck + j) * D + d0;
+          k0 = *reinterpret_cast<const f32x4*>(kr);
+          k1 = *reinterpret_cast<const f32x4*>(kr + 4);
+          v0 = *reinterpret_cast<const f32x4*>(vr);
+          v1 = *reinterpret_cast<const f32x4*>(vr + 4);
+          bias = log2f((float)(ko[j + 1] - ko[j]));
+        }
+        if (d0 == 0) sBias[4 * g4 + r] = bias;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { kf[r][e] = k0[e]; kf[r][e + 4] = k1[e]; vf[r][e] = v0[e]; vf[r][e + 4] = v1[e]; }
+      }
+      bf16* Kh = sK;
+      bf16* Kl = sK + AT_BN * SK;
+      bf16* Vh = sV;
+      bf16* Vl = sV + D * SV;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        bf16x8 h, l;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          bf16 hh, ll;
+          split_bf16(kf[r][e], hh, ll);
+          h[e] = hh;
+          l[e] = ll;
+        }
+        *reinterpret_cast<bf16x8*>(&Kh[(4 * g4 + r) * SK + d0]) = h;
+        *reinterpret_cast<bf16x8*>(&Kl[(4 * g4 + r) * SK + d0]) = l;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        bf16x4 h, l;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          bf16 hh, ll;
+          split_bf16(vf[r][e], hh, ll);
+          h[r] = hh;
+          l[r] = ll;
+        }
+        *reinterpret_cast<bf16x4*>(&Vh[(d0 + e) * SV + 4 * g4]) = h;
+        *reinterpret_cast<bf16x4*>(&Vl[(d0 + e) * SV + 4 * g4]) = l;
+      }
+    }
+    __syncthreads();
+    compute(0, AT_BN, true);
+    __syncthreads();
+  }
+
+  // ---- epilogue
+  const float l_tot = l_run + shfl_xor(l_run, 32);
+  if (qok) {
+    const int orig = qidx[(size_t)bh * N + qrow];
+    const float inv = 1.f / l_tot;
+    bf16* orow = out + ((size_t)bh * N + orig) * D;
+#pragma unroll
+    for (int t = 0; t < DT; ++t)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = (bf16)(o[t][4 * g + e] * inv);
+        *reinterpret_cast<bf16x4*>(orow + 32 * t + 8 * g + 4 * half) = v;
+      }
+    if (lse && half == 0) lse[(size_t)bh * N + orig] = (m_run + log2f(l_tot)) * 0.69314718055994531f;
+  }
+}
+
 // ---------------------------------------------------------------- host side
 struct AtPlan {
   int BH, maxt;
@@ -410,11 +743,19 @@ static void launch_attn(const void* q, const void* k, const void* v, const int32
                         const int32_t* ts, int Cq, const int32_t* koff, int Ck, const float* km, const float* vm,
                         const uint8_t* mask, int BH, int N, float sl2, void* out, float* lse, int maxt,
                         hipStream_t st) {
-  using L = AttnLds<T, D>;
-  const size_t lds = L::fixed + (size_t)(3 * Ck + 1) * sizeof(int);
-  (void)hipFuncSetAttribute((const void*)attn_kernel<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  hipLaunchKernelGGL((attn_kernel<T, D>), dim3(maxt, BH), dim3(256), lds, st, (const T*)q, (const T*)k, (const T*)v,
-                     qidx, qoff, ts, Cq, koff, Ck, km, vm, mask, N, sl2, (T*)out, lse);
+  if constexpr (sizeof(T) == 2) {
+    const size_t lds = (size_t)2 * AT_BN * (D + 8) * 2 + (size_t)2 * D * (AT_BN + 8) * 2 + AT_BN * 4 +
+                       2 * AT_BN * 4 + (size_t)(3 * Ck + 1) * sizeof(int);
+    (void)hipFuncSetAttribute((const void*)attn_bf16_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipLaunchKernelGGL((attn_bf16_kernel<D>), dim3(maxt, BH), dim3(256), lds, st, (const bf16*)q, (const bf16*)k,
+                       (const bf16*)v, qidx, qoff, ts, Cq, koff, Ck, km, vm, mask, N, sl2, (bf16*)out, lse);
+  } else {
+    using L = AttnLds<T, D>;
+    const size_t lds = L::fixed + (size_t)(3 * Ck + 1) * sizeof(int);
+    (void)hipFuncSetAttribute((const void*)attn_kernel<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipLaunchKernelGGL((attn_kernel<T, D>), dim3(maxt, BH), dim3(256), lds, st, (const T*)q, (const T*)k,
+                       (const T*)v, qidx, qoff, ts, Cq, koff, Ck, km, vm, mask, N, sl2, (T*)out, lse);
+  }
 }
 
 }  // namespace svg
