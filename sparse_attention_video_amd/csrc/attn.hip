@@ -403,6 +403,7 @@ __global__ void __launch_bounds__(256) attn_kernel(const T* __restrict__ qp, con
 //  * skipped clusters (pseudo-keys, bf16 hi + lo) run in a second loop.
 // ---------------------------------------------------------------------------
 constexpr float AT_LAZY = 8.f;
+constexpr int AT_XCDS = 8;  // MI355X: 8 XCDs, each with its own L2
 
 __device__ __forceinline__ uint32_t perm_b32(uint32_t hi_src, uint32_t lo_src, uint32_t sel) {
   return __builtin_amdgcn_perm(hi_src, lo_src, sel);
@@ -417,7 +418,8 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
                                                            const float* __restrict__ kmeans,
                                                            const float* __restrict__ vmeans,
                                                            const uint8_t* __restrict__ mask, int N, float sl2,
-                                                           bf16* __restrict__ out, float* __restrict__ lse) {
+                                                           bf16* __restrict__ out, float* __restrict__ lse,
+                                                           int maxt, int BHn) {
   constexpr int KS = D / 16, DT = D / 32;
   constexpr int SK = D + 8, SV = AT_BN + 8;
   constexpr int NUNIT = (AT_BN / 4) * (D / 8);
@@ -432,16 +434,23 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
   __shared__ int sScan[16];
   __shared__ int sInfo[4];
 
-  const int bh = blockIdx.y, tid = threadIdx.x, lane = lane_id(), w = wave_id();
+  // Workgroups are dealt to the 8 XCDs round-robin by linear id; give each XCD
+  // a contiguous range of (head, tile) so the tiles of one query cluster, which
+  // stream the same keys, run on the same XCD and share its L2.
+  const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
   const int half = lane >> 5, col = lane & 31;
+  const int per_xcd = (int)gridDim.x / AT_XCDS;
+  const int logical = ((int)blockIdx.x % AT_XCDS) * per_xcd + (int)blockIdx.x / AT_XCDS;
+  const int bh = logical / maxt, tile = logical - bh * maxt;
+  if (bh >= BHn) return;
   const int32_t* ts = tstart + (size_t)bh * (Cq + 1);
-  if ((int)blockIdx.x >= ts[Cq]) return;
-  if (tid == 0) sInfo[0] = upper_index(ts, Cq, blockIdx.x);
+  if (tile >= ts[Cq]) return;
+  if (tid == 0) sInfo[0] = upper_index(ts, Cq, tile);
   __syncthreads();
   const int ci = sInfo[0];
   const int32_t* qo = qoff + (size_t)bh * (Cq + 1);
   const int32_t* ko = koff + (size_t)bh * (Ck + 1);
-  const int row0 = qo[ci] + ((int)blockIdx.x - ts[ci]) * AT_BM;
+  const int row0 = qo[ci] + (tile - ts[ci]) * AT_BM;
   const int rowEnd = qo[ci + 1];
   const uint8_t* mrow = mask + ((size_t)bh * Cq + ci) * Ck;
   {
@@ -489,27 +498,22 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
   for (int t = 0; t < DT; ++t) o[t] = f32x16{};
   float m_run = -1e30f, l_run = 0.f;
 
-  // staging unit: keys 4*g4 .. 4*g4+3, dims d0 .. d0+7
+  // staging unit: keys 4*g4 .. 4*g4+3, dims d0 .. d0+7.  Each thread walks the
+  // selected-cluster list with its own cursor (positions only grow), and rows
+  // past the end of the stream load row 0 instead; their scores are masked.
   const bool has_unit = tid < NUNIT;
   const int g4 = tid & 15, d0 = (tid >> 4) * 8;
-  auto src_of = [&](int p) -> int {
-    if (p >= nkeys) return -1;
-    const int s = upper_index(sSelPre, nsel, p);
-    return sSelStart[s] + (p - sSelPre[s]);
-  };
+  int cur = 0;
   u32x4 pk[4], pv[4];
   auto issue = [&](int kt) {
     if (has_unit) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int src = sSrc[(kt & 1) * AT_BN + 4 * g4 + r];
-        u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-        if (src >= 0) {
-          a = ld16(kb + (size_t)src * D + d0);
-          b = ld16(vb + (size_t)src * D + d0);
-        }
-        pk[r] = a;
-        pv[r] = b;
+        const int p = kt * AT_BN + 4 * g4 + r;
+        while (cur + 1 < nsel && sSelPre[cur + 1] <= p) ++cur;
+        const int src = p < nkeys ? sSelStart[cur] + (p - sSelPre[cur]) : 0;
+        pk[r] = ld16(kb + (size_t)src * D + d0);
+        pv[r] = ld16(vb + (size_t)src * D + d0);
       }
     }
   };
@@ -532,43 +536,37 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
     }
   };
 
-  // one tile of keys already in LDS buffer `buf`: S^T, online softmax, O^T += V^T P^T
+  // one tile of keys already in LDS buffer `buf`: S^T, online softmax, O^T += V^T P^T.
+  // Real tiles take the max on the raw scores (scale > 0) and fold the scale
+  // into one FMA per weight; pseudo tiles add the log2 n_j bias first.
   auto compute = [&](int buf, int lim, bool pseudo) {
     const bf16* Kh = pseudo ? sK : sK + buf * AT_BN * SK;
     const bf16* Vh = pseudo ? sV : sV + buf * D * SV;
-    f32x16 s[2];
+    f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      f32x16 acc = {};
-      const int krow = sub * 32 + col;
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+        s[sub] = mfma_bf16(*reinterpret_cast<const bf16x8*>(&Kh[(sub * 32 + col) * SK + 16 * ks + 8 * half]), bq[ks],
+                           s[sub]);
+    if (pseudo) {
+      const bf16* Kl = sK + AT_BN * SK;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
-        acc = mfma_bf16(*reinterpret_cast<const bf16x8*>(&Kh[krow * SK + 16 * ks + 8 * half]), bq[ks], acc);
-      if (pseudo) {
-        const bf16* Kl = sK + AT_BN * SK;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          acc = mfma_bf16(*reinterpret_cast<const bf16x8*>(&Kl[krow * SK + 16 * ks + 8 * half]), bq[ks], acc);
-      }
-      s[sub] = acc;
-    }
-    if (pseudo) {
+        for (int sub = 0; sub < 2; ++sub)
+          s[sub] = mfma_bf16(*reinterpret_cast<const bf16x8*>(&Kl[(sub * 32 + col) * SK + 16 * ks + 8 * half]), bq[ks],
+                             s[sub]);
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[sub][r] = fmaf(s[sub][r], sl2, sBias[sub * 32 + c_row(r, half)]);
-    } else {
+    } else if (lim < AT_BN) {
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[sub][r] *= sl2;
-      if (lim < AT_BN) {
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (sub * 32 + c_row(r, half) >= lim) s[sub][r] = -INFINITY;
-      }
+        for (int r = 0; r < 16; ++r)
+          if (sub * 32 + c_row(r, half) >= lim) s[sub][r] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -576,10 +574,11 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
     mx = fmaxf(mx, shfl_xor(mx, 32));
+    if (!pseudo) mx *= sl2;
     const bool grow = mx > m_run + AT_LAZY;
     if (ballot(grow)) {
       const float m_new = grow ? mx : m_run;
-      const float alpha = exp2f(m_run - m_new);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
@@ -587,12 +586,14 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
     }
+    const float sc = pseudo ? 1.f : sl2;
+    const float nm = -m_run;
     float lsum = 0.f;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = exp2f(s[sub][r] - m_run);
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[sub][r], sc, nm));
         s[sub][r] = p;
         lsum += p;
       }
@@ -628,18 +629,16 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
 
   // ---- selected keys: packed 64-key tiles, double buffered
   if (nreal > 0) {
-    if (tid < AT_BN) sSrc[tid] = src_of(tid);
-    if (tid < AT_BN && nreal > 1) sSrc[AT_BN + tid] = src_of(AT_BN + tid);
-    __syncthreads();
     issue(0);
     commit(0);
+    // the Q fragments and tile 0 are in: later waits only cover the prefetch
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int kt = 0; kt < nreal; ++kt) {
       const bool more = kt + 1 < nreal;
       if (more) issue(kt + 1);
       compute(kt & 1, nkeys - kt * AT_BN, false);
       if (more) commit((kt + 1) & 1);
-      if (kt + 2 < nreal && tid < AT_BN) sSrc[(kt & 1) * AT_BN + tid] = src_of((kt + 2) * AT_BN + tid);
       __syncthreads();
     }
   }
@@ -747,8 +746,9 @@ static void launch_attn(const void* q, const void* k, const void* v, const int32
     const size_t lds = (size_t)2 * AT_BN * (D + 8) * 2 + (size_t)2 * D * (AT_BN + 8) * 2 + AT_BN * 4 +
                        2 * AT_BN * 4 + (size_t)(3 * Ck + 1) * sizeof(int);
     (void)hipFuncSetAttribute((const void*)attn_bf16_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    hipLaunchKernelGGL((attn_bf16_kernel<D>), dim3(maxt, BH), dim3(256), lds, st, (const bf16*)q, (const bf16*)k,
-                       (const bf16*)v, qidx, qoff, ts, Cq, koff, Ck, km, vm, mask, N, sl2, (bf16*)out, lse);
+    const int total = round_up(maxt * BH, AT_XCDS);
+    hipLaunchKernelGGL((attn_bf16_kernel<D>), dim3(total), dim3(256), lds, st, (const bf16*)q, (const bf16*)k,
+                       (const bf16*)v, qidx, qoff, ts, Cq, koff, Ck, km, vm, mask, N, sl2, (bf16*)out, lse, maxt, BH);
   } else {
     using L = AttnLds<T, D>;
     const size_t lds = L::fixed + (size_t)(3 * Ck + 1) * sizeof(int);

@@ -29,52 +29,47 @@ constexpr float PAD_NORM = 1e30f;   // squared norm given to padding centroids
 //   chi[c][0:D]      = hi part of -2 c      chi[c][D:D+16] = (1, 1, 1, n_hi, n_mid, n_lo, 0, ...)
 //   clo[c][0:D]      = lo part of -2 c      with n = ||c||^2 rounded to fp32 and split in three
 // Padding rows (c >= C) get zeros and n = PAD_NORM, so they never win.
-// cmax[bh] = max_c ||c|| (slightly rounded up), used by the error window.
+// nmax[bh] collects the largest ||c||^2 (bit pattern) for the error window;
+// it is cleared by km_scan_kernel (and once before the first round).
 // --------------------------------------------------------------------------
 template <int D>
 __global__ void __launch_bounds__(256) km_prep_kernel(const float* __restrict__ cent, int C, int Cpad,
                                                       bf16* __restrict__ chi, bf16* __restrict__ clo,
-                                                      float* __restrict__ cmax) {
+                                                      uint32_t* __restrict__ nmax) {
   constexpr int EPL = D / SV_WAVE;  // elements per lane
-  __shared__ double s_max[4];
-  const int bh = blockIdx.x, lane = lane_id(), w = wave_id();
+  const int bh = blockIdx.y, lane = lane_id();
+  const int c = blockIdx.x * 4 + wave_id();
+  if (c >= Cpad) return;
   const float* cb = cent + (size_t)bh * C * D;
   bf16* hb = chi + (size_t)bh * Cpad * (D + KM_EXTRA);
   bf16* lb = clo + (size_t)bh * Cpad * D;
-  double wmax = 0.0;
-  for (int c = w; c < Cpad; c += 4) {
-    double cc = 0.0;
+  double cc = 0.0;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) {
-      int d = lane + e * SV_WAVE;
-      float v = c < C ? cb[(size_t)c * D + d] : 0.f;
-      bf16 hi, lo;
-      split_bf16(-2.f * v, hi, lo);
-      hb[(size_t)c * (D + KM_EXTRA) + d] = hi;
-      lb[(size_t)c * D + d] = lo;
-      cc += (double)v * (double)v;
-    }
-    cc = wave_sum_d(cc);
-    if (c < C) wmax = fmax(wmax, cc);
-    if (lane < KM_EXTRA) {
-      float n = c < C ? (float)cc : PAD_NORM;
-      bf16 n_hi = (bf16)n;
-      float r1 = n - (float)n_hi;
-      bf16 n_mid = (bf16)r1;
-      bf16 n_lo = (bf16)(r1 - (float)n_mid);
-      bf16 val = (bf16)0.f;
-      if (lane < 3) val = (bf16)1.f;
-      else if (lane == 3) val = n_hi;
-      else if (lane == 4) val = c < C ? n_mid : (bf16)0.f;
-      else if (lane == 5) val = c < C ? n_lo : (bf16)0.f;
-      hb[(size_t)c * (D + KM_EXTRA) + D + lane] = val;
-    }
+  for (int e = 0; e < EPL; ++e) {
+    const int d = lane + e * SV_WAVE;
+    const float v = c < C ? cb[(size_t)c * D + d] : 0.f;
+    bf16 hi, lo;
+    split_bf16(-2.f * v, hi, lo);
+    hb[(size_t)c * (D + KM_EXTRA) + d] = hi;
+    lb[(size_t)c * D + d] = lo;
+    cc += (double)v * (double)v;
   }
-  if (lane == 0) s_max[w] = wmax;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    double m = fmax(fmax(s_max[0], s_max[1]), fmax(s_max[2], s_max[3]));
-    cmax[bh] = (float)(sqrt(m) * (1.0 + 1e-6));
+  cc = wave_sum_d(cc);
+  // largest ||c||^2 per head: the max of positive floats is the max of their bit
+  // patterns, so an integer atomic max gives the same result in any order
+  if (lane == 0 && c < C) atomicMax(&nmax[blockIdx.y], __float_as_uint((float)(cc * (1.0 + 1e-6))));
+  if (lane < KM_EXTRA) {
+    const float n = c < C ? (float)cc : PAD_NORM;
+    const bf16 n_hi = (bf16)n;
+    const float r1 = n - (float)n_hi;
+    const bf16 n_mid = (bf16)r1;
+    const bf16 n_lo = (bf16)(r1 - (float)n_mid);
+    bf16 val = (bf16)0.f;
+    if (lane < 3) val = (bf16)1.f;
+    else if (lane == 3) val = n_hi;
+    else if (lane == 4) val = c < C ? n_mid : (bf16)0.f;
+    else if (lane == 5) val = c < C ? n_lo : (bf16)0.f;
+    hb[(size_t)c * (D + KM_EXTRA) + D + lane] = val;
   }
 }
 
@@ -97,7 +92,7 @@ __global__ void __launch_bounds__(256) km_prep_kernel(const float* __restrict__ 
 // --------------------------------------------------------------------------
 template <typename T, int D>
 __global__ void __launch_bounds__(256) km_assign_kernel(const T* __restrict__ x, const bf16* __restrict__ chi,
-                                                        const bf16* __restrict__ clo, const float* __restrict__ cmax,
+                                                        const bf16* __restrict__ clo, const uint32_t* __restrict__ nmax,
                                                         const float* __restrict__ cent, int N, int C, int Cpad, int ib,
                                                         int32_t* __restrict__ labels) {
   constexpr bool F32 = sizeof(T) == 4;
@@ -105,8 +100,9 @@ __global__ void __launch_bounds__(256) km_assign_kernel(const T* __restrict__ x,
   constexpr int SH = D + KM_EXTRA + 8;  // LDS row strides (bf16 elements): odd multiples of 16 bytes
   constexpr int SL = D + 8;
   constexpr int HU = (D + KM_EXTRA) / 8, LU = D / 8;  // 16-byte units per row
-  __shared__ __attribute__((aligned(16))) bf16 s_hi[32 * SH];
-  __shared__ __attribute__((aligned(16))) bf16 s_lo[32 * SL];
+  constexpr int NU = (32 * (HU + LU) + 255) / 256;     // units per thread per chunk
+  __shared__ __attribute__((aligned(16))) bf16 s_hi[2][32 * SH];
+  __shared__ __attribute__((aligned(16))) bf16 s_lo[2][32 * SL];
 
   const int bh = blockIdx.y, tid = threadIdx.x, lane = lane_id(), w = wave_id();
   const int half = lane >> 5, col = lane & 31;
@@ -161,21 +157,62 @@ __global__ void __launch_bounds__(256) km_assign_kernel(const T* __restrict__ x,
     xx[t] = part + shfl_xor(part, 32);
   }
 
-  // Error window (see above).  s: split error factor; K: products per output.
-  const float cm = cmax[bh];
+  const uint32_t imask = (1u << ib) - 1u;
+  float key[2][4];
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) key[t][k] = FLT_MAX;
+
+  // chunk staging: unit v < 32*HU is a 16-byte piece of a hi row, else of a lo row
+  u32x4 pre[NU];
+  auto fetch = [&](int c0) {
+#pragma unroll
+    for (int k = 0; k < NU; ++k) {
+      const int v = tid + 256 * k;
+      if (v < 32 * HU) {
+        const int r = v / HU, cu = v - r * HU;
+        pre[k] = ld16(hb + (size_t)(c0 + r) * (D + KM_EXTRA) + cu * 8);
+      } else if (v < 32 * (HU + LU)) {
+        const int v2 = v - 32 * HU, r = v2 / LU, cu = v2 - r * LU;
+        pre[k] = ld16(lb + (size_t)(c0 + r) * D + cu * 8);
+      }
+    }
+  };
+  auto store = [&](int buf) {
+#pragma unroll
+    for (int k = 0; k < NU; ++k) {
+      const int v = tid + 256 * k;
+      if (v < 32 * HU) {
+        const int r = v / HU, cu = v - r * HU;
+        st16(&s_hi[buf][r * SH + cu * 8], pre[k]);
+      } else if (v < 32 * (HU + LU)) {
+        const int v2 = v - 32 * HU, r = v2 / LU, cu = v2 - r * LU;
+        st16(&s_lo[buf][r * SL + cu * 8], pre[k]);
+      }
+    }
+  };
+
+  // extra K slots of the token side: (||x||^2 hi, lo, offset, 1, 1, 1)
+  // the offset keeps V positive; it is set from a first window estimate below
   const float s_split = F32 ? 3.01f : 1.0f;
   const int kprod = D * (F32 ? 3 : 2) + KM_EXTRA;
   const float gam = (kprod * u) / (1.f - kprod * u);
-  const float q = ldexpf(1.f, ib - 23);
+  const int nchunk = Cpad / 32;
+  fetch(0);
+  store(0);
+  __syncthreads();
+  const float cm_pre = sqrtf(__uint_as_float(nmax[bh])) * (1.f + 1e-5f);
   float E0[2], off[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const float X = sqrtf(xx[t]) * (1.f + 1e-6f);
     const float xxb = xx[t] * (1.f + 2e-5f) + 1e-30f;
-    const float pre = u * cm * cm + 4.f * s_split * 3.8146973e-06f * X * cm;  // 2^-18
-    float e0 = 1.25f * (pre + gam * (xxb + 2.f + cm * cm + 2.05f * X * cm));
+    const float cm = cm_pre;
+    const float pre_ = u * cm * cm + 4.f * s_split * 3.8146973e-06f * X * cm;  // 2^-18
+    const float e0 = 1.25f * (pre_ + gam * (xxb + 2.f + cm * cm + 2.05f * X * cm));
     const float o = 1.f + 4.f * e0 + 4e-5f * xxb;
-    E0[t] = 1.25f * (pre + gam * (xxb + o + 2.f + cm * cm + 2.05f * X * cm));
+    E0[t] = 1.25f * (pre_ + gam * (xxb + o + 2.f + cm * cm + 2.05f * X * cm));
     off[t] = o;
     bf16x8 ex = {};
     if (half == 0) {
@@ -190,36 +227,23 @@ __global__ void __launch_bounds__(256) km_assign_kernel(const T* __restrict__ x,
     }
     bext[t] = ex;
   }
+  const float q = ldexpf(1.f, ib - 23);
 
-  const uint32_t imask = (1u << ib) - 1u;
-  float key[2][4];
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int k = 0; k < 4; ++k) key[t][k] = FLT_MAX;
-
-  for (int c0 = 0; c0 < Cpad; c0 += 32) {
-    __syncthreads();
-    for (int v = tid; v < 32 * HU; v += 256) {
-      const int r = v / HU, cu = v - r * HU;
-      *reinterpret_cast<u32x4*>(&s_hi[r * SH + cu * 8]) =
-          *reinterpret_cast<const u32x4*>(hb + (size_t)(c0 + r) * (D + KM_EXTRA) + cu * 8);
-    }
-    for (int v = tid; v < 32 * LU; v += 256) {
-      const int r = v / LU, cu = v - r * LU;
-      *reinterpret_cast<u32x4*>(&s_lo[r * SL + cu * 8]) =
-          *reinterpret_cast<const u32x4*>(lb + (size_t)(c0 + r) * D + cu * 8);
-    }
-    __syncthreads();
+  for (int ci = 0; ci < nchunk; ++ci) {
+    const int c0 = ci * 32, buf = ci & 1;
+    const bool more = ci + 1 < nchunk;
+    if (more) fetch(c0 + 32);
+    const bf16* SHb = s_hi[buf];
+    const bf16* SLb = s_lo[buf];
     f32x16 acc0 = {}, acc1 = {};
     {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s_hi[col * SH + D + 8 * half]);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&SHb[col * SH + D + 8 * half]);
       acc0 = mfma_bf16(a, bext[0], acc0);
       acc1 = mfma_bf16(a, bext[1], acc1);
     }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s_hi[col * SH + 16 * ks + 8 * half]);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&SHb[col * SH + 16 * ks + 8 * half]);
       acc0 = mfma_bf16(a, bx[0][ks], acc0);
       acc1 = mfma_bf16(a, bx[1][ks], acc1);
       if constexpr (F32) {
@@ -229,7 +253,7 @@ __global__ void __launch_bounds__(256) km_assign_kernel(const T* __restrict__ x,
     }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&s_lo[col * SL + 16 * ks + 8 * half]);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&SLb[col * SL + 16 * ks + 8 * half]);
       acc0 = mfma_bf16(a, bx[0][ks], acc0);
       acc1 = mfma_bf16(a, bx[1][ks], acc1);
     }
@@ -247,6 +271,8 @@ __global__ void __launch_bounds__(256) km_assign_kernel(const T* __restrict__ x,
       key[1][1] = med3f(key[1][0], key[1][1], k1);
       key[1][0] = fminf(key[1][0], k1);
     }
+    if (more) store(buf ^ 1);
+    __syncthreads();
   }
 
   // merge the two halves' lists (they hold different centroids of the same tokens)
@@ -320,6 +346,11 @@ __global__ void __launch_bounds__(256) km_assign_kernel(const T* __restrict__ x,
 // --------------------------------------------------------------------------
 // tile histograms: counts[bh][tile][c] = #tokens of tile with label c
 // --------------------------------------------------------------------------
+__global__ void km_clear_kernel(uint32_t* __restrict__ v, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) v[i] = 0u;
+}
+
 __global__ void __launch_bounds__(256) km_hist_kernel(const int32_t* __restrict__ labels, int N, int C, int ntiles,
                                                       int32_t* __restrict__ counts) {
   __shared__ int32_t h[SVGEAR_MAX_CLUSTERS];
@@ -340,9 +371,10 @@ __global__ void __launch_bounds__(256) km_hist_kernel(const int32_t* __restrict_
 // --------------------------------------------------------------------------
 __global__ void __launch_bounds__(1024) km_scan_kernel(int32_t* __restrict__ counts, int N, int C, int ntiles,
                                                        int rows, int32_t* __restrict__ offsets,
-                                                       int32_t* __restrict__ chunk_start) {
+                                                       int32_t* __restrict__ chunk_start, uint32_t* __restrict__ nmax) {
   __shared__ int sm[16];
   const int bh = blockIdx.x;
+  if (threadIdx.x == 0) nmax[bh] = 0u;  // the assign kernel of this round has finished
   int32_t* cnt = counts + (size_t)bh * ntiles * C;
   int tot[4], nch[4];
   int sum = 0, csum = 0;
@@ -468,7 +500,23 @@ __global__ void __launch_bounds__(256) km_partial_kernel(const T* __restrict__ x
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
-  for (int p = r0 + g; p < r1; p += RPI) {
+  int p = r0 + g;
+  for (; p + 3 * RPI < r1; p += 4 * RPI) {
+    int src[4];
+    u32x4 v[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) src[k] = pb[p + k * RPI];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = ld16(xb + (size_t)src[k] * D + e0);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (xpb) st16(xpb + (size_t)(p + k * RPI) * D + e0, v[k]);
+      const T* tv = reinterpret_cast<const T*>(&v[k]);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] += to_f32(tv[e]);
+    }
+  }
+  for (; p < r1; p += RPI) {
     const int src = pb[p];
     const u32x4 v = ld16(xb + (size_t)src * D + e0);
     if (xpb) st16(xpb + (size_t)p * D + e0, v);
@@ -512,7 +560,7 @@ __global__ void __launch_bounds__(256) km_finalize_kernel(const float* __restric
 // ---------------------------------------------------------------- host side
 struct KmPlan {
   int BH, Cpad, ib, ntiles, maxch;
-  size_t off_chi, off_clo, off_cmax, off_counts, off_cs, off_partial, total;
+  size_t off_chi, off_clo, off_nmax, off_counts, off_cs, off_partial, total;
 };
 
 static KmPlan km_plan(int B, int H, int N, int D, int C) {
@@ -526,7 +574,7 @@ static KmPlan km_plan(int B, int H, int N, int D, int C) {
   Carver cv(nullptr);
   p.off_chi = cv.used; cv.take<bf16>((size_t)p.BH * p.Cpad * (D + KM_EXTRA));
   p.off_clo = cv.used; cv.take<bf16>((size_t)p.BH * p.Cpad * D);
-  p.off_cmax = cv.used; cv.take<float>(p.BH);
+  p.off_nmax = cv.used; cv.take<uint32_t>(p.BH);
   p.off_counts = cv.used; cv.take<int32_t>((size_t)p.BH * p.ntiles * C);
   p.off_cs = cv.used; cv.take<int32_t>((size_t)p.BH * (C + 1));
   p.off_partial = cv.used; cv.take<float>((size_t)p.BH * p.maxch * D);
@@ -562,16 +610,19 @@ static svgear_status kmeans_impl(const void* x, int BH, int N, int C, int iters,
                                  int32_t* perm, int32_t* offsets, char* ws, const KmPlan& p, hipStream_t st) {
   bf16* chi = reinterpret_cast<bf16*>(ws + p.off_chi);
   bf16* clo = reinterpret_cast<bf16*>(ws + p.off_clo);
-  float* cmax = reinterpret_cast<float*>(ws + p.off_cmax);
   int32_t* counts = reinterpret_cast<int32_t*>(ws + p.off_counts);
   int32_t* cs = reinterpret_cast<int32_t*>(ws + p.off_cs);
   float* partial = reinterpret_cast<float*>(ws + p.off_partial);
+  uint32_t* nmax = reinterpret_cast<uint32_t*>(ws + p.off_nmax);
+  hipLaunchKernelGGL(km_clear_kernel, dim3(cdiv(BH, 256)), dim3(256), 0, st, nmax, BH);
   for (int it = 0; it < iters; ++it) {
-    hipLaunchKernelGGL((km_prep_kernel<D>), dim3(BH), dim3(256), 0, st, cent, C, p.Cpad, chi, clo, cmax);
+    hipLaunchKernelGGL((km_prep_kernel<D>), dim3(cdiv(p.Cpad, 4), BH), dim3(256), 0, st, cent, C, p.Cpad, chi, clo,
+                       nmax);
     hipLaunchKernelGGL((km_assign_kernel<T, D>), dim3(cdiv(N, KM_TOK_WG), BH), dim3(256), 0, st, (const T*)x, chi,
-                       clo, cmax, cent, N, C, p.Cpad, p.ib, labels);
+                       clo, nmax, cent, N, C, p.Cpad, p.ib, labels);
     hipLaunchKernelGGL(km_hist_kernel, dim3(p.ntiles, BH), dim3(256), 0, st, labels, N, C, p.ntiles, counts);
-    hipLaunchKernelGGL(km_scan_kernel, dim3(BH), dim3(1024), 0, st, counts, N, C, p.ntiles, MEAN_ROWS, offsets, cs);
+    hipLaunchKernelGGL(km_scan_kernel, dim3(BH), dim3(1024), 0, st, counts, N, C, p.ntiles, MEAN_ROWS, offsets, cs,
+                       nmax);
     (void)hipFuncSetAttribute((const void*)km_scatter_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                               (int)(4 * C * sizeof(int32_t)));
     hipLaunchKernelGGL(km_scatter_kernel, dim3(p.ntiles, BH), dim3(256), 4 * C * sizeof(int32_t), st, labels, counts,

@@ -44,18 +44,35 @@ __global__ void __launch_bounds__(256) rt_prep_kernel(const float* __restrict__ 
   qlo[(size_t)bh * Cqp * D + i] = l;
 }
 
-// s_bar[i][j] = scale * q_bar_i . k_bar_j in fp64, rounded to fp32.
+// s_bar[i][j] = scale * q_bar_i . k_bar_j in fp64, rounded to fp32.  A block
+// computes a 16 x 64 tile from rows staged in LDS (row stride D + 1 floats).
 __global__ void __launch_bounds__(256) rt_sbar_kernel(const float* __restrict__ qm, const float* __restrict__ km,
                                                       int Cq, int Ck, int D, float scale, float* __restrict__ sbar) {
-  const int bh = blockIdx.y;
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t >= Cq * Ck) return;
-  const int i = t / Ck, j = t - i * Ck;
-  const float* a = qm + ((size_t)bh * Cq + i) * D;
-  const float* b = km + ((size_t)bh * Ck + j) * D;
-  double s = 0.0;
-  for (int d = 0; d < D; ++d) s += (double)a[d] * (double)b[d];
-  sbar[(size_t)bh * Cq * Ck + t] = (float)(s * (double)scale);
+  __shared__ float sq[16 * 129];
+  __shared__ float sk[64 * 129];
+  const int bh = blockIdx.z, i0 = blockIdx.y * 16, j0 = blockIdx.x * 64, tid = threadIdx.x;
+  const int S = D + 1;
+  for (int v = tid; v < 16 * D; v += 256) {
+    const int r = v / D, d = v - r * D;
+    sq[r * S + d] = (i0 + r < Cq) ? qm[((size_t)bh * Cq + i0 + r) * D + d] : 0.f;
+  }
+  for (int v = tid; v < 64 * D; v += 256) {
+    const int r = v / D, d = v - r * D;
+    sk[r * S + d] = (j0 + r < Ck) ? km[((size_t)bh * Ck + j0 + r) * D + d] : 0.f;
+  }
+  __syncthreads();
+  const int jj = tid & 63, ig = tid >> 6;
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int d = 0; d < D; ++d) {
+    const double kv = (double)sk[jj * S + d];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[r] += (double)sq[(ig * 4 + r) * S + d] * kv;
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int i = i0 + ig * 4 + r, j = j0 + jj;
+    if (i < Cq && j < Ck) sbar[((size_t)bh * Cq + i) * Ck + j] = (float)(acc[r] * (double)scale);
+  }
 }
 
 // One workgroup per piece (<= RT_PIECE keys of one key cluster).  Output per
@@ -428,8 +445,8 @@ extern "C" svgear_status svgear_route(const float* q_means, const int32_t* q_off
     else
       hipLaunchKernelGGL((rt_prep_kernel<64>), dim3(cdiv(p.Cqp * D, 256), BH), dim3(256), 0, stream, q_means, Cq,
                          p.Cqp, qh, ql);
-    hipLaunchKernelGGL(rt_sbar_kernel, dim3(cdiv(Cq * Ck, 256), BH), dim3(256), 0, stream, q_means, k_means, Cq, Ck,
-                       D, scale, sbar);
+    hipLaunchKernelGGL(rt_sbar_kernel, dim3(cdiv(Ck, 64), cdiv(Cq, 16), BH), dim3(256), 0, stream, q_means, k_means,
+                       Cq, Ck, D, scale, sbar);
     hipLaunchKernelGGL(chunk_list_kernel, dim3(BH), dim3(1024), 0, stream, k_offsets, Ck, RT_PIECE, ps);
 #define RT_MAIN(T, DD)                                                                                              \
   hipLaunchKernelGGL((rt_main_kernel<T, DD>), dim3(p.maxp, BH), dim3(256), 0, stream, (const T*)k_perm,          \

@@ -232,12 +232,20 @@ class Layer:
                    lib.svgear_route_workspace(B, H, N, D, Cq, Ck),
                    lib.svgear_sparse_attn_workspace(B, H, N, D, Cq, Ck))
         self.ws = _workspace(need, dev)
+        # k-means of Q and of K are independent: the K clustering runs on a
+        # side stream with its own workspace
+        self.ws_k = _workspace(lib.svgear_kmeans_workspace(B, H, N, D, Ck), dev)
+        self.side = torch.cuda.Stream(device=dev)
 
     def forward(self, q, k, v, cq, ck, iters, density, scale=None):
         B, H, N, D, Cq, Ck = self.shape
         scale = 1.0 / math.sqrt(D) if scale is None else scale
+        main = torch.cuda.current_stream(self.side.device)
+        self.side.wait_stream(main)
+        with torch.cuda.stream(self.side):
+            kmeans(k, ck, iters, self.lk, self.pk, self.ok, ws=self.ws_k)
         kmeans(q, cq, iters, self.lq, self.pq, self.oq, ws=self.ws)
-        kmeans(k, ck, iters, self.lk, self.pk, self.ok, ws=self.ws)
+        main.wait_stream(self.side)
         centroids(q, self.pq, self.oq, x_perm=self.qp, means=self.qm, ws=self.ws)
         centroids(k, self.pk, self.ok, x_perm=self.kp, means=self.km, ws=self.ws)
         centroids(v, self.pk, self.ok, x_perm=self.vp, means=self.vm, ws=self.ws)
