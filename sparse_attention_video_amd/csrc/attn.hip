@@ -421,7 +421,10 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
                                                            bf16* __restrict__ out, float* __restrict__ lse,
                                                            int maxt, int BHn) {
   constexpr int KS = D / 16, DT = D / 32;
-  constexpr int SK = D + 8, SV = AT_BN + 8;
+  // LDS row strides: K rows 68 dwords (8 consecutive rows hit distinct bank
+  // quads for 16-byte accesses); V^T rows 34 dwords (16 consecutive rows hit
+  // distinct bank pairs for the 8-byte fragment reads)
+  constexpr int SK = D + 8, SV = AT_BN + 4;
   constexpr int NUNIT = (AT_BN / 4) * (D / 8);
   extern __shared__ __attribute__((aligned(16))) char smem[];
   bf16* sK = reinterpret_cast<bf16*>(smem);                 // [2][64][SK]
@@ -503,17 +506,36 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
   // past the end of the stream load row 0 instead; their scores are masked.
   const bool has_unit = tid < NUNIT;
   const int g4 = tid & 15, d0 = (tid >> 4) * 8;
-  int cur = 0;
+  int cur = 0, cur_base = 0, cur_pre = 0;               // cluster cursor: start row, key prefix
+  int nxt = nsel > 1 ? sSelPre[1] : 0x7fffffff;        // key prefix where the next cluster begins
+  if (nsel > 0) { cur_base = sSelStart[0]; cur_pre = 0; }
+  int kcur = cur, kcur_base = cur_base, kcur_pre = cur_pre, knxt = nxt;  // second cursor (K rows)
   u32x4 pk[4], pv[4];
   auto issue = [&](int kt) {
     if (has_unit) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int p = kt * AT_BN + 4 * g4 + r;
-        while (cur + 1 < nsel && sSelPre[cur + 1] <= p) ++cur;
-        const int src = p < nkeys ? sSelStart[cur] + (p - sSelPre[cur]) : 0;
-        pk[r] = ld16(kb + (size_t)src * D + d0);
+        while (p >= nxt) {
+          ++cur;
+          cur_base = sSelStart[cur];
+          cur_pre = nxt;
+          nxt = cur + 1 < nsel ? sSelPre[cur + 1] : 0x7fffffff;
+        }
+        const int src = p < nkeys ? cur_base + (p - cur_pre) : 0;
         pv[r] = ld16(vb + (size_t)src * D + d0);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int p = kt * AT_BN + g4 + 16 * r;
+        while (p >= knxt) {
+          ++kcur;
+          kcur_base = sSelStart[kcur];
+          kcur_pre = knxt;
+          knxt = kcur + 1 < nsel ? sSelPre[kcur + 1] : 0x7fffffff;
+        }
+        const int src = p < nkeys ? kcur_base + (p - kcur_pre) : 0;
+        pk[r] = ld16(kb + (size_t)src * D + d0);
       }
     }
   };
@@ -522,7 +544,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
       bf16* K = sK + buf * AT_BN * SK;
       bf16* V = sV + buf * D * SV;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) st16(&K[(4 * g4 + r) * SK + d0], pk[r]);
+      for (int r = 0; r < 4; ++r) st16(&K[(g4 + 16 * r) * SK + d0], pk[r]);
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
         uint2 lo, hi;
@@ -573,7 +595,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
-    mx = fmaxf(mx, shfl_xor(mx, 32));
+    mx = max_halves(mx);
     if (!pseudo) mx *= sl2;
     const bool grow = mx > m_run + AT_LAZY;
     if (ballot(grow)) {
@@ -703,7 +725,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
   }
 
   // ---- epilogue
-  const float l_tot = l_run + shfl_xor(l_run, 32);
+  const float l_tot = sum_halves(l_run);
   if (qok) {
     const int orig = qidx[(size_t)bh * N + qrow];
     const float inv = 1.f / l_tot;
@@ -743,7 +765,7 @@ static void launch_attn(const void* q, const void* k, const void* v, const int32
                         const uint8_t* mask, int BH, int N, float sl2, void* out, float* lse, int maxt,
                         hipStream_t st) {
   if constexpr (sizeof(T) == 2) {
-    const size_t lds = (size_t)2 * AT_BN * (D + 8) * 2 + (size_t)2 * D * (AT_BN + 8) * 2 + AT_BN * 4 +
+    const size_t lds = (size_t)2 * AT_BN * (D + 8) * 2 + (size_t)2 * D * (AT_BN + 4) * 2 + AT_BN * 4 +
                        2 * AT_BN * 4 + (size_t)(3 * Ck + 1) * sizeof(int);
     (void)hipFuncSetAttribute((const void*)attn_bf16_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     const int total = round_up(maxt * BH, AT_XCDS);
