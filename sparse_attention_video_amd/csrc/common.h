@@ -89,6 +89,16 @@ __device__ __forceinline__ float sum_halves(float v) {
 // float order equals their bit order.
 __device__ __forceinline__ float med3f(float a, float b, float c) { return __builtin_amdgcn_fmed3f(a, b, c); }
 
+// Sum over each row of 16 lanes by a fixed DPP butterfly (xor 1, xor 2,
+// mirror within 8, mirror within 16); every lane of the row gets the same sum.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, true));   // quad_perm [1,0,3,2]
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, true));   // quad_perm [2,3,0,1]
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, true));  // row_half_mirror
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, true));  // row_mirror
+  return v;
+}
+
 // Binary search: largest idx in [0, n) with starts[idx] <= v (starts[0] <= v assumed).
 __device__ __forceinline__ int upper_index(const int32_t* starts, int n, int v) {
   int lo = 0, hi = n - 1;

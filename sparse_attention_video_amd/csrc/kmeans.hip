@@ -23,53 +23,68 @@ constexpr int KM_TOK_WG = 256;      // tokens per assign workgroup (4 waves x 64
 constexpr int SORT_TILE = 4096;     // tokens per histogram / scatter tile
 constexpr int MEAN_ROWS = 256;      // rows per segment-sum chunk
 constexpr float PAD_NORM = 1e30f;   // squared norm given to padding centroids
+constexpr int KM_PREP_ROWS = 32;    // centroid rows per prep workgroup
 
 // --------------------------------------------------------------------------
-// prep: per (batch, head), the bf16 operands of the distance GEMM.
-//   chi[c][0:D]      = hi part of -2 c      chi[c][D:D+16] = (1, 1, 1, n_hi, n_mid, n_lo, 0, ...)
-//   clo[c][0:D]      = lo part of -2 c      with n = ||c||^2 rounded to fp32 and split in three
+// prep: per (batch, head), the bf16 operands of the distance GEMM, one row
+// of KM_ROW(D) elements per centroid:
+//   [0, D)          hi part of -2 c
+//   [D, D + 16)     (1, 1, 1, n_hi, n_mid, n_lo, 0, ...)   n = ||c||^2 (fp32) split in three
+//   [D + 16, 2D+16) lo part of -2 c
 // Padding rows (c >= C) get zeros and n = PAD_NORM, so they never win.
 // nmax[bh] collects the largest ||c||^2 (bit pattern) for the error window;
 // it is cleared by km_scan_kernel (and once before the first round).
 // --------------------------------------------------------------------------
 template <int D>
+constexpr int km_row() { return 2 * D + KM_EXTRA; }
+
+template <int D>
 __global__ void __launch_bounds__(256) km_prep_kernel(const float* __restrict__ cent, int C, int Cpad,
-                                                      bf16* __restrict__ chi, bf16* __restrict__ clo,
-                                                      uint32_t* __restrict__ nmax) {
+                                                      bf16* __restrict__ ops, uint32_t* __restrict__ nmax) {
   constexpr int EPL = D / SV_WAVE;  // elements per lane
-  const int bh = blockIdx.y, lane = lane_id();
-  const int c = blockIdx.x * 4 + wave_id();
-  if (c >= Cpad) return;
+  constexpr int RW = km_row<D>();
+  __shared__ double s_max[4];
+  const int bh = blockIdx.y, lane = lane_id(), w = wave_id();
   const float* cb = cent + (size_t)bh * C * D;
-  bf16* hb = chi + (size_t)bh * Cpad * (D + KM_EXTRA);
-  bf16* lb = clo + (size_t)bh * Cpad * D;
-  double cc = 0.0;
+  double wmax = 0.0;
+  for (int rr = 0; rr < KM_PREP_ROWS / 4; ++rr) {
+    const int c = blockIdx.x * KM_PREP_ROWS + rr * 4 + w;
+    if (c >= Cpad) break;
+    bf16* row = ops + ((size_t)bh * Cpad + c) * RW;
+    double cc = 0.0;
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) {
-    const int d = lane + e * SV_WAVE;
-    const float v = c < C ? cb[(size_t)c * D + d] : 0.f;
-    bf16 hi, lo;
-    split_bf16(-2.f * v, hi, lo);
-    hb[(size_t)c * (D + KM_EXTRA) + d] = hi;
-    lb[(size_t)c * D + d] = lo;
-    cc += (double)v * (double)v;
+    for (int e = 0; e < EPL; ++e) {
+      const int d = lane + e * SV_WAVE;
+      const float v = c < C ? cb[(size_t)c * D + d] : 0.f;
+      bf16 hi, lo;
+      split_bf16(-2.f * v, hi, lo);
+      row[d] = hi;
+      row[D + KM_EXTRA + d] = lo;
+      cc += (double)v * (double)v;
+    }
+    cc = wave_sum_d(cc);
+    if (c < C) wmax = fmax(wmax, cc);
+    if (lane < KM_EXTRA) {
+      const float n = c < C ? (float)cc : PAD_NORM;
+      const bf16 n_hi = (bf16)n;
+      const float r1 = n - (float)n_hi;
+      const bf16 n_mid = (bf16)r1;
+      const bf16 n_lo = (bf16)(r1 - (float)n_mid);
+      bf16 val = (bf16)0.f;
+      if (lane < 3) val = (bf16)1.f;
+      else if (lane == 3) val = n_hi;
+      else if (lane == 4) val = c < C ? n_mid : (bf16)0.f;
+      else if (lane == 5) val = c < C ? n_lo : (bf16)0.f;
+      row[D + lane] = val;
+    }
   }
-  cc = wave_sum_d(cc);
-  // largest ||c||^2 per head: the max of positive floats is the max of their bit
-  // patterns, so an integer atomic max gives the same result in any order
-  if (lane == 0 && c < C) atomicMax(&nmax[blockIdx.y], __float_as_uint((float)(cc * (1.0 + 1e-6))));
-  if (lane < KM_EXTRA) {
-    const float n = c < C ? (float)cc : PAD_NORM;
-    const bf16 n_hi = (bf16)n;
-    const float r1 = n - (float)n_hi;
-    const bf16 n_mid = (bf16)r1;
-    const bf16 n_lo = (bf16)(r1 - (float)n_mid);
-    bf16 val = (bf16)0.f;
-    if (lane < 3) val = (bf16)1.f;
-    else if (lane == 3) val = n_hi;
-    else if (lane == 4) val = c < C ? n_mid : (bf16)0.f;
-    else if (lane == 5) val = c < C ? n_lo : (bf16)0.f;
-    hb[(size_t)c * (D + KM_EXTRA) + D + lane] = val;
+  if (lane == 0) s_max[w] = wmax;
+  __syncthreads();
+  // the max of positive floats is the max of their bit patterns, so an
+  // integer atomic max gives the same result in any order
+  if (threadIdx.x == 0) {
+    const double m = fmax(fmax(s_max[0], s_max[1]), fmax(s_max[2], s_max[3]));
+    if (m > 0.0) atomicMax(&nmax[bh], __float_as_uint((float)(m * (1.0 + 1e-6))));
   }
 }
 
@@ -91,24 +106,22 @@ __global__ void __launch_bounds__(256) km_prep_kernel(const float* __restrict__ 
 // The exact distances are summed by a fixed 64-lane butterfly.
 // --------------------------------------------------------------------------
 template <typename T, int D>
-__global__ void __launch_bounds__(256) km_assign_kernel(const T* __restrict__ x, const bf16* __restrict__ chi,
-                                                        const bf16* __restrict__ clo, const uint32_t* __restrict__ nmax,
+__global__ void __launch_bounds__(256) km_assign_kernel(const T* __restrict__ x, const bf16* __restrict__ ops,
+                                                        const uint32_t* __restrict__ nmax,
                                                         const float* __restrict__ cent, int N, int C, int Cpad, int ib,
                                                         int32_t* __restrict__ labels) {
   constexpr bool F32 = sizeof(T) == 4;
   constexpr int KS = D / 16;
-  constexpr int SH = D + KM_EXTRA + 8;  // LDS row strides (bf16 elements): odd multiples of 16 bytes
-  constexpr int SL = D + 8;
-  constexpr int HU = (D + KM_EXTRA) / 8, LU = D / 8;  // 16-byte units per row
-  constexpr int NU = (32 * (HU + LU) + 255) / 256;     // units per thread per chunk
-  __shared__ __attribute__((aligned(16))) bf16 s_hi[2][32 * SH];
-  __shared__ __attribute__((aligned(16))) bf16 s_lo[2][32 * SL];
+  constexpr int RW = km_row<D>();          // operand row (bf16 elements)
+  constexpr int SR = RW + 8;               // LDS row stride: an odd multiple of 16 bytes
+  constexpr int U = RW / 8;                // 16-byte units per row
+  constexpr int NU = (32 * U + 255) / 256; // units per thread per 32-row chunk
+  __shared__ __attribute__((aligned(16))) bf16 s_ops[2][32 * SR];
 
   const int bh = blockIdx.y, tid = threadIdx.x, lane = lane_id(), w = wave_id();
   const int half = lane >> 5, col = lane & 31;
   const T* xb = x + (size_t)bh * N * D;
-  const bf16* hb = chi + (size_t)bh * Cpad * (D + KM_EXTRA);
-  const bf16* lb = clo + (size_t)bh * Cpad * D;
+  const bf16* ob = ops + (size_t)bh * Cpad * RW;
   const float* cb = cent + (size_t)bh * C * D;
   const int tok0 = blockIdx.x * KM_TOK_WG + w * 64;
   const float u = 5.9604645e-08f;  // 2^-24
@@ -164,33 +177,29 @@ __global__ void __launch_bounds__(256) km_assign_kernel(const T* __restrict__ x,
 #pragma unroll
     for (int k = 0; k < 4; ++k) key[t][k] = FLT_MAX;
 
-  // chunk staging: unit v < 32*HU is a 16-byte piece of a hi row, else of a lo row
+  // chunk staging: thread tid moves units tid + 256 k of the chunk (row, 16-byte
+  // column); offsets are fixed per thread, so loads are unconditional (a
+  // thread past the end reloads unit 0 and skips its store)
+  int goff[NU], loff[NU];
+  bool uok[NU];
+#pragma unroll
+  for (int k = 0; k < NU; ++k) {
+    const int v = tid + 256 * k;
+    uok[k] = v < 32 * U;
+    const int r = uok[k] ? v / U : 0, cu = uok[k] ? v - (v / U) * U : 0;
+    goff[k] = r * RW + cu * 8;
+    loff[k] = r * SR + cu * 8;
+  }
   u32x4 pre[NU];
   auto fetch = [&](int c0) {
+    const bf16* base = ob + (size_t)c0 * RW;
 #pragma unroll
-    for (int k = 0; k < NU; ++k) {
-      const int v = tid + 256 * k;
-      if (v < 32 * HU) {
-        const int r = v / HU, cu = v - r * HU;
-        pre[k] = ld16(hb + (size_t)(c0 + r) * (D + KM_EXTRA) + cu * 8);
-      } else if (v < 32 * (HU + LU)) {
-        const int v2 = v - 32 * HU, r = v2 / LU, cu = v2 - r * LU;
-        pre[k] = ld16(lb + (size_t)(c0 + r) * D + cu * 8);
-      }
-    }
+    for (int k = 0; k < NU; ++k) pre[k] = ld16(base + goff[k]);
   };
   auto store = [&](int buf) {
 #pragma unroll
-    for (int k = 0; k < NU; ++k) {
-      const int v = tid + 256 * k;
-      if (v < 32 * HU) {
-        const int r = v / HU, cu = v - r * HU;
-        st16(&s_hi[buf][r * SH + cu * 8], pre[k]);
-      } else if (v < 32 * (HU + LU)) {
-        const int v2 = v - 32 * HU, r = v2 / LU, cu = v2 - r * LU;
-        st16(&s_lo[buf][r * SL + cu * 8], pre[k]);
-      }
-    }
+    for (int k = 0; k < NU; ++k)
+      if (uok[k]) st16(&s_ops[buf][loff[k]], pre[k]);
   };
 
   // extra K slots of the token side: (||x||^2 hi, lo, offset, 1, 1, 1)
@@ -233,17 +242,16 @@ __global__ void __launch_bounds__(256) km_assign_kernel(const T* __restrict__ x,
     const int c0 = ci * 32, buf = ci & 1;
     const bool more = ci + 1 < nchunk;
     if (more) fetch(c0 + 32);
-    const bf16* SHb = s_hi[buf];
-    const bf16* SLb = s_lo[buf];
+    const bf16* R = &s_ops[buf][col * SR];
     f32x16 acc0 = {}, acc1 = {};
     {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&SHb[col * SH + D + 8 * half]);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(R + D + 8 * half);
       acc0 = mfma_bf16(a, bext[0], acc0);
       acc1 = mfma_bf16(a, bext[1], acc1);
     }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&SHb[col * SH + 16 * ks + 8 * half]);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(R + 16 * ks + 8 * half);
       acc0 = mfma_bf16(a, bx[0][ks], acc0);
       acc1 = mfma_bf16(a, bx[1][ks], acc1);
       if constexpr (F32) {
@@ -253,23 +261,25 @@ __global__ void __launch_bounds__(256) km_assign_kernel(const T* __restrict__ x,
     }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&SLb[col * SL + 16 * ks + 8 * half]);
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(R + D + KM_EXTRA + 16 * ks + 8 * half);
       acc0 = mfma_bf16(a, bx[0][ks], acc0);
       acc1 = mfma_bf16(a, bx[1][ks], acc1);
     }
+    // keys: the low ib bits of V's pattern carry the centroid index; keep the
+    // 4 smallest per lane with med3 (min(a, b) = med3(a, b, -inf))
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const uint32_t idx = (uint32_t)(c0 + c_row(r, half));
-      float k0 = __uint_as_float((__float_as_uint(acc0[r]) & ~imask) | idx);
-      float k1 = __uint_as_float((__float_as_uint(acc1[r]) & ~imask) | idx);
+      const float k0 = __uint_as_float((__float_as_uint(acc0[r]) & ~imask) | idx);
+      const float k1 = __uint_as_float((__float_as_uint(acc1[r]) & ~imask) | idx);
       key[0][3] = med3f(key[0][2], key[0][3], k0);
       key[0][2] = med3f(key[0][1], key[0][2], k0);
       key[0][1] = med3f(key[0][0], key[0][1], k0);
-      key[0][0] = fminf(key[0][0], k0);
+      key[0][0] = med3f(key[0][0], k0, -INFINITY);
       key[1][3] = med3f(key[1][2], key[1][3], k1);
       key[1][2] = med3f(key[1][1], key[1][2], k1);
       key[1][1] = med3f(key[1][0], key[1][1], k1);
-      key[1][0] = fminf(key[1][0], k1);
+      key[1][0] = med3f(key[1][0], k1, -INFINITY);
     }
     if (more) store(buf ^ 1);
     __syncthreads();
@@ -287,7 +297,7 @@ __global__ void __launch_bounds__(256) km_assign_kernel(const T* __restrict__ x,
       key[t][3] = med3f(key[t][2], key[t][3], kk);
       key[t][2] = med3f(key[t][1], key[t][2], kk);
       key[t][1] = med3f(key[t][0], key[t][1], kk);
-      key[t][0] = fminf(key[t][0], kk);
+      key[t][0] = med3f(key[t][0], kk, -INFINITY);
     }
   }
 
@@ -303,7 +313,14 @@ __global__ void __launch_bounds__(256) km_assign_kernel(const T* __restrict__ x,
     ncand[t] = nc;  // 1: decided; 2..3: refine candidates; 4: full scan
   }
 
-  // exact refinement, one flagged token at a time, all 64 lanes cooperating
+  // Near ties: exact distances of the candidates, one flagged token at a time.
+  // Each 16-lane row of the wave evaluates one centroid: a lane takes D/16
+  // consecutive coordinates, (x - c)^2 in fp32, then a fixed 16-lane butterfly
+  // (pairwise summation: error <= (log2 D + 3) u D, far inside the 1e-5
+  // relative tie tolerance).  With 4 candidates inside the window every
+  // centroid is scanned, 4 at a time.
+  constexpr int EPG = D / 16;
+  const int grp = lane >> 4, gl = lane & 15;
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int n_mine = tok0 + 32 * t + col;
@@ -313,28 +330,36 @@ __global__ void __launch_bounds__(256) km_assign_kernel(const T* __restrict__ x,
       todo &= todo - 1;
       const int n = tok0 + 32 * t + src;
       const int nc = __shfl(ncand[t], src, SV_WAVE);
-      double xv[D / SV_WAVE];
+      float xv[EPG];
 #pragma unroll
-      for (int e = 0; e < D / SV_WAVE; ++e) xv[e] = (double)to_f32(xb[(size_t)n * D + lane + e * SV_WAVE]);
-      int cand[3];
+      for (int e = 0; e < EPG; ++e) xv[e] = to_f32(xb[(size_t)n * D + gl * EPG + e]);
+      int cand[4];
 #pragma unroll
-      for (int j = 0; j < 3; ++j) cand[j] = (int)(__float_as_uint(__shfl(key[t][j], src, SV_WAVE)) & imask);
-      double best = 0.0;
+      for (int j = 0; j < 4; ++j) cand[j] = (int)(__float_as_uint(__shfl(key[t][j], src, SV_WAVE)) & imask);
+      float best = 0.f;
       int bidx = -1;
       const int count = nc >= 4 ? C : nc;
-      for (int j = 0; j < count; ++j) {
-        const int c = nc >= 4 ? j : (j == 0 ? cand[0] : (j == 1 ? cand[1] : cand[2]));
-        if (c >= C) continue;  // padding centroids never qualify; guard the read anyway
-        double part = 0.0;
+      for (int j0 = 0; j0 < count; j0 += 4) {
+        int c = nc >= 4 ? j0 + grp : (grp == 0 ? cand[0] : grp == 1 ? cand[1] : grp == 2 ? cand[2] : cand[3]);
+        const bool live = (j0 + grp < count) && c < C;
+        if (!live) c = 0;
+        const float* cr = cb + (size_t)c * D + gl * EPG;
+        float part = 0.f;
 #pragma unroll
-        for (int e = 0; e < D / SV_WAVE; ++e) {
-          const double dv = xv[e] - (double)cb[(size_t)c * D + lane + e * SV_WAVE];
-          part += dv * dv;
+        for (int e = 0; e < EPG; ++e) {
+          const float dv = xv[e] - cr[e];
+          part = fmaf(dv, dv, part);
         }
-        const double dist = wave_sum_d(part);
-        if (bidx < 0 || dist < best || (dist == best && c < bidx)) {
-          best = dist;
-          bidx = c;
+        const float dist = row16_sum(part);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const float dg = __shfl(dist, 16 * g, SV_WAVE);
+          const int cg = __shfl(c, 16 * g, SV_WAVE);
+          const bool lg = __shfl((int)live, 16 * g, SV_WAVE) != 0;
+          if (lg && (bidx < 0 || dg < best || (dg == best && cg < bidx))) {
+            best = dg;
+            bidx = cg;
+          }
         }
       }
       if (lane == src) lab[t] = bidx;
@@ -560,7 +585,7 @@ __global__ void __launch_bounds__(256) km_finalize_kernel(const float* __restric
 // ---------------------------------------------------------------- host side
 struct KmPlan {
   int BH, Cpad, ib, ntiles, maxch;
-  size_t off_chi, off_clo, off_nmax, off_counts, off_cs, off_partial, total;
+  size_t off_ops, off_nmax, off_counts, off_cs, off_partial, total;
 };
 
 static KmPlan km_plan(int B, int H, int N, int D, int C) {
@@ -572,8 +597,7 @@ static KmPlan km_plan(int B, int H, int N, int D, int C) {
   p.ntiles = cdiv(N, SORT_TILE);
   p.maxch = cdiv(N, MEAN_ROWS) + C;
   Carver cv(nullptr);
-  p.off_chi = cv.used; cv.take<bf16>((size_t)p.BH * p.Cpad * (D + KM_EXTRA));
-  p.off_clo = cv.used; cv.take<bf16>((size_t)p.BH * p.Cpad * D);
+  p.off_ops = cv.used; cv.take<bf16>((size_t)p.BH * p.Cpad * (2 * D + KM_EXTRA));
   p.off_nmax = cv.used; cv.take<uint32_t>(p.BH);
   p.off_counts = cv.used; cv.take<int32_t>((size_t)p.BH * p.ntiles * C);
   p.off_cs = cv.used; cv.take<int32_t>((size_t)p.BH * (C + 1));
@@ -608,18 +632,17 @@ static void launch_partial(const void* x, const int32_t* perm, const int32_t* of
 template <typename T, int D>
 static svgear_status kmeans_impl(const void* x, int BH, int N, int C, int iters, float* cent, int32_t* labels,
                                  int32_t* perm, int32_t* offsets, char* ws, const KmPlan& p, hipStream_t st) {
-  bf16* chi = reinterpret_cast<bf16*>(ws + p.off_chi);
-  bf16* clo = reinterpret_cast<bf16*>(ws + p.off_clo);
+  bf16* ops = reinterpret_cast<bf16*>(ws + p.off_ops);
   int32_t* counts = reinterpret_cast<int32_t*>(ws + p.off_counts);
   int32_t* cs = reinterpret_cast<int32_t*>(ws + p.off_cs);
   float* partial = reinterpret_cast<float*>(ws + p.off_partial);
   uint32_t* nmax = reinterpret_cast<uint32_t*>(ws + p.off_nmax);
   hipLaunchKernelGGL(km_clear_kernel, dim3(cdiv(BH, 256)), dim3(256), 0, st, nmax, BH);
   for (int it = 0; it < iters; ++it) {
-    hipLaunchKernelGGL((km_prep_kernel<D>), dim3(cdiv(p.Cpad, 4), BH), dim3(256), 0, st, cent, C, p.Cpad, chi, clo,
-                       nmax);
-    hipLaunchKernelGGL((km_assign_kernel<T, D>), dim3(cdiv(N, KM_TOK_WG), BH), dim3(256), 0, st, (const T*)x, chi,
-                       clo, nmax, cent, N, C, p.Cpad, p.ib, labels);
+    hipLaunchKernelGGL((km_prep_kernel<D>), dim3(cdiv(p.Cpad, KM_PREP_ROWS), BH), dim3(256), 0, st, cent, C, p.Cpad,
+                       ops, nmax);
+    hipLaunchKernelGGL((km_assign_kernel<T, D>), dim3(cdiv(N, KM_TOK_WG), BH), dim3(256), 0, st, (const T*)x, ops,
+                       nmax, cent, N, C, p.Cpad, p.ib, labels);
     hipLaunchKernelGGL(km_hist_kernel, dim3(p.ntiles, BH), dim3(256), 0, st, labels, N, C, p.ntiles, counts);
     hipLaunchKernelGGL(km_scan_kernel, dim3(BH), dim3(1024), 0, st, counts, N, C, p.ntiles, MEAN_ROWS, offsets, cs,
                        nmax);
