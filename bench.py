@@ -75,47 +75,22 @@ def algorithmic_flops(mask, qoff, koff, D):
 
 
 def cpu_baseline(w, h0, scale):
-    """The fp64 oracle on one head, on bounded samples, scaled to ms per layer."""
+    """The fp64 oracle on one whole head (every Lloyd round, every query row),
+    scaled by the number of heads to ms per layer."""
     from oracle import svgear_oracle as orc
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         cores = os.cpu_count() or 1
-    q, k, v = (np.asarray(h0[x], np.float64) for x in ("q", "k", "v"))
-    t = {}
     s = time.perf_counter()
-    orc.lloyd(q, h0["cq0"], 1)
-    t["kmeans_q_round"] = time.perf_counter() - s
-    s = time.perf_counter()
-    ck, lk = orc.lloyd(k, h0["ck0"], 1)
-    t["kmeans_k_round"] = time.perf_counter() - s
-    cq, lq = orc.lloyd(q, h0["cq0"], 1)
-    s = time.perf_counter()
-    pq, oq = orc.permute(lq, w.Cq)
-    pk, ok = orc.permute(lk, w.Ck)
-    qbar, kbar, vbar = orc.means(q, pq, oq), orc.means(k, pk, ok), orc.means(v, pk, ok)
-    Kp, Vp = k[pk], v[pk]
-    t["permute_means"] = time.perf_counter() - s
-    s = time.perf_counter()
-    r, mask = orc.route(qbar, oq, Kp, Vp, kbar, vbar, ok, scale, w.density)
-    t["route"] = time.perf_counter() - s
-    # attention on a sample of query clusters, scaled by the rows covered
-    sizes = np.diff(oq)
-    pick = [i for i in np.argsort(-sizes) if sizes[i] > 0][::12][:4]
-    rows = int(sum(sizes[i] for i in pick))
-    s = time.perf_counter()
-    for i in pick:
-        toks = pq[oq[i]:oq[i + 1]]
-        orc.attend_rows(q[toks], k, v, pk, ok, kbar, vbar, mask[i], scale)
-    t["attend_sample"] = time.perf_counter() - s
-    per_head = (w.iters * (t["kmeans_q_round"] + t["kmeans_k_round"]) + t["permute_means"] + t["route"]
-                + t["attend_sample"] * (w.N / max(rows, 1)))
-    ms = per_head * w.B * w.H * 1e3
-    sample = (f"1 of {w.B * w.H} heads: one Lloyd round of Q and of K (x{w.iters}), permute+means, route, "
-              f"attention for {rows} of {w.N} query rows (x{w.N / max(rows, 1):.1f}); scaled x{w.B * w.H} heads")
-    return {"value": round(ms, 1), "unit": "ms", "cores": int(cores), "kind": "oracle", "sample": sample,
-            "measured_s": round(sum(t.values()), 2)}
+    orc.layer(h0["q"], h0["k"], h0["v"], h0["cq0"], h0["ck0"], w.iters, w.density, scale)
+    sec = time.perf_counter() - s
+    heads = w.B * w.H
+    return {"value": round(sec * heads * 1e3, 1), "unit": "ms", "cores": int(cores), "kind": "oracle",
+            "sample": f"1 of {heads} heads in full ({w.iters} Lloyd rounds of Q and K, permute, means, route, "
+                      f"attention for all {w.N} rows), scaled x{heads}",
+            "measured_s": round(sec, 2)}
 
 
 def main():

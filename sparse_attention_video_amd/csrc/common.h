@@ -99,6 +99,12 @@ __device__ __forceinline__ float row16_sum(float v) {
   return v;
 }
 
+// The smaller of two positive, finite float keys, compared as bit patterns
+// (an integer min: no NaN canonicalisation).
+__device__ __forceinline__ float minkey(float a, float b) {
+  return __uint_as_float(min(__float_as_uint(a), __float_as_uint(b)));
+}
+
 // Binary search: largest idx in [0, n) with starts[idx] <= v (starts[0] <= v assumed).
 __device__ __forceinline__ int upper_index(const int32_t* starts, int n, int v) {
   int lo = 0, hi = n - 1;

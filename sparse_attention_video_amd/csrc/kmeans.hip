@@ -106,7 +106,7 @@ __global__ void __launch_bounds__(256) km_prep_kernel(const float* __restrict__ 
 // The exact distances are summed by a fixed 64-lane butterfly.
 // --------------------------------------------------------------------------
 template <typename T, int D>
-__global__ void __launch_bounds__(256) km_assign_kernel(const T* __restrict__ x, const bf16* __restrict__ ops,
+__global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) km_assign_kernel(const T* __restrict__ x, const bf16* __restrict__ ops,
                                                         const uint32_t* __restrict__ nmax,
                                                         const float* __restrict__ cent, int N, int C, int Cpad, int ib,
                                                         int32_t* __restrict__ labels) {
@@ -238,12 +238,10 @@ __global__ void __launch_bounds__(256) km_assign_kernel(const T* __restrict__ x,
   }
   const float q = ldexpf(1.f, ib - 23);
 
-  for (int ci = 0; ci < nchunk; ++ci) {
-    const int c0 = ci * 32, buf = ci & 1;
-    const bool more = ci + 1 < nchunk;
-    if (more) fetch(c0 + 32);
+  auto mma = [&](int buf, f32x16& acc0, f32x16& acc1) {
     const bf16* R = &s_ops[buf][col * SR];
-    f32x16 acc0 = {}, acc1 = {};
+    acc0 = f32x16{};
+    acc1 = f32x16{};
     {
       const bf16x8 a = *reinterpret_cast<const bf16x8*>(R + D + 8 * half);
       acc0 = mfma_bf16(a, bext[0], acc0);
@@ -265,8 +263,11 @@ __global__ void __launch_bounds__(256) km_assign_kernel(const T* __restrict__ x,
       acc0 = mfma_bf16(a, bx[0][ks], acc0);
       acc1 = mfma_bf16(a, bx[1][ks], acc1);
     }
-    // keys: the low ib bits of V's pattern carry the centroid index; keep the
-    // 4 smallest per lane with med3 (min(a, b) = med3(a, b, -inf))
+  };
+  // keys: the low ib bits of V's pattern carry the centroid index; keep the
+  // 4 smallest per lane with med3 and an integer min (keys are positive floats,
+  // whose order is the order of their bit patterns)
+  auto keys = [&](int c0, const f32x16& acc0, const f32x16& acc1) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const uint32_t idx = (uint32_t)(c0 + c_row(r, half));
@@ -275,12 +276,20 @@ __global__ void __launch_bounds__(256) km_assign_kernel(const T* __restrict__ x,
       key[0][3] = med3f(key[0][2], key[0][3], k0);
       key[0][2] = med3f(key[0][1], key[0][2], k0);
       key[0][1] = med3f(key[0][0], key[0][1], k0);
-      key[0][0] = med3f(key[0][0], k0, -INFINITY);
+      key[0][0] = minkey(key[0][0], k0);
       key[1][3] = med3f(key[1][2], key[1][3], k1);
       key[1][2] = med3f(key[1][1], key[1][2], k1);
       key[1][1] = med3f(key[1][0], key[1][1], k1);
-      key[1][0] = med3f(key[1][0], k1, -INFINITY);
+      key[1][0] = minkey(key[1][0], k1);
     }
+  };
+  for (int ci = 0; ci < nchunk; ++ci) {
+    const int buf = ci & 1;
+    const bool more = ci + 1 < nchunk;
+    if (more) fetch((ci + 1) * 32);
+    f32x16 acc0, acc1;
+    mma(buf, acc0, acc1);
+    keys(ci * 32, acc0, acc1);
     if (more) store(buf ^ 1);
     __syncthreads();
   }
@@ -297,7 +306,7 @@ __global__ void __launch_bounds__(256) km_assign_kernel(const T* __restrict__ x,
       key[t][3] = med3f(key[t][2], key[t][3], kk);
       key[t][2] = med3f(key[t][1], key[t][2], kk);
       key[t][1] = med3f(key[t][0], key[t][1], kk);
-      key[t][0] = med3f(key[t][0], kk, -INFINITY);
+      key[t][0] = minkey(key[t][0], kk);
     }
   }
 
@@ -314,13 +323,14 @@ __global__ void __launch_bounds__(256) km_assign_kernel(const T* __restrict__ x,
   }
 
   // Near ties: exact distances of the candidates, one flagged token at a time.
-  // Each 16-lane row of the wave evaluates one centroid: a lane takes D/16
-  // consecutive coordinates, (x - c)^2 in fp32, then a fixed 16-lane butterfly
-  // (pairwise summation: error <= (log2 D + 3) u D, far inside the 1e-5
-  // relative tie tolerance).  With 4 candidates inside the window every
-  // centroid is scanned, 4 at a time.
+  // 2-3 candidates: each 16-lane row of the wave evaluates one centroid (a lane
+  // takes D/16 coordinates, fp32, then a fixed 16-lane butterfly: pairwise
+  // summation, error <= (log2 D + 3) u D, far inside the 1e-5 relative tie
+  // tolerance).  4 keys inside the window (rare): every centroid is scanned,
+  // one per lane, with fp64 sums and a wave argmin.
   constexpr int EPG = D / 16;
   const int grp = lane >> 4, gl = lane & 15;
+  __shared__ float s_x[4][D];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int n_mine = tok0 + 32 * t + col;
@@ -330,18 +340,19 @@ __global__ void __launch_bounds__(256) km_assign_kernel(const T* __restrict__ x,
       todo &= todo - 1;
       const int n = tok0 + 32 * t + src;
       const int nc = __shfl(ncand[t], src, SV_WAVE);
-      float xv[EPG];
-#pragma unroll
-      for (int e = 0; e < EPG; ++e) xv[e] = to_f32(xb[(size_t)n * D + gl * EPG + e]);
-      int cand[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) cand[j] = (int)(__float_as_uint(__shfl(key[t][j], src, SV_WAVE)) & imask);
       float best = 0.f;
       int bidx = -1;
-      const int count = nc >= 4 ? C : nc;
-      for (int j0 = 0; j0 < count; j0 += 4) {
-        int c = nc >= 4 ? j0 + grp : (grp == 0 ? cand[0] : grp == 1 ? cand[1] : grp == 2 ? cand[2] : cand[3]);
-        const bool live = (j0 + grp < count) && c < C;
+      if (nc < 4) {
+        float xv[EPG];
+#pragma unroll
+        for (int e = 0; e < EPG; ++e) xv[e] = to_f32(xb[(size_t)n * D + gl * EPG + e]);
+        // every lane needs all three candidates of lane src (a shuffle returns the
+        // source lane's register, so each key is fetched on its own)
+        const uint32_t c0 = __float_as_uint(__shfl(key[t][0], src, SV_WAVE)) & imask;
+        const uint32_t c1 = __float_as_uint(__shfl(key[t][1], src, SV_WAVE)) & imask;
+        const uint32_t c2 = __float_as_uint(__shfl(key[t][2], src, SV_WAVE)) & imask;
+        int c = (int)(grp == 0 ? c0 : grp == 1 ? c1 : c2);
+        const bool live = grp < nc && c < C;
         if (!live) c = 0;
         const float* cr = cb + (size_t)c * D + gl * EPG;
         float part = 0.f;
@@ -352,7 +363,7 @@ __global__ void __launch_bounds__(256) km_assign_kernel(const T* __restrict__ x,
         }
         const float dist = row16_sum(part);
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
+        for (int g = 0; g < 3; ++g) {
           const float dg = __shfl(dist, 16 * g, SV_WAVE);
           const int cg = __shfl(c, 16 * g, SV_WAVE);
           const bool lg = __shfl((int)live, 16 * g, SV_WAVE) != 0;
@@ -361,6 +372,34 @@ __global__ void __launch_bounds__(256) km_assign_kernel(const T* __restrict__ x,
             bidx = cg;
           }
         }
+      } else {
+        for (int d = lane; d < D; d += SV_WAVE) s_x[w][d] = to_f32(xb[(size_t)n * D + d]);
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        double bd = 0.0;
+        int bi = -1;
+        for (int c = lane; c < C; c += SV_WAVE) {
+          const float* cr = cb + (size_t)c * D;
+          double acc = 0.0;
+          for (int d = 0; d < D; d += 4) {
+            const f32x4 cv = *reinterpret_cast<const f32x4*>(cr + d);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const double dv = (double)s_x[w][d + e] - (double)cv[e];
+              acc = fma(dv, dv, acc);
+            }
+          }
+          if (bi < 0 || acc < bd) { bd = acc; bi = c; }  // c ascends within a lane
+        }
+        // wave argmin of (distance, index)
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) {
+          const double od = shfl_xor_d(bd, m);
+          const int oi = __shfl_xor(bi, m, SV_WAVE);
+          if (oi >= 0 && (bi < 0 || od < bd || (od == bd && oi < bi))) { bd = od; bi = oi; }
+        }
+        bidx = bi;
+        __builtin_amdgcn_wave_barrier();
       }
       if (lane == src) lab[t] = bidx;
     }
