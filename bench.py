@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--attn-only", action="store_true", help="after one layer, time only the attention pass")
     ap.add_argument("--attn-reps", type=int, default=5)
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="first run a plain device copy of this many MiB (calibrates HBM byte counters)")
     return ap.parse_args()
 
 
@@ -108,6 +110,14 @@ def main():
         w = scaled(w, H=args.heads)
     dev = torch.device("cuda:0")
     sv.load()
+    if args.copy_probe_mb:
+        n = args.copy_probe_mb << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"# copy probe: {n} bytes read, {n} bytes written", file=sys.stderr, flush=True)
+        del src, dst
     BH = w.B * w.H
     t0 = time.time()
     hs = gen_inputs(w, BH)

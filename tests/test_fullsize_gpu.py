@@ -1,0 +1,371 @@
+"""GPU parity at the full layer sizes, in the launch configuration the
+benchmark times: every call covers all heads of the layer at once, through
+the Layer object's buffers, workspaces and streams.  The oracle computes one
+sampled head per workload; the comparisons use the same rules and tolerances
+as the small-size parity tests.
+
+Workloads (seeded Gaussian mixtures standing in for real activations):
+  wan       1 x 40 x 75,600 x 128 bf16, C_q 100, C_k 500, 20 cold rounds, rho 0.25
+  hunyuan   1 x 24 x 118,800 x 128 bf16, same clustering and budget
+  sweep     the HunyuanVideo shape with a 1:2 mix of tight and loose
+            components, budgets 0.10, 0.15, 0.25, 0.40, 1.00
+  sequence  the Wan shape, one warm-started step (1 round from the previous
+            step's centroids after 40 cold rounds on step 0)
+
+Per sampled head the oracle runs every stage; each GPU stage is then given
+the oracle's inputs to that stage for that head (teacher forcing; the other
+heads carry the GPU's own intermediates, so the launch is the full one).
+Attention is compared on 512 sampled query rows (plus the first and last
+token) of the sampled head.  Progress lines go to stdout (pytest -s shows
+them) because the oracle takes tens of seconds per head."""
+import concurrent.futures
+import os
+import sys
+import time
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import svgear_oracle as orc
+from synth.gen import WORKLOADS, head_inputs
+from tests.helpers import check_labels_near_ties, f32, host, i32, mean_bound, to_dev
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
+
+SAMPLED_HEAD = {"wan": 39, "hunyuan": 0, "sweep": 5, "sequence": 17}
+N_ROWS = 512
+AMAX, AMEAN = 2e-2, 2e-3            # bf16 attention output vs the fp64 oracle
+LSE_TOL = 1e-2
+
+
+def say(msg):
+    print(f"[fullsize] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def sv():
+    import sparse_attention_video_amd as pkg
+    pkg.load()
+    assert torch.cuda.is_available()
+    return pkg
+
+
+def upload_layer(w, step=0):
+    """All heads' inputs on the GPU (generated in chunks to bound host memory);
+    returns the device tensors and the sampled head's host inputs."""
+    hs = SAMPLED_HEAD[w.name]
+    BH = w.B * w.H
+    shp = (w.B, w.H, w.N, w.D)
+    dev = {k: torch.empty(shp, dtype=torch.bfloat16, device="cuda") for k in ("q", "k", "v")}
+    dev["cq0"] = torch.empty((w.B, w.H, w.Cq, w.D), dtype=torch.float32, device="cuda")
+    dev["ck0"] = torch.empty((w.B, w.H, w.Ck, w.D), dtype=torch.float32, device="cuda")
+    keep = None
+    workers = min(16, os.cpu_count() or 1)
+    with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+        for c0 in range(0, BH, 8):
+            heads = list(range(c0, min(BH, c0 + 8)))
+            for h, x in zip(heads, ex.map(lambda h: head_inputs(w, h, step), heads)):
+                b, hh = divmod(h, w.H)
+                for key in ("q", "k", "v"):
+                    dev[key][b, hh].copy_(to_dev(x[key], "bf16"))
+                dev["cq0"][b, hh].copy_(f32(x["cq0"]))
+                dev["ck0"][b, hh].copy_(f32(x["ck0"]))
+                if h == hs:
+                    keep = x
+    return dev, keep
+
+
+def oracle_head(x, w, iters, density, rows):
+    """Every oracle stage for one head; the last k-means round is kept apart
+    so the GPU's last round can be fed the same starting centroids."""
+    sc = 1.0 / np.sqrt(w.D)
+    out = {"scale": sc}
+    for which, c0 in (("q", x["cq0"]), ("k", x["ck0"])):
+        X = x[which]
+        start = orc.lloyd(X, c0, iters - 1)[0] if iters > 1 else np.asarray(c0, np.float64)
+        # the GPU takes centroids as float32: the last round starts from exactly those
+        start = start.astype(np.float32).astype(np.float64)
+        lab = orc.assign(X, start)
+        out[f"c{which}_start"] = start
+        out[f"l{which}"] = lab
+        out[f"c{which}"] = orc.update(X, lab, start)
+    out["pq"], out["oq"] = orc.permute(out["lq"], w.Cq)
+    out["pk"], out["ok"] = orc.permute(out["lk"], w.Ck)
+    out["qbar"] = orc.means(x["q"], out["pq"], out["oq"])
+    out["kbar"] = orc.means(x["k"], out["pk"], out["ok"])
+    out["vbar"] = orc.means(x["v"], out["pk"], out["ok"])
+    Kp, Vp = x["k"][out["pk"]], x["v"][out["pk"]]
+    qs, ks = np.diff(out["oq"]), np.diff(out["ok"])
+    e, _ = orc.probe_errors(out["qbar"], Kp, Vp, out["kbar"], out["vbar"], out["ok"], sc, q_nonempty=qs > 0)
+    out["ratio"] = orc.ratios(e, qs, ks)
+    out["mask"] = orc.select(out["ratio"], qs, ks, density, w.N)
+    out["rows"] = rows
+    out["O"], out["LSE"] = orc.attend(x["q"], x["k"], x["v"], out["pq"], out["oq"], out["pk"], out["ok"],
+                                      out["kbar"], out["vbar"], out["mask"], sc, rows=rows)
+    return out
+
+
+def sample_rows(w, h):
+    r = np.random.default_rng([977, h]).choice(w.N, N_ROWS, replace=False)
+    return np.unique(np.concatenate([r, [0, w.N - 1]]))
+
+
+_CACHE = {}
+
+
+def full_case(sv, name):
+    """GPU layer on all heads (the benchmark's step) + the oracle on one head."""
+    if name in _CACHE:
+        return _CACHE[name]
+    w = WORKLOADS[name]
+    h = SAMPLED_HEAD[name]
+    t0 = time.time()
+    dev, x = upload_layer(w)
+    say(f"{name}: inputs for {w.B * w.H} heads on the GPU ({time.time() - t0:.1f}s)")
+    L = sv.Layer(w.B, w.H, w.N, w.D, w.Cq, w.Ck, dtype=torch.bfloat16)
+    cq, ck = dev["cq0"].clone(), dev["ck0"].clone()
+    sc = 1.0 / np.sqrt(w.D)
+    L.forward(dev["q"], dev["k"], dev["v"], cq, ck, w.iters, w.density, sc)
+    torch.cuda.synchronize()
+    say(f"{name}: GPU layer done")
+    t0 = time.time()
+    rows = sample_rows(w, h)
+    ref = oracle_head(x, w, w.iters, w.density, rows)
+    say(f"{name}: oracle head {h} done ({time.time() - t0:.1f}s)")
+    _CACHE[name] = (w, h, dev, x, L, cq, ck, ref)
+    return _CACHE[name]
+
+
+def bh_index(w, h):
+    return divmod(h, w.H)
+
+
+def forced(t, w, h, value):
+    """Clone of a [B, H, ...] device tensor with head h replaced by value."""
+    t = t.clone()
+    b, hh = bh_index(w, h)
+    t[b, hh].copy_(value)
+    return t
+
+
+def check_kmeans_round(sv, w, h, dev, x, ref, which, iters_before):
+    """GPU round from the oracle's starting centroids for head h."""
+    C = w.Cq if which == "q" else w.Ck
+    cent = forced(dev[f"c{which}0"], w, h, f32(ref[f"c{which}_start"]))
+    lab, perm, off = sv.kmeans(dev[which], cent, 1)
+    b, hh = bh_index(w, h)
+    lab, perm, off, cent = (host(t[b, hh]) for t in (lab, perm, off, cent))
+    X = x[which]
+    nbad = check_labels_near_ties(X, ref[f"c{which}_start"], lab, ref[f"l{which}"])
+    say(f"{w.name}: k-means {which} round {iters_before + 1}: {nbad} near-tie label differences")
+    if nbad == 0:
+        np.testing.assert_array_equal(perm, ref[f"p{which}"])
+        np.testing.assert_array_equal(off, ref[f"o{which}"])
+        bound = mean_bound(X, ref[f"p{which}"], ref[f"o{which}"])
+        err = np.abs(cent - ref[f"c{which}"]).max(axis=1)
+        assert np.all(err <= bound + 1e-30), (err.max(), bound.max())
+        empty = np.diff(ref[f"o{which}"]) == 0
+        np.testing.assert_array_equal(cent[empty], ref[f"c{which}_start"][empty].astype(np.float32))
+    else:
+        assert nbad <= 1e-4 * w.N
+
+
+def teacher_forced_device(w, h, dev, x, L, ref):
+    """Stage inputs for route / attention: head h from the oracle, the other
+    heads from the GPU's own layer."""
+    pk, pq = ref["pk"], ref["pq"]
+    return dict(
+        qp=forced(L.qp, w, h, to_dev(x["q"][pq], "bf16")),
+        kp=forced(L.kp, w, h, to_dev(x["k"][pk], "bf16")),
+        vp=forced(L.vp, w, h, to_dev(x["v"][pk], "bf16")),
+        pq=forced(L.pq, w, h, i32(pq)),
+        oq=forced(L.oq, w, h, i32(ref["oq"])),
+        ok=forced(L.ok, w, h, i32(ref["ok"])),
+        qm=forced(L.qm, w, h, f32(ref["qbar"])),
+        km=forced(L.km, w, h, f32(ref["kbar"])),
+        vm=forced(L.vm, w, h, f32(ref["vbar"])),
+    )
+
+
+def check_route(sv, w, h, t, ref, density, ratios=None, mask_ref=None):
+    sc = ref["scale"]
+    b, hh = bh_index(w, h)
+    scores, mask = sv.route(t["qm"], t["oq"], t["kp"], t["vp"], t["km"], t["vm"], t["ok"], sc, density)
+    r_o = ref["ratio"] if ratios is None else ratios
+    m_o = ref["mask"] if mask_ref is None else mask_ref
+    scores, mask = host(scores[b, hh]).astype(np.float64), host(mask[b, hh])
+    rowmax = r_o.max(axis=1, keepdims=True).astype(np.float64)
+    err = np.abs(scores - r_o)
+    assert (err <= 2e-3 * r_o + 1e-7 * rowmax + 1e-37).all(), (err / (r_o + 1e-30)).max()
+    ndiff = 0
+    for i in np.flatnonzero((mask != m_o).any(axis=1)):
+        thr = r_o[i][m_o[i] == 1].min()
+        diff = np.flatnonzero(mask[i] != m_o[i])
+        ndiff += diff.size
+        assert np.all(np.abs(r_o[i][diff] - thr) <= 4e-3 * thr + 1e-7 * rowmax[i]), (i, diff)
+    # bit-exact selection from the oracle's float32 ratios
+    s_in = forced(torch.zeros((w.B, w.H, w.Cq, w.Ck), dtype=torch.float32, device="cuda"), w, h, f32(r_o))
+    _, mask2 = sv.route(t["qm"], t["oq"], t["kp"], t["vp"], t["km"], t["vm"], t["ok"], sc, density,
+                        scores_in=s_in)
+    np.testing.assert_array_equal(host(mask2[b, hh]), m_o)
+    return ndiff
+
+
+def check_attention_rows(w, h, out, lse, O, LSE, rows):
+    b, hh = bh_index(w, h)
+    o = host(out[b, hh])[rows]
+    err = np.abs(o - O[rows])
+    say(f"{w.name}: attention on {rows.size} rows: max {err.max():.3e}, mean {err.mean():.3e}")
+    assert err.max() <= AMAX and err.mean() <= AMEAN, (err.max(), err.mean())
+    if lse is not None:
+        assert np.abs(host(lse[b, hh])[rows] - LSE[rows]).max() <= LSE_TOL
+
+
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["wan", "hunyuan"])
+@pytest.mark.parametrize("which", ["q", "k"])
+def test_full_kmeans_last_round(sv, name, which):
+    w, h, dev, x, L, cq, ck, ref = full_case(sv, name)
+    check_kmeans_round(sv, w, h, dev, x, ref, which, w.iters - 1)
+
+
+@pytest.mark.parametrize("name", ["wan", "hunyuan"])
+def test_full_centroids(sv, name):
+    w, h, dev, x, L, cq, ck, ref = full_case(sv, name)
+    b, hh = bh_index(w, h)
+    for key, p, o in (("q", "pq", "oq"), ("k", "pk", "ok"), ("v", "pk", "ok")):
+        perm = forced(L.pq if p == "pq" else L.pk, w, h, i32(ref[p]))
+        off = forced(L.oq if o == "oq" else L.ok, w, h, i32(ref[o]))
+        xp, mu = sv.centroids(dev[key], perm, off)
+        xp, mu = host(xp[b, hh]), host(mu[b, hh])
+        np.testing.assert_array_equal(xp, x[key][ref[p]])
+        want = ref["qbar" if key == "q" else key + "bar"]
+        err = np.abs(mu - want).max(axis=1)
+        assert (err <= mean_bound(x[key], ref[p], ref[o]) + 1e-30).all()
+
+
+@pytest.mark.parametrize("name", ["wan", "hunyuan"])
+def test_full_route(sv, name):
+    w, h, dev, x, L, cq, ck, ref = full_case(sv, name)
+    t = teacher_forced_device(w, h, dev, x, L, ref)
+    ndiff = check_route(sv, w, h, t, ref, w.density)
+    say(f"{name}: route mask differs from the oracle's in {ndiff} near-tie blocks")
+
+
+@pytest.mark.parametrize("name", ["wan", "hunyuan"])
+def test_full_attention(sv, name):
+    w, h, dev, x, L, cq, ck, ref = full_case(sv, name)
+    t = teacher_forced_device(w, h, dev, x, L, ref)
+    mask = forced(L.mask, w, h, torch.from_numpy(ref["mask"].astype(np.uint8)).cuda())
+    out, lse = sv.sparse_attn(t["qp"], t["kp"], t["vp"], t["pq"], t["oq"], t["ok"], t["km"], t["vm"], mask,
+                              ref["scale"], want_lse=True)
+    check_attention_rows(w, h, out, lse, ref["O"], ref["LSE"], ref["rows"])
+
+
+def first_divergence(sv, w, h, dev, x, which):
+    """Rounds 1, 2, ... of the GPU's cold k-means (all heads, r rounds per
+    call) against the oracle's Lloyd iterates for head h.  Returns the first
+    round whose labels differ and the number of differing labels there; the
+    differences must be near ties for the oracle's centroids of the round
+    before (the GPU's own centroids agree with them to float32 rounding)."""
+    b, hh = bh_index(w, h)
+    X = x[which]
+    C = np.asarray(x["cq0"] if which == "q" else x["ck0"], np.float64)
+    for r in range(1, w.iters + 1):
+        lab_o = orc.assign(X, C)
+        cent = dev[f"c{which}0"].clone()
+        lab_g = host(sv.kmeans(dev[which], cent, r)[0][b, hh])
+        if (lab_g != lab_o).any():
+            return r, check_labels_near_ties(X, C, lab_g, lab_o)
+        C = orc.update(X, lab_o, C)
+    return None, 0
+
+
+@pytest.mark.parametrize("name", ["wan", "hunyuan"])
+def test_full_layer_end_to_end(sv, name):
+    """The benchmark's step itself (cold k-means, all stages) against the
+    oracle's layer for the sampled head.  Lloyd iterations amplify a near tie
+    (a token whose two nearest centroids agree to float32 rounding) into
+    later label changes, so where the final labels differ the first round
+    that differs must differ only at near ties."""
+    w, h, dev, x, L, cq, ck, ref = full_case(sv, name)
+    b, hh = bh_index(w, h)
+    lq, lk = host(L.lq[b, hh]), host(L.lk[b, hh])
+    dq, dk = int((lq != ref["lq"]).sum()), int((lk != ref["lk"]).sum())
+    mask = host(L.mask[b, hh])
+    agree = float((mask == ref["mask"]).mean())
+    say(f"{name}: end to end: {dq} / {dk} label differences (Q / K), mask agreement {agree:.5f}")
+    for which, nd in (("q", dq), ("k", dk)):
+        if nd:
+            r, n = first_divergence(sv, w, h, dev, x, which)
+            assert r is not None
+            say(f"{name}: {which} labels first differ in round {r}, at {n} near ties")
+    if dq == 0 and dk == 0:
+        assert agree > 0.99
+        if agree == 1.0:
+            check_attention_rows(w, h, L.out, None, ref["O"], ref["LSE"], ref["rows"])
+
+
+def test_full_density_sweep(sv):
+    """Every budget of the sweep on the HunyuanVideo shape: exact selection
+    from the oracle's ratios, the GPU's own ratios within tolerance, and
+    attention at the lowest budget and at 100 % (= full softmax attention)."""
+    w, h, dev, x, L, cq, ck, ref = full_case(sv, "sweep")
+    t = teacher_forced_device(w, h, dev, x, L, ref)
+    qs, ks = np.diff(ref["oq"]), np.diff(ref["ok"])
+    b, hh = bh_index(w, h)
+    rows = ref["rows"]
+    for rho in w.densities:
+        m_o = orc.select(ref["ratio"], qs, ks, rho, w.N)
+        ndiff = check_route(sv, w, h, t, ref, rho, mask_ref=m_o)
+        realised = float((qs * (m_o * ks[None, :]).sum(1)).sum()) / float(w.N) ** 2
+        say(f"sweep: density {rho}: realised {realised:.4f}, {ndiff} near-tie blocks")
+        if rho in (min(w.densities), 1.0):
+            mask = forced(L.mask, w, h, torch.from_numpy(m_o.astype(np.uint8)).cuda())
+            out, lse = sv.sparse_attn(t["qp"], t["kp"], t["vp"], t["pq"], t["oq"], t["ok"], t["km"], t["vm"],
+                                      mask, ref["scale"], want_lse=True)
+            if rho == 1.0:
+                assert (m_o[qs > 0] == (ks > 0)[None, :]).all() and not m_o[qs == 0].any()
+                O = np.full((w.N, w.D), np.nan)
+                O[rows] = orc.full_attention(x["q"][rows], x["k"], x["v"], ref["scale"])
+                check_attention_rows(w, h, out, None, O, None, rows)
+            else:
+                O, LSE = orc.attend(x["q"], x["k"], x["v"], ref["pq"], ref["oq"], ref["pk"], ref["ok"],
+                                    ref["kbar"], ref["vbar"], m_o, ref["scale"], rows=rows)
+                check_attention_rows(w, h, out, lse, O, LSE, rows)
+
+
+def test_full_sequence_warm_step(sv):
+    """Denoising sequence: step 1 runs one round warm-started from step 0's
+    centroids (40 cold rounds), at the Wan shape with drifted means."""
+    w = WORKLOADS["sequence"]
+    h = SAMPLED_HEAD["sequence"]
+    t0 = time.time()
+    dev0, x0 = upload_layer(w, step=0)
+    sc = 1.0 / np.sqrt(w.D)
+    start = {}
+    for which, c0 in (("q", x0["cq0"]), ("k", x0["ck0"])):
+        start[which] = orc.lloyd(x0[which], c0, w.iters)[0].astype(np.float32).astype(np.float64)
+    say(f"sequence: oracle step 0 ({w.iters} rounds) done ({time.time() - t0:.1f}s)")
+    # the GPU's own step 0 on every head, then step 1 on every head warm
+    L = sv.Layer(w.B, w.H, w.N, w.D, w.Cq, w.Ck, dtype=torch.bfloat16)
+    cq, ck = dev0["cq0"].clone(), dev0["ck0"].clone()
+    L.forward(dev0["q"], dev0["k"], dev0["v"], cq, ck, w.iters, w.density, sc)
+    del dev0
+    dev1, x1 = upload_layer(w, step=1)
+    mask0 = host(L.mask)
+    L.forward(dev1["q"], dev1["k"], dev1["v"], cq, ck, w.iters_warm, w.density, sc)
+    torch.cuda.synchronize()
+    churn = float((host(L.mask) != mask0).mean())
+    say(f"sequence: routing-mask churn step 0 -> 1 over all heads: {churn:.4f}")
+    for which in ("q", "k"):
+        C = w.Cq if which == "q" else w.Ck
+        ref = {f"c{which}_start": start[which]}
+        lab = orc.assign(x1[which], start[which])
+        ref[f"l{which}"] = lab
+        ref[f"c{which}"] = orc.update(x1[which], lab, start[which])
+        ref[f"p{which}"], ref[f"o{which}"] = orc.permute(lab, C)
+        dev1[f"c{which}0"] = cq if which == "q" else ck
+        check_kmeans_round(sv, w, h, dev1, x1, ref, which, w.iters)
