@@ -35,6 +35,18 @@ def _compile(src: str, obj: str, verbose: bool) -> None:
         print(out, file=sys.stderr)
 
 
+def _check_no_undefined_kernels(lib: str) -> None:
+    """A kernel whose host-side stub the compiler silently dropped shows up as
+    an undefined symbol of the library's own namespace; refuse such a build."""
+    nm = shutil.which("nm")
+    if nm is None:
+        return
+    r = subprocess.run([nm, "-D", "--undefined-only", lib], capture_output=True, text=True)
+    bad = [l.split()[-1] for l in r.stdout.splitlines() if "3svg" in l]
+    if bad:
+        raise RuntimeError("library has undefined kernel symbols (host stub not emitted): " + ", ".join(bad))
+
+
 def build(verbose: bool = False) -> str:
     """Always recompiles every source and relinks the library; returns its path."""
     objdir = os.path.join(HERE, "_build")
@@ -48,6 +60,7 @@ def build(verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
+    _check_no_undefined_kernels(tmp)
     os.replace(tmp, LIB)
     return LIB
 

@@ -390,24 +390,59 @@ __global__ void __launch_bounds__(256) attn_kernel(const T* __restrict__ qp, con
 }
 
 // ---------------------------------------------------------------------------
-// bf16 path.  Same algorithm, arranged for throughput:
-//  * each thread owns one staging unit (4 consecutive keys x 8 dims); the
-//    next tile's K/V rows are loaded into registers while the current tile
-//    computes, then written to the other LDS buffer (one barrier per tile);
-//  * K rows are copied as raw 16-byte vectors; V is transposed to V^T with
-//    byte permutes on the way into LDS;
+// bf16 path.  Same algorithm, arranged for throughput on gfx950:
+//  * K and V rows go straight from global memory into LDS
+//    (global_load_lds_dwordx4, no registers); the source row of every key
+//    position of a tile comes from a small table that wave 0 fills two tiles
+//    ahead by walking the selected-cluster list;
+//  * tiles are unpadded, 16-byte chunks swizzled per row (see below); the
+//    S^T = K Q^T fragments are plain 16-byte reads, and the V^T fragments of
+//    O^T = V^T P^T come from row-major V through the transposing LDS read
+//    ds_read_b64_tr_b16;
+//  * two tile buffers, each its own LDS array, so the reads of the tile in
+//    use never wait for the loads of the next one;
 //  * the running max is raised only when a tile's max exceeds it by more
 //    than AT_LAZY (log2 units), so O and the sum are rarely rescaled (the
 //    weights stay <= 2^AT_LAZY, and the final normalisation uses the same
 //    max, so the result is unchanged);
+//  * the row sum adds the bf16-rounded weights that multiply V (v_dot2), so
+//    numerator and denominator use the same weights;
 //  * skipped clusters (pseudo-keys, bf16 hi + lo) run in a second loop.
+//
+// Tile layout: 64 rows of D bf16 (ROWB = 2 D bytes), chunk c (16 bytes) of
+// row r in slot c ^ swz(r):
+//   K: swz(r) = r & 7      -- an A-fragment read touches 8 consecutive rows
+//                            at one chunk: 8 distinct bank quads;
+//   V: swz(r) = 2 (r & 3)  -- a transposing read touches 4 rows x 2 chunks
+//                            per 16 lanes: 8 distinct bank quads.
+// One load instruction fills 1 KiB = RPI consecutive rows; lane L writes
+// slot L % CH of row L / CH (CH = chunks per row).
 // ---------------------------------------------------------------------------
 constexpr float AT_LAZY = 8.f;
 constexpr int AT_XCDS = 8;  // MI355X: 8 XCDs, each with its own L2
 
-__device__ __forceinline__ uint32_t perm_b32(uint32_t hi_src, uint32_t lo_src, uint32_t sel) {
-  return __builtin_amdgcn_perm(hi_src, lo_src, sel);
+typedef __bf16 at_bf16x2 __attribute__((ext_vector_type(2)));
+#define AT_LDS(p) ((__attribute__((address_space(3))) void*)(p))
+#define AT_LDS16(p) ((__attribute__((address_space(3))) bf16x4*)(p))
+
+// 16 bytes per lane from global memory straight into LDS: lane L's bytes land
+// at dst + 16 L (dst is the same for the whole wave)
+__device__ __forceinline__ void load_lds16(const char* src, char* dst) {
+  __builtin_amdgcn_global_load_lds(src, AT_LDS(dst), 16, 0, 0);
 }
+
+// A fragment of V^T (8 keys at one dim) from two transposing reads of 4 keys each
+__device__ __forceinline__ bf16x8 vt_frag(const char* p0, const char* p1) {
+  const bf16x4 x0 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(AT_LDS16(p0));
+  const bf16x4 x1 = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(AT_LDS16(p1));
+  return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <int D>
+struct AtTile {
+  static constexpr int ROWB = 2 * D, CH = D / 8, RPI = 64 / CH, NI = CH / 4;
+  static constexpr int BYTES = AT_BN * ROWB;
+};
 
 template <int D>
 __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restrict__ qp, const bf16* __restrict__ kp,
@@ -420,27 +455,26 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
                                                            const uint8_t* __restrict__ mask, int N, float sl2,
                                                            bf16* __restrict__ out, float* __restrict__ lse,
                                                            int maxt, int BHn) {
-  constexpr int KS = D / 16, DT = D / 32;
-  // LDS row strides: K rows 68 dwords (8 consecutive rows hit distinct bank
-  // quads for 16-byte accesses); V^T rows 34 dwords (16 consecutive rows hit
-  // distinct bank pairs for the 8-byte fragment reads)
-  constexpr int SK = D + 8, SV = AT_BN + 4;
-  constexpr int NUNIT = (AT_BN / 4) * (D / 8);
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  bf16* sK = reinterpret_cast<bf16*>(smem);                 // [2][64][SK]
-  bf16* sV = sK + 2 * AT_BN * SK;                           // [2][D][SV]  (V^T)
-  float* sBias = reinterpret_cast<float*>(sV + 2 * D * SV);  // [64]
-  int* sSrc = reinterpret_cast<int*>(sBias + AT_BN);        // [2][64]
-  int* sSelStart = sSrc + 2 * AT_BN;
-  int* sSelPre = sSelStart + Ck;
-  int* sComp = sSelPre + Ck + 1;
+  using TL = AtTile<D>;
+  constexpr int KS = D / 16, DT = D / 32, ROWB = TL::ROWB, CH = TL::CH, RPI = TL::RPI, NI = TL::NI;
+  __shared__ __attribute__((aligned(1024))) char sK0[TL::BYTES];
+  __shared__ __attribute__((aligned(1024))) char sK1[TL::BYTES];
+  __shared__ __attribute__((aligned(1024))) char sV0[TL::BYTES];
+  __shared__ __attribute__((aligned(1024))) char sV1[TL::BYTES];
+  __shared__ __attribute__((aligned(16))) int sTab[2 * AT_BN];
+  __shared__ float sBias[AT_BN];
   __shared__ int sScan[16];
   __shared__ int sInfo[4];
+  extern __shared__ __attribute__((aligned(16))) int sLists[];
+  int* sSelStart = sLists;        // [Ck]  first permuted row of the c-th selected cluster
+  int* sSelPre = sSelStart + Ck;  // [Ck+1] key position where the c-th selected cluster begins
+  int* sComp = sSelPre + Ck + 1;  // [Ck]  skipped non-empty clusters
 
   // Workgroups are dealt to the 8 XCDs round-robin by linear id; give each XCD
   // a contiguous range of (head, tile) so the tiles of one query cluster, which
   // stream the same keys, run on the same XCD and share its L2.
-  const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
+  const int tid = threadIdx.x, lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(wave_id());
   const int half = lane >> 5, col = lane & 31;
   const int per_xcd = (int)gridDim.x / AT_XCDS;
   const int logical = ((int)blockIdx.x % AT_XCDS) * per_xcd + (int)blockIdx.x / AT_XCDS;
@@ -485,8 +519,8 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
   const int npseudo = (ncomp + AT_BN - 1) / AT_BN;
 
   const bf16* qb = qp + (size_t)bh * N * D;
-  const bf16* kb = kp + (size_t)bh * N * D;
-  const bf16* vb = vp + (size_t)bh * N * D;
+  const char* kb = reinterpret_cast<const char*>(kp + (size_t)bh * N * D);
+  const char* vb = reinterpret_cast<const char*>(vp + (size_t)bh * N * D);
   const int qrow = row0 + 32 * w + col;
   const bool qok = qrow < rowEnd;
   bf16x8 bq[KS];
@@ -501,84 +535,87 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
   for (int t = 0; t < DT; ++t) o[t] = f32x16{};
   float m_run = -1e30f, l_run = 0.f;
 
-  // staging unit: keys 4*g4 .. 4*g4+3, dims d0 .. d0+7.  Each thread walks the
-  // selected-cluster list with its own cursor (positions only grow), and rows
-  // past the end of the stream load row 0 instead; their scores are masked.
-  const bool has_unit = tid < NUNIT;
-  const int g4 = tid & 15, d0 = (tid >> 4) * 8;
-  int cur = 0, cur_base = 0, cur_pre = 0;               // cluster cursor: start row, key prefix
-  int nxt = nsel > 1 ? sSelPre[1] : 0x7fffffff;        // key prefix where the next cluster begins
-  if (nsel > 0) { cur_base = sSelStart[0]; cur_pre = 0; }
-  int kcur = cur, kcur_base = cur_base, kcur_pre = cur_pre, knxt = nxt;  // second cursor (K rows)
-  u32x4 pk[4], pv[4];
-  auto issue = [&](int kt) {
-    if (has_unit) {
+  // ---- per-lane LDS offsets
+  // S^T A-fragment: row sub*32 + col, chunk 2 ks + half
+  int aK[KS];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int p = kt * AT_BN + 4 * g4 + r;
-        while (p >= nxt) {
-          ++cur;
-          cur_base = sSelStart[cur];
-          cur_pre = nxt;
-          nxt = cur + 1 < nsel ? sSelPre[cur + 1] : 0x7fffffff;
-        }
-        const int src = p < nkeys ? cur_base + (p - cur_pre) : 0;
-        pv[r] = ld16(vb + (size_t)src * D + d0);
-      }
+  for (int ks = 0; ks < KS; ++ks) aK[ks] = col * ROWB + (((2 * ks + half) ^ (col & 7)) << 4);
+  // V^T A-fragment by transposing reads: in each 16-lane group (j = lane % 16,
+  // group g = lane / 16) lane j points at row kbase + j / 4, dims
+  // 32 t + 16 (g & 1) + 4 (j % 4) .. +3; lane j then receives the 4 rows'
+  // values at dim 32 t + 16 (g & 1) + j.
+  int aV[DT];
+  {
+    const int j = lane & 15, g1 = (lane >> 4) & 1, r4 = j >> 2;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int p = kt * AT_BN + g4 + 16 * r;
-        while (p >= knxt) {
-          ++kcur;
-          kcur_base = sSelStart[kcur];
-          kcur_pre = knxt;
-          knxt = kcur + 1 < nsel ? sSelPre[kcur + 1] : 0x7fffffff;
-        }
-        const int src = p < nkeys ? kcur_base + (p - kcur_pre) : 0;
-        pk[r] = ld16(kb + (size_t)src * D + d0);
-      }
+    for (int t = 0; t < DT; ++t) {
+      const int chunk = 4 * t + 2 * g1 + ((j >> 1) & 1);
+      aV[t] = (4 * half + r4) * ROWB + ((chunk ^ (2 * (r4 & 3))) << 4) + ((j & 1) << 3);
     }
+  }
+  // direct-to-LDS loads: instruction i of wave w fills rows (w NI + i) RPI + L / CH
+  const int lq = lane / CH, lslot = lane % CH;
+  int chK[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) chK[i] = lslot ^ ((((w * NI + i) * RPI) + lq) & 7);
+  const int chV = lslot ^ (2 * (lq & 3));
+
+  // ---- source-row table, filled by wave 0 two tiles ahead
+  int tc = 0, tc_base = nsel > 0 ? sSelStart[0] : 0, tc_pre = 0;
+  int tc_nxt = nsel > 1 ? sSelPre[1] : 0x7fffffff;
+  auto fill_table = [&](int kt) {
+    const int p = kt * AT_BN + lane;
+    while (p >= tc_nxt) {
+      ++tc;
+      tc_base = sSelStart[tc];
+      tc_pre = tc_nxt;
+      tc_nxt = tc + 1 < nsel ? sSelPre[tc + 1] : 0x7fffffff;
+    }
+    const int src = p < nkeys ? tc_base + (p - tc_pre) : 0;  // rows past the end load row 0, masked later
+    const int rw = lane >> 4, rem = lane & 15;
+    sTab[(kt & 1) * AT_BN + rw * 16 + (rem % RPI) * NI + rem / RPI] = src;
   };
-  auto commit = [&](int buf) {
-    if (has_unit) {
-      bf16* K = sK + buf * AT_BN * SK;
-      bf16* V = sV + buf * D * SV;
+  auto issue = [&](int kt, char* dK, char* dV) {
+    const int* tab = sTab + (kt & 1) * AT_BN + w * 16 + lq * NI;
+    int src[NI];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) st16(&K[(g4 + 16 * r) * SK + d0], pk[r]);
+    for (int i = 0; i < NI; ++i) src[i] = tab[i];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        uint2 lo, hi;
-        lo.x = perm_b32(pv[1][m], pv[0][m], 0x05040100u);
-        lo.y = perm_b32(pv[3][m], pv[2][m], 0x05040100u);
-        hi.x = perm_b32(pv[1][m], pv[0][m], 0x07060302u);
-        hi.y = perm_b32(pv[3][m], pv[2][m], 0x07060302u);
-        *reinterpret_cast<uint2*>(&V[(d0 + 2 * m) * SV + 4 * g4]) = lo;
-        *reinterpret_cast<uint2*>(&V[(d0 + 2 * m + 1) * SV + 4 * g4]) = hi;
-      }
+    for (int i = 0; i < NI; ++i) {
+      const int g = w * NI + i;
+      const uint32_t rowoff = (uint32_t)src[i] * (uint32_t)ROWB;
+      load_lds16(kb + rowoff + (chK[i] << 4), dK + g * 1024);
+      load_lds16(vb + rowoff + (chV << 4), dV + g * 1024);
     }
   };
 
-  // one tile of keys already in LDS buffer `buf`: S^T, online softmax, O^T += V^T P^T.
-  // Real tiles take the max on the raw scores (scale > 0) and fold the scale
-  // into one FMA per weight; pseudo tiles add the log2 n_j bias first.
-  auto compute = [&](int buf, int lim, bool pseudo) {
-    const bf16* Kh = pseudo ? sK : sK + buf * AT_BN * SK;
-    const bf16* Vh = pseudo ? sV : sV + buf * D * SV;
+  // one tile of keys in LDS: S^T, online softmax, O^T += V^T P^T.  Real tiles
+  // take the max on the raw scores (scale > 0) and fold the scale into one FMA
+  // per weight; pseudo tiles (hi in buffer 0, lo in buffer 1) add the log2 n_j
+  // bias first.
+  auto compute = [&](const char* Kh, const char* Vh, int lim, bool pseudo) {
     f32x16 s[2] = {f32x16{}, f32x16{}};
+    {
+      // fragments of step ks + 1 are read before the products of step ks
+      bf16x8 fr[2][2];
+      fr[0][0] = *reinterpret_cast<const bf16x8*>(Kh + aK[0]);
+      fr[0][1] = *reinterpret_cast<const bf16x8*>(Kh + aK[0] + 32 * ROWB);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-        s[sub] = mfma_bf16(*reinterpret_cast<const bf16x8*>(&Kh[(sub * 32 + col) * SK + 16 * ks + 8 * half]), bq[ks],
-                           s[sub]);
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 1 < KS) {
+          fr[(ks + 1) & 1][0] = *reinterpret_cast<const bf16x8*>(Kh + aK[ks + 1]);
+          fr[(ks + 1) & 1][1] = *reinterpret_cast<const bf16x8*>(Kh + aK[ks + 1] + 32 * ROWB);
+        }
+        s[0] = mfma_bf16(fr[ks & 1][0], bq[ks], s[0]);
+        s[1] = mfma_bf16(fr[ks & 1][1], bq[ks], s[1]);
+      }
+    }
     if (pseudo) {
-      const bf16* Kl = sK + AT_BN * SK;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub)
-          s[sub] = mfma_bf16(*reinterpret_cast<const bf16x8*>(&Kl[(sub * 32 + col) * SK + 16 * ks + 8 * half]), bq[ks],
-                             s[sub]);
+          s[sub] = mfma_bf16(*reinterpret_cast<const bf16x8*>(sK1 + aK[ks] + sub * 32 * ROWB), bq[ks], s[sub]);
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
@@ -610,65 +647,65 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
     }
     const float sc = pseudo ? 1.f : sl2;
     const float nm = -m_run;
-    float lsum = 0.f;
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[sub][r], sc, nm));
-        s[sub][r] = p;
-        lsum += p;
-      }
-    l_run += lsum;
+    const at_bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
       const int sub = st >> 1, tp = st & 1;
       bf16x8 pb;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pb[e] = (bf16)s[sub][8 * tp + e];
-      const int k0 = 16 * st + 4 * half;
+      for (int e = 0; e < 8; ++e) pb[e] = (bf16)__builtin_amdgcn_exp2f(fmaf(s[sub][8 * tp + e], sc, nm));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const at_bf16x2 pr = {pb[2 * e], pb[2 * e + 1]};
+        l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
+      }
 #pragma unroll
       for (int t = 0; t < DT; ++t) {
-        const int d = 32 * t + col;
-        const bf16x4 x0 = *reinterpret_cast<const bf16x4*>(&Vh[d * SV + k0]);
-        const bf16x4 x1 = *reinterpret_cast<const bf16x4*>(&Vh[d * SV + k0 + 8]);
-        bf16x8 a;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) { a[e] = x0[e]; a[e + 4] = x1[e]; }
-        o[t] = mfma_bf16(a, pb, o[t]);
+        const char* base = Vh + aV[t] + 16 * st * ROWB;
+        o[t] = mfma_bf16(vt_frag(base, base + 8 * ROWB), pb, o[t]);
         if (pseudo) {
-          const bf16* Vl = sV + D * SV;
-          const bf16x4 y0 = *reinterpret_cast<const bf16x4*>(&Vl[d * SV + k0]);
-          const bf16x4 y1 = *reinterpret_cast<const bf16x4*>(&Vl[d * SV + k0 + 8]);
-          bf16x8 b;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) { b[e] = y0[e]; b[e + 4] = y1[e]; }
-          o[t] = mfma_bf16(b, pb, o[t]);
+          const char* bl = sV1 + aV[t] + 16 * st * ROWB;
+          o[t] = mfma_bf16(vt_frag(bl, bl + 8 * ROWB), pb, o[t]);
         }
       }
     }
   };
 
-  // ---- selected keys: packed 64-key tiles, double buffered
+  // ---- selected keys: packed 64-key tiles, double buffered, loop unrolled by
+  // two so each half reads one fixed buffer
   if (nreal > 0) {
-    issue(0);
-    commit(0);
+    if (w == 0) {
+      fill_table(0);
+      if (nreal > 1) fill_table(1);
+    }
+    __syncthreads();
+    issue(0, sK0, sV0);
     // the Q fragments and tile 0 are in: later waits only cover the prefetch
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    for (int kt = 0; kt < nreal; ++kt) {
-      const bool more = kt + 1 < nreal;
-      if (more) issue(kt + 1);
-      compute(kt & 1, nkeys - kt * AT_BN, false);
-      if (more) commit((kt + 1) & 1);
+    for (int kt = 0; kt < nreal; kt += 2) {
+      if (kt + 1 < nreal) issue(kt + 1, sK1, sV1);
+      if (w == 0 && kt + 2 < nreal) fill_table(kt + 2);
+      compute(sK0, sV0, nkeys - kt * AT_BN, false);
+      __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
+      if (kt + 1 < nreal) {
+        if (kt + 2 < nreal) issue(kt + 2, sK0, sV0);
+        if (w == 0 && kt + 3 < nreal) fill_table(kt + 3);
+        compute(sK1, sV1, nkeys - (kt + 1) * AT_BN, false);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
     }
   }
 
-  // ---- skipped non-empty clusters: pseudo-keys k_bar_j (hi, lo), v_bar_j (hi, lo), bias log2 n_j
+  // ---- skipped non-empty clusters: pseudo-keys k_bar_j (hi, lo), v_bar_j (hi, lo), bias log2 n_j.
+  // Staging unit: keys 4 g4 .. 4 g4 + 3, dims d0 .. d0 + 7 (one 16-byte chunk per key).
+  constexpr int NUNIT = (AT_BN / 4) * (D / 8);
+  const bool has_unit = tid < NUNIT;
+  const int g4 = tid & 15, d0 = (tid >> 4) * 8;
   for (int pt = 0; pt < npseudo; ++pt) {
     if (has_unit) {
-      float kf[4][8], vf[4][8];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int c = pt * AT_BN + 4 * g4 + r;
@@ -684,43 +721,27 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
           v1 = *reinterpret_cast<const f32x4*>(vr + 4);
           bias = log2f((float)(ko[j + 1] - ko[j]));
         }
-        if (d0 == 0) sBias[4 * g4 + r] = bias;
+        const int row = 4 * g4 + r, chunk = d0 >> 3;
+        if (d0 == 0) sBias[row] = bias;
+        bf16x8 kh, kl, vh, vl;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) { kf[r][e] = k0[e]; kf[r][e + 4] = k1[e]; vf[r][e] = v0[e]; vf[r][e + 4] = v1[e]; }
-      }
-      bf16* Kh = sK;
-      bf16* Kl = sK + AT_BN * SK;
-      bf16* Vh = sV;
-      bf16* Vl = sV + D * SV;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        bf16x8 h, l;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < 4; ++e) {
           bf16 hh, ll;
-          split_bf16(kf[r][e], hh, ll);
-          h[e] = hh;
-          l[e] = ll;
+          split_bf16(k0[e], hh, ll); kh[e] = hh; kl[e] = ll;
+          split_bf16(k1[e], hh, ll); kh[e + 4] = hh; kl[e + 4] = ll;
+          split_bf16(v0[e], hh, ll); vh[e] = hh; vl[e] = ll;
+          split_bf16(v1[e], hh, ll); vh[e + 4] = hh; vl[e + 4] = ll;
         }
-        *reinterpret_cast<bf16x8*>(&Kh[(4 * g4 + r) * SK + d0]) = h;
-        *reinterpret_cast<bf16x8*>(&Kl[(4 * g4 + r) * SK + d0]) = l;
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        bf16x4 h, l;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          bf16 hh, ll;
-          split_bf16(vf[r][e], hh, ll);
-          h[r] = hh;
-          l[r] = ll;
-        }
-        *reinterpret_cast<bf16x4*>(&Vh[(d0 + e) * SV + 4 * g4]) = h;
-        *reinterpret_cast<bf16x4*>(&Vl[(d0 + e) * SV + 4 * g4]) = l;
+        const int ok_ = row * ROWB + ((chunk ^ (row & 7)) << 4);
+        const int ov_ = row * ROWB + ((chunk ^ (2 * (row & 3))) << 4);
+        *reinterpret_cast<bf16x8*>(sK0 + ok_) = kh;
+        *reinterpret_cast<bf16x8*>(sK1 + ok_) = kl;
+        *reinterpret_cast<bf16x8*>(sV0 + ov_) = vh;
+        *reinterpret_cast<bf16x8*>(sV1 + ov_) = vl;
       }
     }
     __syncthreads();
-    compute(0, AT_BN, true);
+    compute(sK0, sV0, AT_BN, true);
     __syncthreads();
   }
 
@@ -742,7 +763,6 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
     if (lse && half == 0) lse[(size_t)bh * N + orig] = (m_run + log2f(l_tot)) * 0.69314718055994531f;
   }
 }
-
 // ---------------------------------------------------------------- host side
 struct AtPlan {
   int BH, maxt;
@@ -765,8 +785,7 @@ static void launch_attn(const void* q, const void* k, const void* v, const int32
                         const uint8_t* mask, int BH, int N, float sl2, void* out, float* lse, int maxt,
                         hipStream_t st) {
   if constexpr (sizeof(T) == 2) {
-    const size_t lds = (size_t)2 * AT_BN * (D + 8) * 2 + (size_t)2 * D * (AT_BN + 4) * 2 + AT_BN * 4 +
-                       2 * AT_BN * 4 + (size_t)(3 * Ck + 1) * sizeof(int);
+    const size_t lds = (size_t)(3 * Ck + 1) * sizeof(int);  // cluster lists; the tiles are static
     (void)hipFuncSetAttribute((const void*)attn_bf16_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     const int total = round_up(maxt * BH, AT_XCDS);
     hipLaunchKernelGGL((attn_bf16_kernel<D>), dim3(total), dim3(256), lds, st, (const bf16*)q, (const bf16*)k,
