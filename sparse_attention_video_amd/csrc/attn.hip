@@ -410,11 +410,11 @@ __global__ void __launch_bounds__(256) attn_kernel(const T* __restrict__ qp, con
 //  * skipped clusters (pseudo-keys, bf16 hi + lo) run in a second loop.
 //
 // Tile layout: 64 rows of D bf16 (ROWB = 2 D bytes), chunk c (16 bytes) of
-// row r in slot c ^ swz(r):
-//   K: swz(r) = r & 7      -- an A-fragment read touches 8 consecutive rows
-//                            at one chunk: 8 distinct bank quads;
-//   V: swz(r) = 2 (r & 3)  -- a transposing read touches 4 rows x 2 chunks
-//                            per 16 lanes: 8 distinct bank quads.
+// row r in slot c ^ swz(r).  For D = 128 (64 LDS banks, 256 bytes per clock):
+//   K: swz(r) = r & 15     -- 16 lanes of an A-fragment read touch 16
+//                            consecutive rows at one chunk: 16 slots;
+//   V: swz(r) = 4 (r & 3)  -- 32 lanes of a transposing read touch 4 rows x
+//                            4 chunks: 16 slots.
 // One load instruction fills 1 KiB = RPI consecutive rows; lane L writes
 // slot L % CH of row L / CH (CH = chunks per row).
 // ---------------------------------------------------------------------------
@@ -442,6 +442,8 @@ template <int D>
 struct AtTile {
   static constexpr int ROWB = 2 * D, CH = D / 8, RPI = 64 / CH, NI = CH / 4;
   static constexpr int BYTES = AT_BN * ROWB;
+  static __device__ __forceinline__ int swzK(int r) { return r & (CH >= 16 ? 15 : 7); }
+  static __device__ __forceinline__ int swzV(int r) { return 4 * (r & (CH >= 16 ? 3 : 1)); }
 };
 
 template <int D>
@@ -461,7 +463,6 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
   __shared__ __attribute__((aligned(1024))) char sK1[TL::BYTES];
   __shared__ __attribute__((aligned(1024))) char sV0[TL::BYTES];
   __shared__ __attribute__((aligned(1024))) char sV1[TL::BYTES];
-  __shared__ __attribute__((aligned(16))) int sTab[2 * AT_BN];
   __shared__ float sBias[AT_BN];
   __shared__ int sScan[16];
   __shared__ int sInfo[4];
@@ -539,7 +540,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
   // S^T A-fragment: row sub*32 + col, chunk 2 ks + half
   int aK[KS];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) aK[ks] = col * ROWB + (((2 * ks + half) ^ (col & 7)) << 4);
+  for (int ks = 0; ks < KS; ++ks) aK[ks] = col * ROWB + (((2 * ks + half) ^ TL::swzK(col)) << 4);
   // V^T A-fragment by transposing reads: in each 16-lane group (j = lane % 16,
   // group g = lane / 16) lane j points at row kbase + j / 4, dims
   // 32 t + 16 (g & 1) + 4 (j % 4) .. +3; lane j then receives the 4 rows'
@@ -550,42 +551,41 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
 #pragma unroll
     for (int t = 0; t < DT; ++t) {
       const int chunk = 4 * t + 2 * g1 + ((j >> 1) & 1);
-      aV[t] = (4 * half + r4) * ROWB + ((chunk ^ (2 * (r4 & 3))) << 4) + ((j & 1) << 3);
+      aV[t] = (4 * half + r4) * ROWB + ((chunk ^ TL::swzV(r4)) << 4) + ((j & 1) << 3);
     }
   }
   // direct-to-LDS loads: instruction i of wave w fills rows (w NI + i) RPI + L / CH
   const int lq = lane / CH, lslot = lane % CH;
   int chK[NI];
 #pragma unroll
-  for (int i = 0; i < NI; ++i) chK[i] = lslot ^ ((((w * NI + i) * RPI) + lq) & 7);
-  const int chV = lslot ^ (2 * (lq & 3));
+  for (int i = 0; i < NI; ++i) chK[i] = lslot ^ TL::swzK((w * NI + i) * RPI + lq);
+  const int chV = lslot ^ TL::swzV(lq);  // RPI is a multiple of 4
 
-  // ---- source-row table, filled by wave 0 two tiles ahead
+  // ---- source rows: each lane follows the key positions it loads,
+  // kt * 64 + (w NI + i) RPI + lq, with its own cursor over the selected
+  // clusters (positions only grow); positions past the end load row 0, whose
+  // scores are masked
   int tc = 0, tc_base = nsel > 0 ? sSelStart[0] : 0, tc_pre = 0;
   int tc_nxt = nsel > 1 ? sSelPre[1] : 0x7fffffff;
-  auto fill_table = [&](int kt) {
-    const int p = kt * AT_BN + lane;
-    while (p >= tc_nxt) {
-      ++tc;
-      tc_base = sSelStart[tc];
-      tc_pre = tc_nxt;
-      tc_nxt = tc + 1 < nsel ? sSelPre[tc + 1] : 0x7fffffff;
-    }
-    const int src = p < nkeys ? tc_base + (p - tc_pre) : 0;  // rows past the end load row 0, masked later
-    const int rw = lane >> 4, rem = lane & 15;
-    sTab[(kt & 1) * AT_BN + rw * 16 + (rem % RPI) * NI + rem / RPI] = src;
-  };
-  auto issue = [&](int kt, char* dK, char* dV) {
-    const int* tab = sTab + (kt & 1) * AT_BN + w * 16 + lq * NI;
-    int src[NI];
+  auto sources = [&](int kt, uint32_t* rowoff) {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) src[i] = tab[i];
+    for (int i = 0; i < NI; ++i) {
+      const int p = kt * AT_BN + (w * NI + i) * RPI + lq;
+      while (p >= tc_nxt) {
+        ++tc;
+        tc_base = sSelStart[tc];
+        tc_pre = tc_nxt;
+        tc_nxt = tc + 1 < nsel ? sSelPre[tc + 1] : 0x7fffffff;
+      }
+      rowoff[i] = (uint32_t)(p < nkeys ? tc_base + (p - tc_pre) : 0) * (uint32_t)ROWB;
+    }
+  };
+  auto issue = [&](const uint32_t* rowoff, char* dK, char* dV) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int g = w * NI + i;
-      const uint32_t rowoff = (uint32_t)src[i] * (uint32_t)ROWB;
-      load_lds16(kb + rowoff + (chK[i] << 4), dK + g * 1024);
-      load_lds16(vb + rowoff + (chV << 4), dV + g * 1024);
+      load_lds16(kb + rowoff[i] + (chK[i] << 4), dK + g * 1024);
+      load_lds16(vb + rowoff[i] + (chV << 4), dV + g * 1024);
     }
   };
 
@@ -593,7 +593,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
   // take the max on the raw scores (scale > 0) and fold the scale into one FMA
   // per weight; pseudo tiles (hi in buffer 0, lo in buffer 1) add the log2 n_j
   // bias first.
-  auto compute = [&](const char* Kh, const char* Vh, int lim, bool pseudo) {
+  auto compute = [&](const char* Kh, const char* Vh, int lim, bool pseudo, auto&& mid) {
     f32x16 s[2] = {f32x16{}, f32x16{}};
     {
       // fragments of step ks + 1 are read before the products of step ks
@@ -610,6 +610,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
         s[1] = mfma_bf16(fr[ks & 1][1], bq[ks], s[1]);
       }
     }
+    mid();  // straight-line work that overlaps the products in flight
     if (pseudo) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
@@ -621,11 +622,13 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[sub][r] = fmaf(s[sub][r], sl2, sBias[sub * 32 + c_row(r, half)]);
     } else if (lim < AT_BN) {
+      // key index sub*32 + c_row(r, half) >= lim, with the lane's part moved to the right
+      const int lh = lim - 4 * half;
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (sub * 32 + c_row(r, half) >= lim) s[sub][r] = -INFINITY;
+          if (sub * 32 + 8 * (r >> 2) + (r & 3) >= lh) s[sub][r] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -674,25 +677,22 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
   // ---- selected keys: packed 64-key tiles, double buffered, loop unrolled by
   // two so each half reads one fixed buffer
   if (nreal > 0) {
-    if (w == 0) {
-      fill_table(0);
-      if (nreal > 1) fill_table(1);
-    }
-    __syncthreads();
-    issue(0, sK0, sV0);
+    uint32_t ro[NI];
+    sources(0, ro);
+    issue(ro, sK0, sV0);
     // the Q fragments and tile 0 are in: later waits only cover the prefetch
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int kt = 0; kt < nreal; kt += 2) {
-      if (kt + 1 < nreal) issue(kt + 1, sK1, sV1);
-      if (w == 0 && kt + 2 < nreal) fill_table(kt + 2);
-      compute(sK0, sV0, nkeys - kt * AT_BN, false);
+      // the next tile's loads go out while this tile's S^T products run; past
+      // the last tile they fetch row 0 into the idle buffer, which is never read
+      sources(kt + 1, ro);
+      compute(sK0, sV0, nkeys - kt * AT_BN, false, [&] { issue(ro, sK1, sV1); });
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (kt + 1 < nreal) {
-        if (kt + 2 < nreal) issue(kt + 2, sK0, sV0);
-        if (w == 0 && kt + 3 < nreal) fill_table(kt + 3);
-        compute(sK1, sV1, nkeys - (kt + 1) * AT_BN, false);
+        sources(kt + 2, ro);
+        compute(sK1, sV1, nkeys - (kt + 1) * AT_BN, false, [&] { issue(ro, sK0, sV0); });
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
       }
@@ -732,8 +732,8 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
           split_bf16(v0[e], hh, ll); vh[e] = hh; vl[e] = ll;
           split_bf16(v1[e], hh, ll); vh[e + 4] = hh; vl[e + 4] = ll;
         }
-        const int ok_ = row * ROWB + ((chunk ^ (row & 7)) << 4);
-        const int ov_ = row * ROWB + ((chunk ^ (2 * (row & 3))) << 4);
+        const int ok_ = row * ROWB + ((chunk ^ TL::swzK(row)) << 4);
+        const int ov_ = row * ROWB + ((chunk ^ TL::swzV(row)) << 4);
         *reinterpret_cast<bf16x8*>(sK0 + ok_) = kh;
         *reinterpret_cast<bf16x8*>(sK1 + ok_) = kl;
         *reinterpret_cast<bf16x8*>(sV0 + ov_) = vh;
@@ -741,7 +741,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
       }
     }
     __syncthreads();
-    compute(sK0, sV0, AT_BN, true);
+    compute(sK0, sV0, AT_BN, true, [] {});
     __syncthreads();
   }
 
