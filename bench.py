@@ -29,6 +29,16 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "ms per attention layer (cluster+route+sparse attn), 75.6k tok, 25% density; MFMA %"
+
+# HBM bytes of one attention launch on the Wan layer, from rocprofv3
+# FETCH_SIZE / WRITE_SIZE calibrated against a 1 GiB device copy (FETCH x 2.0,
+# WRITE x 1.0); valid only for the attention source it was measured on.
+ATTN_TRAFFIC = {
+    "source_sha256": "af6787ec2763c0922bc7c8de7cfdb0fef4879a3e3261e2b3ea5d1d82b504e6ff",
+    "workload": "wan",
+    "fetch_bytes": 41.27e9,
+    "write_bytes": 0.774e9,
+}
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_F32_TFLOPS = 157.3
 
@@ -74,6 +84,19 @@ def algorithmic_flops(mask, qoff, koff, D):
     pairs_sel = int((qs * sel_keys).sum())
     pairs_comp = int((qs * comp).sum())
     return 4 * D * (pairs_sel + pairs_comp), pairs_sel, pairs_comp
+
+
+def attn_traffic(workload_name, full_layer):
+    """Calibrated HBM bytes per attention launch, or None when the kernel
+    source changed since the counters were taken (or another workload runs)."""
+    import hashlib
+    src = os.path.join(ROOT, "sparse_attention_video_amd", "csrc", "attn.hip")
+    with open(src, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    t = ATTN_TRAFFIC
+    if sha != t["source_sha256"] or workload_name != t["workload"] or not full_layer:
+        return None
+    return t["fetch_bytes"] + t["write_bytes"]
 
 
 def cpu_baseline(w, h0, scale):
@@ -210,8 +233,10 @@ def main():
                                f"{w.iters} cold k-means rounds, density {w.density}",
                    "B": w.B, "H": w.H, "N": w.N, "D": w.D, "Cq": w.Cq, "Ck": w.Ck, "kmeans_iters": w.iters,
                    "density": w.density},
-        "roofline": {"kernel": "attn_kernel (svgear_sparse_attn)", "bound": "mfma", "achieved": round(achieved, 1),
-                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4), "traffic": None,
+        "roofline": {"kernel": "attn_bf16_kernel (svgear_sparse_attn)" if w.dtype == "bf16" else
+                     "attn_kernel (svgear_sparse_attn)", "bound": "mfma", "achieved": round(achieved, 1),
+                     "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": attn_traffic(w.name, not args.heads), "traffic_unit": "HBM bytes per launch",
                      "launch_ms": round(t_attn, 3), "flops_per_launch": flops},
         "stages_ms": stages,
         "realized_density": round(pairs_sel / (BH * float(w.N) ** 2), 4),
