@@ -35,7 +35,14 @@ stabilised by the row maximum M_i of the probe scores (the per-row ranking is
 unchanged by that common factor); the budget is rho * N_k keys per query
 cluster and the block that crosses it is included; ties in ratio break to the
 lower key-cluster index; compensation uses each query token against the exact
-means of the current assignment; no variance term.
+means of the current assignment; no variance term in the plain method.
+
+Variance-corrected compensation (a variant the FrontierCS blog describes in
+its paragraph on the centroid's low guess): a skipped cluster's score is
+raised by strength * sigma^2 / 2 with sigma^2 = (1/d) sum_i q_i^2 Var(k_i),
+the per-coordinate population variance of the cluster's keys.  ``variances``
+and the ``kvar`` / ``strength`` arguments of ``attend`` implement it;
+strength 0 is the plain method.
 """
 from __future__ import annotations
 
@@ -136,6 +143,23 @@ def means(X: np.ndarray, perm: np.ndarray, offsets: np.ndarray) -> np.ndarray:
         lo, hi = int(offsets[c]), int(offsets[c + 1])
         if hi > lo:
             out[c] = X[perm[lo:hi]].mean(axis=0)
+    return out
+
+
+def variances(X: np.ndarray, perm: np.ndarray, offsets: np.ndarray) -> np.ndarray:
+    """Per-coordinate population variance of each cluster's rows, Var(x_i) =
+    mean over members of (x_i - mean_i)^2 (FrontierCS blog, variance
+    correction: one variance per key coordinate; its two-key example, scores
+    0 and 2, has variance 1, i.e. the mean of squared deviations).  An empty
+    cluster's variance is defined as 0."""
+    X = np.asarray(X, F64)
+    C = offsets.shape[0] - 1
+    out = np.zeros((C, X.shape[1]), F64)
+    for c in range(C):
+        lo, hi = int(offsets[c]), int(offsets[c + 1])
+        if hi > lo:
+            rows = X[perm[lo:hi]]
+            out[c] = ((rows - rows.mean(axis=0)) ** 2).mean(axis=0)
     return out
 
 
@@ -241,13 +265,17 @@ def route(qbar, q_offsets, Kp, Vp, kbar, vbar, k_offsets, scale, density):
 # --------------------------------------------------------------------------
 # 5. sparse attention with centroid compensation
 # --------------------------------------------------------------------------
-def attend_rows(q_rows, K, V, k_perm, k_offsets, kbar, vbar, sel_row, scale):
+def attend_rows(q_rows, K, V, k_perm, k_offsets, kbar, vbar, sel_row, scale, kvar=None, strength=0.0):
     """Outputs and log-sum-exp for query rows that share one routing row.
 
     Keys of selected clusters are attended exactly.  Each skipped non-empty
     key cluster j enters as one key k_bar_j with score q.k_bar_j * scale +
     ln n_j and value v_bar_j, i.e. weight n_j e^{q.k_bar_j scale} (FrontierCS
-    blog toy example; SVG-EAR task page walkthrough step 3)."""
+    blog toy example; SVG-EAR task page walkthrough step 3).  With ``kvar``
+    (per-cluster coordinate variances) the score also gains
+    strength * sigma^2 / 2, sigma^2 = scale^2 sum_i q_i^2 kvar_ji, the
+    variance of the query's scores over the cluster under independent
+    coordinates (FrontierCS blog, variance-correction paragraph)."""
     q_rows = np.asarray(q_rows, F64)
     K = np.asarray(K, F64)
     V = np.asarray(V, F64)
@@ -262,7 +290,11 @@ def attend_rows(q_rows, K, V, k_perm, k_offsets, kbar, vbar, sel_row, scale):
     values = [V[exact_idx]]
     if comp:
         comp = np.asarray(comp)
-        logits.append(scale * (q_rows @ kbar[comp].T) + np.log(sizes[comp].astype(F64))[None, :])
+        pseudo = scale * (q_rows @ kbar[comp].T) + np.log(sizes[comp].astype(F64))[None, :]
+        if kvar is not None and strength != 0.0:
+            sigma2 = scale * scale * ((q_rows * q_rows) @ np.asarray(kvar, F64)[comp].T)
+            pseudo = pseudo + strength * 0.5 * sigma2
+        logits.append(pseudo)
         values.append(vbar[comp])
     L = np.concatenate(logits, axis=1)
     Vall = np.concatenate(values, axis=0)
@@ -274,7 +306,8 @@ def attend_rows(q_rows, K, V, k_perm, k_offsets, kbar, vbar, sel_row, scale):
     return out, lse
 
 
-def attend(Q, K, V, q_perm, q_offsets, k_perm, k_offsets, kbar, vbar, mask, scale, rows=None):
+def attend(Q, K, V, q_perm, q_offsets, k_perm, k_offsets, kbar, vbar, mask, scale, rows=None, kvar=None,
+           strength=0.0):
     """O [N, D] and LSE [N] in original token order (SVG2 summary: the output
     is un-permuted back to the original order).
 
@@ -292,7 +325,7 @@ def attend(Q, K, V, q_perm, q_offsets, k_perm, k_offsets, kbar, vbar, mask, scal
             toks = np.asarray([t for t in toks if int(t) in want], dtype=np.int64)
         if toks.size == 0:
             continue
-        o, l = attend_rows(Q[toks], K, V, k_perm, k_offsets, kbar, vbar, mask[i], scale)
+        o, l = attend_rows(Q[toks], K, V, k_perm, k_offsets, kbar, vbar, mask[i], scale, kvar, strength)
         O[toks] = o
         LSE[toks] = l
     return O, LSE

@@ -302,3 +302,103 @@ def test_clusters_of_identical_members_make_compensation_exact(density):
     assert (np.diff(out["ok"]) == 3).all()
     assert out["mask"].sum(axis=1).max() < 20
     np.testing.assert_allclose(out["O"], sdpa64(q, k, v, out["scale"]), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- variance-corrected compensation
+def lse_corrected(q, K, V, lab, mask_row, members, strength):
+    keep = np.flatnonzero(np.isin(lab, members))
+    Ks, Vs, ls = K[keep], V[keep], lab[keep]
+    C = int(lab.max()) + 1
+    perm, off = orc.permute(ls, C)
+    kbar, vbar = orc.means(Ks, perm, off), orc.means(Vs, perm, off)
+    kvar = orc.variances(Ks, perm, off)
+    _, lse = orc.attend_rows(q, Ks, Vs, perm, off, kbar, vbar, np.asarray(mask_row), 1.0, kvar, strength)
+    return float(np.exp(lse[0]))
+
+
+def test_toy_variance_corrected_estimate_matches_printed_value():
+    """FrontierCS blog, variance-correction paragraph: B's scores 0 and 2 have
+    variance 1 and the corrected estimate is about 9.0 (closed form 2 e^{1.5})."""
+    g, q, K, V, lab = toy()
+    p, tol = g["printed"], g["printed_abs_tolerance"]
+    perm, off = orc.permute(lab, 2)
+    var = orc.variances(K, perm, off)
+    assert var[1, 0] == 1.0 and var[0, 0] == 0.0
+    est = lse_corrected(q, K, V, lab, [0, 0], [1], 1.0)
+    assert abs(est - p["variance_corrected_estimate_B"]) < tol
+    assert est == pytest.approx(2.0 * np.exp(1.5), rel=1e-14)
+    # still closer to the true 8.4 (1 + e^2) than the plain 5.4, and above it
+    assert abs(est - (1 + np.e ** 2)) < abs(2 * np.e - (1 + np.e ** 2))
+    # strength scales the raised score: strength 1/2 gives 2 e^{1 + 1/4}
+    assert lse_corrected(q, K, V, lab, [0, 0], [1], 0.5) == pytest.approx(2.0 * np.exp(1.25), rel=1e-14)
+
+
+def test_variance_hand_example_and_empty_cluster():
+    X = np.array([[0.0, 1.0], [2.0, 1.0], [5.0, -3.0], [1.0, 7.0], [3.0, 9.0]])
+    lab = np.array([0, 0, 2, 0, 2])
+    perm, off = orc.permute(lab, 3)
+    var = orc.variances(X, perm, off)
+    # cluster 0: x = 0, 2, 1 (mean 1, deviations -1, 1, 0) and 1, 1, 7 (mean 3, deviations -2, -2, 4)
+    np.testing.assert_allclose(var[0], [2.0 / 3.0, 24.0 / 3.0], rtol=0, atol=1e-15)
+    np.testing.assert_array_equal(var[1], [0.0, 0.0])             # empty
+    np.testing.assert_allclose(var[2], [1.0, 36.0], rtol=0, atol=1e-15)  # 5, 3 and -3, 9
+
+
+def test_variance_term_in_one_dimension_is_the_score_variance():
+    """d = 1: sigma^2 = scale^2 q^2 Var(k) is exactly the variance of the
+    query's scores over the cluster, so the corrected pseudo-score of every
+    skipped cluster is ln n + mean score + strength * Var(scores) / 2."""
+    rng = np.random.default_rng(3)
+    K = rng.normal(size=(12, 1))
+    V = rng.normal(size=(12, 1))
+    lab = np.repeat(np.arange(3), 4)
+    q = rng.normal(size=(1, 1))
+    scale = 0.7
+    perm, off = orc.permute(lab, 3)
+    kbar, vbar, kvar = orc.means(K, perm, off), orc.means(V, perm, off), orc.variances(K, perm, off)
+    mask = np.array([1, 0, 0], np.uint8)
+    for strength in (0.5, 1.0, 1.5):
+        _, lse = orc.attend_rows(q, K, V, perm, off, kbar, vbar, mask, scale, kvar, strength)
+        total = sum(np.exp(scale * q[0, 0] * K[u, 0]) for u in range(4))
+        for j in (1, 2):
+            s = scale * q[0, 0] * K[4 * j:4 * j + 4, 0]
+            total += 4 * np.exp(s.mean() + strength * 0.5 * s.var())
+        assert float(lse[0]) == pytest.approx(np.log(total), rel=1e-13)
+
+
+def test_variance_correction_is_second_order_and_neutral_at_zero():
+    """strength 0 is the plain method bit for bit; clusters of identical keys
+    have no variance; for a tight cluster the corrected weight is much closer
+    to the exact sum of weights than the plain n e^{s_bar} (second order)."""
+    x = small_head(seed=5)
+    q, k, v = x["q"], x["k"], x["v"]
+    D = q.shape[1]
+    sc = 1.0 / np.sqrt(D)
+    _, lk = orc.lloyd(k, x["ck0"], 5)
+    pk, ok = orc.permute(lk, x["ck0"].shape[0])
+    kbar, vbar, kvar = orc.means(k, pk, ok), orc.means(v, pk, ok), orc.variances(k, pk, ok)
+    mask = np.zeros((1, kbar.shape[0]), np.uint8)
+    plain, lse0 = orc.attend_rows(q[:8], k, v, pk, ok, kbar, vbar, mask[0], sc)
+    zero, lsez = orc.attend_rows(q[:8], k, v, pk, ok, kbar, vbar, mask[0], sc, kvar, 0.0)
+    np.testing.assert_array_equal(plain, zero)
+    np.testing.assert_array_equal(lse0, lsez)
+    # identical keys: variance 0, corrected == plain
+    kk = np.repeat(k[:3], 4, axis=0)
+    lab = np.repeat(np.arange(3), 4)
+    p2, o2 = orc.permute(lab, 3)
+    kv = orc.variances(kk, p2, o2)
+    assert not kv.any()
+    # second order: per cluster, exact vs plain vs corrected weights for each query
+    worse = 0
+    for j in range(kbar.shape[0]):
+        lo, hi = int(ok[j]), int(ok[j + 1])
+        if hi - lo < 2:
+            continue
+        s = sc * (q[:8] @ k[pk[lo:hi]].T)
+        exact = np.exp(s).sum(axis=1)
+        sbar = sc * (q[:8] @ kbar[j])
+        plain_w = (hi - lo) * np.exp(sbar)
+        corr_w = (hi - lo) * np.exp(sbar + 0.5 * sc * sc * ((q[:8] ** 2) @ kvar[j]))
+        assert np.all(plain_w <= exact * (1 + 1e-12))          # Jensen: the plain guess is low
+        worse += int(np.sum(np.abs(corr_w - exact) > np.abs(plain_w - exact)))
+    assert worse == 0
