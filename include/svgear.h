@@ -193,6 +193,47 @@ svgear_status svgear_sparse_attn(const void* q_perm, const void* k_perm, const v
                                  void* out, float* lse, void* ws, size_t ws_bytes,
                                  hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Variance-corrected compensation (a variant; FrontierCS blog on SVG-EAR,
+ * the paragraph on the centroid's low guess): the centroid score q.k_bar
+ * under-estimates the average of e^{s} over the cluster, and a second-order
+ * expansion raises it by sigma^2 / 2, sigma^2 = (1/d) sum_i q_i^2 Var(k_i)
+ * with one variance per key coordinate.  A strength factor scales the term.
+ * ---------------------------------------------------------------------- */
+
+/* svgear_centroid_variances -- per-cluster, per-coordinate population
+ * variance of x's rows: Var_c(x_i) = mean over c's rows of (x_i - mean_c,i)^2
+ * (the blog's two-key example, scores 0 and 2, has variance 1: the mean of
+ * the squared deviations).
+ *
+ *   x, perm, offsets  as for svgear_centroids.
+ *   means      [B,H,C,D] float32: the cluster means (svgear_centroids).
+ *   vars       [B,H,C,D] float32 OUT; an empty cluster gets 0.
+ *   ws         at least svgear_centroids_workspace(B, H, N, D, C) bytes.
+ * Deterministic (fixed summation order); asynchronous on stream. */
+svgear_status svgear_centroid_variances(const void* x, svgear_dtype dt, int B, int H, int N, int D, int C,
+                                        const int32_t* perm, const int32_t* offsets, const float* means,
+                                        float* vars, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* svgear_sparse_attn_var -- svgear_sparse_attn with every skipped cluster's
+ * score raised by strength * sigma^2 / 2, sigma^2 = scale^2 sum_i
+ * q_t,i^2 k_vars[j][i] for query token t: the pseudo-key weight becomes
+ * n_j e^{q_t.k_bar_j scale + strength sigma^2 / 2}.  strength = 0 gives
+ * svgear_sparse_attn's result.  Arguments as svgear_sparse_attn, plus
+ *   k_vars     [B,H,Ck,D] float32: per-coordinate key variances
+ *              (svgear_centroid_variances of K).
+ *   strength   >= 0, finite.
+ * bf16 inputs only (SVGEAR_ERR_UNSUPPORTED for float32); the workspace size
+ * is svgear_sparse_attn_workspace's. */
+svgear_status svgear_sparse_attn_var(const void* q_perm, const void* k_perm, const void* v_perm,
+                                     svgear_dtype dt, const int32_t* q_perm_idx,
+                                     const int32_t* q_offsets, int Cq, const int32_t* k_offsets,
+                                     int Ck, const float* k_means, const float* v_means,
+                                     const float* k_vars, float strength,
+                                     const uint8_t* mask, int B, int H, int N, int D, float scale,
+                                     void* out, float* lse, void* ws, size_t ws_bytes,
+                                     hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -446,7 +446,9 @@ struct AtTile {
   static __device__ __forceinline__ int swzV(int r) { return 4 * (r & (CH >= 16 ? 3 : 1)); }
 };
 
-template <int D>
+// VAR: skipped clusters' scores also gain vcoef * sum_i q_i^2 kvars[j][i]
+// (variance-corrected compensation; vcoef in log2 units).
+template <int D, bool VAR = false>
 __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restrict__ qp, const bf16* __restrict__ kp,
                                                            const bf16* __restrict__ vp, const int32_t* __restrict__ qidx,
                                                            const int32_t* __restrict__ qoff,
@@ -456,7 +458,8 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
                                                            const float* __restrict__ vmeans,
                                                            const uint8_t* __restrict__ mask, int N, float sl2,
                                                            bf16* __restrict__ out, float* __restrict__ lse,
-                                                           int maxt, int BHn) {
+                                                           int maxt, int BHn, const float* __restrict__ kvars,
+                                                           float vcoef) {
   using TL = AtTile<D>;
   constexpr int KS = D / 16, DT = D / 32, ROWB = TL::ROWB, CH = TL::CH, RPI = TL::RPI, NI = TL::NI;
   __shared__ __attribute__((aligned(1024))) char sK0[TL::BYTES];
@@ -589,6 +592,9 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
     }
   };
 
+  // variance term sum_i q_i^2 Var_j(k_i) of the current pseudo tile (VAR only)
+  f32x16 svt[2] = {f32x16{}, f32x16{}};
+
   // one tile of keys in LDS: S^T, online softmax, O^T += V^T P^T.  Real tiles
   // take the max on the raw scores (scale > 0) and fold the scale into one FMA
   // per weight; pseudo tiles (hi in buffer 0, lo in buffer 1) add the log2 n_j
@@ -621,6 +627,12 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[sub][r] = fmaf(s[sub][r], sl2, sBias[sub * 32 + c_row(r, half)]);
+      if constexpr (VAR) {
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) s[sub][r] = fmaf(svt[sub][r], vcoef, s[sub][r]);
+      }
     } else if (lim < AT_BN) {
       // key index sub*32 + c_row(r, half) >= lim, with the lane's part moved to the right
       const int lh = lim - 4 * half;
@@ -704,7 +716,44 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
   constexpr int NUNIT = (AT_BN / 4) * (D / 8);
   const bool has_unit = tid < NUNIT;
   const int g4 = tid & 15, d0 = (tid >> 4) * 8;
+  bf16x8 q2[VAR ? KS : 1];
+  if constexpr (VAR) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) q2[ks][e] = (bf16)((float)bq[ks][e] * (float)bq[ks][e]);
+  }
   for (int pt = 0; pt < npseudo; ++pt) {
+    if constexpr (VAR) {
+      // the tile's key variances (bf16) through sK1 in the K layout, then
+      // svt = Var_j . q^2 by the same products as S^T
+      if (has_unit) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int c = pt * AT_BN + 4 * g4 + r;
+          f32x4 a0 = {}, a1 = {};
+          if (c < ncomp) {
+            const float* vr = kvars + ((size_t)bh * Ck + sComp[c]) * D + d0;
+            a0 = *reinterpret_cast<const f32x4*>(vr);
+            a1 = *reinterpret_cast<const f32x4*>(vr + 4);
+          }
+          bf16x8 h;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) { h[e] = (bf16)a0[e]; h[e + 4] = (bf16)a1[e]; }
+          const int row = 4 * g4 + r;
+          *reinterpret_cast<bf16x8*>(sK1 + row * ROWB + (((d0 >> 3) ^ TL::swzK(row)) << 4)) = h;
+        }
+      }
+      __syncthreads();
+      svt[0] = f32x16{};
+      svt[1] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub)
+          svt[sub] = mfma_bf16(*reinterpret_cast<const bf16x8*>(sK1 + aK[ks] + sub * 32 * ROWB), q2[ks], svt[sub]);
+      __syncthreads();
+    }
     if (has_unit) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -783,14 +832,26 @@ template <typename T, int D>
 static void launch_attn(const void* q, const void* k, const void* v, const int32_t* qidx, const int32_t* qoff,
                         const int32_t* ts, int Cq, const int32_t* koff, int Ck, const float* km, const float* vm,
                         const uint8_t* mask, int BH, int N, float sl2, void* out, float* lse, int maxt,
-                        hipStream_t st) {
+                        const float* kvars, float vcoef, hipStream_t st) {
   if constexpr (sizeof(T) == 2) {
     const size_t lds = (size_t)(3 * Ck + 1) * sizeof(int);  // cluster lists; the tiles are static
-    (void)hipFuncSetAttribute((const void*)attn_bf16_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     const int total = round_up(maxt * BH, AT_XCDS);
-    hipLaunchKernelGGL((attn_bf16_kernel<D>), dim3(total), dim3(256), lds, st, (const bf16*)q, (const bf16*)k,
-                       (const bf16*)v, qidx, qoff, ts, Cq, koff, Ck, km, vm, mask, N, sl2, (bf16*)out, lse, maxt, BH);
+    if (kvars) {
+      (void)hipFuncSetAttribute((const void*)attn_bf16_kernel<D, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)lds);
+      hipLaunchKernelGGL((attn_bf16_kernel<D, true>), dim3(total), dim3(256), lds, st, (const bf16*)q,
+                         (const bf16*)k, (const bf16*)v, qidx, qoff, ts, Cq, koff, Ck, km, vm, mask, N, sl2,
+                         (bf16*)out, lse, maxt, BH, kvars, vcoef);
+    } else {
+      (void)hipFuncSetAttribute((const void*)attn_bf16_kernel<D, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)lds);
+      hipLaunchKernelGGL((attn_bf16_kernel<D, false>), dim3(total), dim3(256), lds, st, (const bf16*)q,
+                         (const bf16*)k, (const bf16*)v, qidx, qoff, ts, Cq, koff, Ck, km, vm, mask, N, sl2,
+                         (bf16*)out, lse, maxt, BH, (const float*)nullptr, 0.f);
+    }
   } else {
+    (void)kvars;
+    (void)vcoef;
     using L = AttnLds<T, D>;
     const size_t lds = L::fixed + (size_t)(3 * Ck + 1) * sizeof(int);
     (void)hipFuncSetAttribute((const void*)attn_kernel<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -810,12 +871,12 @@ extern "C" size_t svgear_sparse_attn_workspace(int B, int H, int N, int D, int C
   return at_plan(B, H, N, Cq).total;
 }
 
-extern "C" svgear_status svgear_sparse_attn(const void* q_perm, const void* k_perm, const void* v_perm,
-                                            svgear_dtype dt, const int32_t* q_perm_idx, const int32_t* q_offsets,
-                                            int Cq, const int32_t* k_offsets, int Ck, const float* k_means,
-                                            const float* v_means, const uint8_t* mask, int B, int H, int N, int D,
-                                            float scale, void* out, float* lse, void* ws, size_t ws_bytes,
-                                            hipStream_t stream) {
+static svgear_status sparse_attn_impl(const void* q_perm, const void* k_perm, const void* v_perm, svgear_dtype dt,
+                                      const int32_t* q_perm_idx, const int32_t* q_offsets, int Cq,
+                                      const int32_t* k_offsets, int Ck, const float* k_means, const float* v_means,
+                                      const float* k_vars, float strength, const uint8_t* mask, int B, int H, int N,
+                                      int D, float scale, void* out, float* lse, void* ws, size_t ws_bytes,
+                                      hipStream_t stream) {
   svgear_status st = check_common("attn", dt, B, H, N, D);
   if (st != SVGEAR_OK) return st;
   if (Cq < 1 || Cq > N || Cq > SVGEAR_MAX_CLUSTERS || Ck < 1 || Ck > N || Ck > SVGEAR_MAX_CLUSTERS)
@@ -831,21 +892,48 @@ extern "C" svgear_status svgear_sparse_attn(const void* q_perm, const void* k_pe
   int32_t* ts = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + p.off_ts);
   const int BH = B * H;
   const float sl2 = scale * 1.4426950408889634f;
+  // variance term in log2 units: strength * sigma^2 / 2 * log2(e), sigma^2 = scale^2 sum q_i^2 Var(k_i)
+  const float vcoef = 0.5f * strength * scale * scale * 1.4426950408889634f;
   hipLaunchKernelGGL(chunk_list_kernel, dim3(BH), dim3(1024), 0, stream, q_offsets, Cq, AT_BM, ts);
   if (dt == SVGEAR_BF16) {
     if (D == 128)
       launch_attn<bf16, 128>(q_perm, k_perm, v_perm, q_perm_idx, q_offsets, ts, Cq, k_offsets, Ck, k_means, v_means,
-                             mask, BH, N, sl2, out, lse, p.maxt, stream);
+                             mask, BH, N, sl2, out, lse, p.maxt, k_vars, vcoef, stream);
     else
       launch_attn<bf16, 64>(q_perm, k_perm, v_perm, q_perm_idx, q_offsets, ts, Cq, k_offsets, Ck, k_means, v_means,
-                            mask, BH, N, sl2, out, lse, p.maxt, stream);
+                            mask, BH, N, sl2, out, lse, p.maxt, k_vars, vcoef, stream);
   } else {
     if (D == 128)
       launch_attn<float, 128>(q_perm, k_perm, v_perm, q_perm_idx, q_offsets, ts, Cq, k_offsets, Ck, k_means, v_means,
-                              mask, BH, N, sl2, out, lse, p.maxt, stream);
+                              mask, BH, N, sl2, out, lse, p.maxt, k_vars, vcoef, stream);
     else
       launch_attn<float, 64>(q_perm, k_perm, v_perm, q_perm_idx, q_offsets, ts, Cq, k_offsets, Ck, k_means, v_means,
-                             mask, BH, N, sl2, out, lse, p.maxt, stream);
+                             mask, BH, N, sl2, out, lse, p.maxt, k_vars, vcoef, stream);
   }
   return check_launch("svgear_sparse_attn");
+}
+
+extern "C" svgear_status svgear_sparse_attn(const void* q_perm, const void* k_perm, const void* v_perm,
+                                            svgear_dtype dt, const int32_t* q_perm_idx, const int32_t* q_offsets,
+                                            int Cq, const int32_t* k_offsets, int Ck, const float* k_means,
+                                            const float* v_means, const uint8_t* mask, int B, int H, int N, int D,
+                                            float scale, void* out, float* lse, void* ws, size_t ws_bytes,
+                                            hipStream_t stream) {
+  return sparse_attn_impl(q_perm, k_perm, v_perm, dt, q_perm_idx, q_offsets, Cq, k_offsets, Ck, k_means, v_means,
+                          nullptr, 0.f, mask, B, H, N, D, scale, out, lse, ws, ws_bytes, stream);
+}
+
+extern "C" svgear_status svgear_sparse_attn_var(const void* q_perm, const void* k_perm, const void* v_perm,
+                                                svgear_dtype dt, const int32_t* q_perm_idx,
+                                                const int32_t* q_offsets, int Cq, const int32_t* k_offsets, int Ck,
+                                                const float* k_means, const float* v_means, const float* k_vars,
+                                                float strength, const uint8_t* mask, int B, int H, int N, int D,
+                                                float scale, void* out, float* lse, void* ws, size_t ws_bytes,
+                                                hipStream_t stream) {
+  if (dt != SVGEAR_BF16) return fail(SVGEAR_ERR_UNSUPPORTED, "attn_var: bf16 inputs only");
+  if (!k_vars) return fail(SVGEAR_ERR_INVALID_ARG, "attn_var: null pointer");
+  if (!(strength >= 0.f) || !(strength < INFINITY))
+    return fail(SVGEAR_ERR_INVALID_ARG, "attn_var: strength must be >= 0 and finite");
+  return sparse_attn_impl(q_perm, k_perm, v_perm, dt, q_perm_idx, q_offsets, Cq, k_offsets, Ck, k_means, v_means,
+                          k_vars, strength, mask, B, H, N, D, scale, out, lse, ws, ws_bytes, stream);
 }

@@ -535,14 +535,15 @@ __global__ void __launch_bounds__(256) km_scatter_kernel(const int32_t* __restri
 // segment sums over the permuted order: chunk k of cluster c sums rows
 // [offsets[c] + k' * rows, ...) of x[perm[.]] (k' = k - chunk_start[c]),
 // optionally writing the permuted copy.  Fixed row-to-lane mapping and a
-// fixed reduction order keep the sums deterministic.
+// fixed reduction order keep the sums deterministic.  SQ: sums of squared
+// deviations from the cluster means `center` instead (variances).
 // --------------------------------------------------------------------------
-template <typename T, int D>
+template <typename T, int D, bool SQ = false>
 __global__ void __launch_bounds__(256) km_partial_kernel(const T* __restrict__ x, const int32_t* __restrict__ perm,
                                                          const int32_t* __restrict__ offsets,
                                                          const int32_t* __restrict__ chunk_start, int N, int C,
                                                          int rows, int maxch, float* __restrict__ partial,
-                                                         T* __restrict__ x_perm) {
+                                                         T* __restrict__ x_perm, const float* __restrict__ center = nullptr) {
   constexpr int EPL = 16 / sizeof(T);     // elements per lane (one 16-byte load)
   constexpr int LPR = D / EPL;            // lanes per row
   constexpr int RPI = 256 / LPR;          // rows per iteration
@@ -561,9 +562,20 @@ __global__ void __launch_bounds__(256) km_partial_kernel(const T* __restrict__ x
   const T* xb = x + (size_t)bh * N * D;
   const int32_t* pb = perm + (size_t)bh * N;
   T* xpb = x_perm ? x_perm + (size_t)bh * N * D : nullptr;
-  float acc[EPL];
+  float acc[EPL], mu[EPL];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  for (int e = 0; e < EPL; ++e) {
+    acc[e] = 0.f;
+    mu[e] = SQ ? center[((size_t)bh * C + c) * D + e0 + e] : 0.f;
+  }
+  auto add = [&](float v, int e) {
+    if constexpr (SQ) {
+      const float dv = v - mu[e];
+      acc[e] = fmaf(dv, dv, acc[e]);
+    } else {
+      acc[e] += v;
+    }
+  };
   int p = r0 + g;
   for (; p + 3 * RPI < r1; p += 4 * RPI) {
     int src[4];
@@ -577,7 +589,7 @@ __global__ void __launch_bounds__(256) km_partial_kernel(const T* __restrict__ x
       if (xpb) st16(xpb + (size_t)(p + k * RPI) * D + e0, v[k]);
       const T* tv = reinterpret_cast<const T*>(&v[k]);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] += to_f32(tv[e]);
+      for (int e = 0; e < EPL; ++e) add(to_f32(tv[e]), e);
     }
   }
   for (; p < r1; p += RPI) {
@@ -586,7 +598,7 @@ __global__ void __launch_bounds__(256) km_partial_kernel(const T* __restrict__ x
     if (xpb) st16(xpb + (size_t)p * D + e0, v);
     const T* tv = reinterpret_cast<const T*>(&v);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] += to_f32(tv[e]);
+    for (int e = 0; e < EPL; ++e) add(to_f32(tv[e]), e);
   }
 #pragma unroll
   for (int e = 0; e < EPL; ++e) red[g * D + e0 + e] = acc[e];
@@ -665,7 +677,14 @@ template <typename T, int D>
 static void launch_partial(const void* x, const int32_t* perm, const int32_t* offsets, const int32_t* cs, int BH,
                            int N, int C, int maxch, float* partial, void* x_perm, hipStream_t st) {
   hipLaunchKernelGGL((km_partial_kernel<T, D>), dim3(maxch, BH), dim3(256), 0, st, (const T*)x, perm, offsets, cs, N,
-                     C, MEAN_ROWS, maxch, partial, (T*)x_perm);
+                     C, MEAN_ROWS, maxch, partial, (T*)x_perm, nullptr);
+}
+
+template <typename T, int D>
+static void launch_partial_sq(const void* x, const int32_t* perm, const int32_t* offsets, const int32_t* cs, int BH,
+                              int N, int C, int maxch, float* partial, const float* means, hipStream_t st) {
+  hipLaunchKernelGGL((km_partial_kernel<T, D, true>), dim3(maxch, BH), dim3(256), 0, st, (const T*)x, perm, offsets,
+                     cs, N, C, MEAN_ROWS, maxch, partial, (T*)nullptr, means);
 }
 
 template <typename T, int D>
@@ -759,4 +778,33 @@ extern "C" svgear_status svgear_centroids(const void* x, svgear_dtype dt, int B,
     hipLaunchKernelGGL(km_finalize_kernel, dim3(cdiv(C * D, 256), BH), dim3(256), 0, stream, partial, offsets, cs, C,
                        D, p.maxch, means, 0);
   return check_launch("svgear_centroids");
+}
+
+extern "C" svgear_status svgear_centroid_variances(const void* x, svgear_dtype dt, int B, int H, int N, int D, int C,
+                                                   const int32_t* perm, const int32_t* offsets, const float* means,
+                                                   float* vars, void* ws, size_t ws_bytes, hipStream_t stream) {
+  svgear_status st = check_common("centroid_variances", dt, B, H, N, D);
+  if (st != SVGEAR_OK) return st;
+  if (C < 1 || C > N || C > SVGEAR_MAX_CLUSTERS)
+    return fail(SVGEAR_ERR_INVALID_ARG, "centroid_variances: C=%d must be in [1, min(N=%d, %d)]", C, N,
+                SVGEAR_MAX_CLUSTERS);
+  if (!x || !perm || !offsets || !means || !vars) return fail(SVGEAR_ERR_INVALID_ARG, "centroid_variances: null pointer");
+  MeanPlan p = mean_plan(B, H, N, D, C);
+  st = check_ws("centroid_variances", ws, ws_bytes, p.total);
+  if (st != SVGEAR_OK) return st;
+  char* w = static_cast<char*>(ws);
+  int32_t* cs = reinterpret_cast<int32_t*>(w + p.off_cs);
+  float* partial = reinterpret_cast<float*>(w + p.off_partial);
+  const int BH = B * H;
+  hipLaunchKernelGGL(chunk_list_kernel, dim3(BH), dim3(1024), 0, stream, offsets, C, MEAN_ROWS, cs);
+  if (dt == SVGEAR_BF16) {
+    if (D == 128) launch_partial_sq<bf16, 128>(x, perm, offsets, cs, BH, N, C, p.maxch, partial, means, stream);
+    else launch_partial_sq<bf16, 64>(x, perm, offsets, cs, BH, N, C, p.maxch, partial, means, stream);
+  } else {
+    if (D == 128) launch_partial_sq<float, 128>(x, perm, offsets, cs, BH, N, C, p.maxch, partial, means, stream);
+    else launch_partial_sq<float, 64>(x, perm, offsets, cs, BH, N, C, p.maxch, partial, means, stream);
+  }
+  hipLaunchKernelGGL(km_finalize_kernel, dim3(cdiv(C * D, 256), BH), dim3(256), 0, stream, partial, offsets, cs, C, D,
+                     p.maxch, vars, 0);
+  return check_launch("svgear_centroid_variances");
 }

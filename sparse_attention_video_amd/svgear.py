@@ -26,6 +26,7 @@ EXPORTS = (
     "svgear_centroids_workspace", "svgear_centroids",
     "svgear_route_workspace", "svgear_route",
     "svgear_sparse_attn_workspace", "svgear_sparse_attn",
+    "svgear_centroid_variances", "svgear_sparse_attn_var",
 )
 
 _lib = None
@@ -64,6 +65,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.svgear_sparse_attn_workspace.restype = Z
     lib.svgear_sparse_attn.argtypes = [P, P, P, I, P, P, I, P, I, P, P, P, I, I, I, I, F, P, P, P, Z, P]
     lib.svgear_sparse_attn.restype = I
+    lib.svgear_centroid_variances.argtypes = [P, I, I, I, I, I, I, P, P, P, P, P, Z, P]
+    lib.svgear_centroid_variances.restype = I
+    lib.svgear_sparse_attn_var.argtypes = [P, P, P, I, P, P, I, P, I, P, P, P, F, P, I, I, I, I, F, P, P, P, Z, P]
+    lib.svgear_sparse_attn_var.restype = I
     _lib = lib
     return lib
 
@@ -186,9 +191,27 @@ def route(q_means, q_offsets, k_perm, v_perm, k_means, v_means, k_offsets, scale
     return (scores if want_scores else None), mask
 
 
+def centroid_variances(x: torch.Tensor, perm: torch.Tensor, offsets: torch.Tensor, means: torch.Tensor, vars=None,
+                       ws=None):
+    """Per-cluster, per-coordinate population variances [B,H,C,D] fp32."""
+    dev = _dev(x, perm, offsets, means)
+    B, H, N, D = x.shape
+    C = offsets.shape[2] - 1
+    vars = vars if vars is not None else torch.empty((B, H, C, D), dtype=torch.float32, device=dev)
+    lib = load()
+    need = lib.svgear_centroids_workspace(B, H, N, D, C)
+    ws = ws if ws is not None else _workspace(need, dev)
+    _check("svgear_centroid_variances",
+           lib.svgear_centroid_variances(_ptr(x), _dtype(x), B, H, N, D, C, _ptr(perm), _ptr(offsets), _ptr(means),
+                                         _ptr(vars), _ptr(ws), ws.numel(), _stream(dev)))
+    return vars
+
+
 def sparse_attn(q_perm, k_perm, v_perm, q_perm_idx, q_offsets, k_offsets, k_means, v_means, mask, scale: float,
-                want_lse: bool = False, out=None, lse=None, ws=None):
-    """Returns (out [B,H,N,D] in original token order, lse [B,H,N] fp32 or None)."""
+                want_lse: bool = False, out=None, lse=None, ws=None, k_vars=None, strength: float = 0.0):
+    """Returns (out [B,H,N,D] in original token order, lse [B,H,N] fp32 or None).
+    With ``k_vars`` the skipped clusters' scores gain strength * sigma^2 / 2
+    (variance-corrected compensation, bf16 only)."""
     dev = _dev(q_perm, k_perm, v_perm, q_perm_idx, q_offsets, k_offsets, k_means, v_means, mask)
     B, H, N, D = q_perm.shape
     Cq, Ck = q_offsets.shape[2] - 1, k_offsets.shape[2] - 1
@@ -198,11 +221,20 @@ def sparse_attn(q_perm, k_perm, v_perm, q_perm_idx, q_offsets, k_offsets, k_mean
     lib = load()
     need = lib.svgear_sparse_attn_workspace(B, H, N, D, Cq, Ck)
     ws = ws if ws is not None else _workspace(need, dev)
-    _check("svgear_sparse_attn",
-           lib.svgear_sparse_attn(_ptr(q_perm), _ptr(k_perm), _ptr(v_perm), _dtype(q_perm), _ptr(q_perm_idx),
-                                  _ptr(q_offsets), Cq, _ptr(k_offsets), Ck, _ptr(k_means), _ptr(v_means), _ptr(mask),
-                                  B, H, N, D, float(scale), _ptr(out), _ptr(lse if want_lse else None), _ptr(ws),
-                                  ws.numel(), _stream(dev)))
+    if k_vars is None:
+        _check("svgear_sparse_attn",
+               lib.svgear_sparse_attn(_ptr(q_perm), _ptr(k_perm), _ptr(v_perm), _dtype(q_perm), _ptr(q_perm_idx),
+                                      _ptr(q_offsets), Cq, _ptr(k_offsets), Ck, _ptr(k_means), _ptr(v_means),
+                                      _ptr(mask), B, H, N, D, float(scale), _ptr(out),
+                                      _ptr(lse if want_lse else None), _ptr(ws), ws.numel(), _stream(dev)))
+    else:
+        _dev(k_vars)
+        _check("svgear_sparse_attn_var",
+               lib.svgear_sparse_attn_var(_ptr(q_perm), _ptr(k_perm), _ptr(v_perm), _dtype(q_perm),
+                                          _ptr(q_perm_idx), _ptr(q_offsets), Cq, _ptr(k_offsets), Ck,
+                                          _ptr(k_means), _ptr(v_means), _ptr(k_vars), float(strength), _ptr(mask),
+                                          B, H, N, D, float(scale), _ptr(out), _ptr(lse if want_lse else None),
+                                          _ptr(ws), ws.numel(), _stream(dev)))
     return out, (lse if want_lse else None)
 
 

@@ -28,7 +28,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared()
-    assert len(names) == 10
+    assert len(names) == 12
     for n in names:
         assert hasattr(lib, n), n
     from sparse_attention_video_amd import svgear
@@ -83,6 +83,16 @@ def test_route_and_attn_validation(lib):
     assert lib.svgear_sparse_attn(F, F, F, 0, F, F, 4, F, 8, F, F, F, 1, 1, 100, 64, ctypes.c_float(0.125),
                                   F, None, None, 0, None) == 3             # no workspace
     assert lib.svgear_centroids(F, 1, 1, 1, 100, 64, 200, F, F, F, F, None, 0, None) == 1
+    # variance variants: bf16 only, strength >= 0, variance table required
+    V = lambda dt, kv, strength: lib.svgear_sparse_attn_var(F, F, F, dt, F, F, 4, F, 8, F, F, kv,
+                                                             ctypes.c_float(strength), F, 1, 1, 100, 64,
+                                                             ctypes.c_float(0.125), F, None, None, 0, None)
+    assert V(1, F, 1.0) == 2                 # float32: unsupported
+    assert V(0, None, 1.0) == 1              # no variances
+    assert V(0, F, -0.5) == 1                # negative strength
+    assert V(0, F, 1.0) == 3                 # valid so far, no workspace
+    assert lib.svgear_centroid_variances(F, 0, 1, 1, 100, 64, 4, F, F, None, F, None, 0, None) == 1
+    assert lib.svgear_centroid_variances(F, 0, 1, 1, 100, 64, 4, F, F, F, F, None, 0, None) == 3
 
 
 def test_fault_injection_returns_injected_without_work():

@@ -369,3 +369,19 @@ def test_full_sequence_warm_step(sv):
         ref[f"p{which}"], ref[f"o{which}"] = orc.permute(lab, C)
         dev1[f"c{which}0"] = cq if which == "q" else ck
         check_kmeans_round(sv, w, h, dev1, x1, ref, which, w.iters)
+
+
+def test_full_attention_variance_corrected(sv):
+    """The variance-corrected variant at the Wan layer size (strength 1)."""
+    w, h, dev, x, L, cq, ck, ref = full_case(sv, "wan")
+    t = teacher_forced_device(w, h, dev, x, L, ref)
+    b, hh = bh_index(w, h)
+    kvar_h = orc.variances(x["k"], ref["pk"], ref["ok"])
+    kv = forced(torch.zeros((w.B, w.H, w.Ck, w.D), dtype=torch.float32, device="cuda"), w, h, f32(kvar_h))
+    mask = forced(L.mask, w, h, torch.from_numpy(ref["mask"].astype(np.uint8)).cuda())
+    out, lse = sv.sparse_attn(t["qp"], t["kp"], t["vp"], t["pq"], t["oq"], t["ok"], t["km"], t["vm"], mask,
+                              ref["scale"], want_lse=True, k_vars=kv, strength=1.0)
+    rows = ref["rows"]
+    O, LSE = orc.attend(x["q"], x["k"], x["v"], ref["pq"], ref["oq"], ref["pk"], ref["ok"], ref["kbar"],
+                        ref["vbar"], ref["mask"], ref["scale"], rows=rows, kvar=kvar_h, strength=1.0)
+    check_attention_rows(w, h, out, lse, O, LSE, rows)

@@ -307,3 +307,56 @@ def test_layer_is_deterministic(sv):
         res.append((out.clone(), L.scores.clone(), cq.clone(), ck.clone()))
     for a, b in zip(res[0], res[1]):
         assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------ variance-corrected compensation
+@pytest.mark.parametrize("name", list(CASES))
+def test_centroid_variances(sv, name, ref_cache):
+    """Per-cluster coordinate variances from the oracle's permutation and
+    means; bound: (n + 4) u relative (fp32 sums of squares of fp32
+    deviations) plus a tiny absolute floor."""
+    w, x, outs, sc = oracle_layer(name, ref_cache)
+    BH = w.B * w.H
+    for key, p, o, mkey in (("k", "pk", "ok", "kbar"), ("q", "pq", "oq", "qbar")):
+        perm = np.stack([oo[p] for oo in outs])
+        off = np.stack([oo[o] for oo in outs])
+        mu = np.stack([oo[mkey] for oo in outs]).astype(np.float32)
+        var = sv.centroid_variances(to_dev(reshape4(x[key], w), w.dtype), i32(reshape4(perm, w)),
+                                    i32(reshape4(off, w)), f32(reshape4(mu, w)))
+        var = host(var).reshape(BH, off.shape[1] - 1, w.D)
+        for h in range(BH):
+            ref = orc.variances(x[key][h], perm[h], off[h])
+            n = np.diff(off[h]).astype(np.float64)[:, None]
+            tol = (n + 4) * 2.0 ** -24 * ref + 1e-12 * max(1.0, float(ref.max()))
+            assert np.all(np.abs(var[h] - ref) <= tol), float((np.abs(var[h] - ref) - tol).max())
+
+
+@pytest.mark.parametrize("name", ["bf16-d128", "bf16-d64"])
+@pytest.mark.parametrize("strength", [0.5, 1.0, 1.5])
+def test_sparse_attn_variance_corrected(sv, name, strength, ref_cache):
+    w, x, outs, sc = oracle_layer(name, ref_cache)
+    BH = w.B * w.H
+    m = np.stack([o["mask"] for o in outs])
+    dev, m = attn_inputs(w, x, outs, m)
+    kvar = np.stack([orc.variances(x["k"][h], outs[h]["pk"], outs[h]["ok"]) for h in range(BH)])
+    out, lse = sv.sparse_attn(*dev, sc, want_lse=True, k_vars=f32(reshape4(kvar, w)), strength=strength)
+    out = host(out).reshape(BH, w.N, w.D)
+    lse = host(lse).reshape(BH, w.N)
+    amax, amean = ATOL[w.dtype]
+    for h in range(BH):
+        o = outs[h]
+        O, L = orc.attend(x["q"][h], x["k"][h], x["v"][h], o["pq"], o["oq"], o["pk"], o["ok"], o["kbar"], o["vbar"],
+                          m[h], sc, kvar=kvar[h], strength=strength)
+        err = np.abs(out[h] - O)
+        assert err.max() <= amax and err.mean() <= amean, (err.max(), err.mean())
+        assert np.abs(lse[h] - L).max() <= 1e-2
+
+
+def test_sparse_attn_variance_strength_zero_is_plain(sv, ref_cache):
+    w, x, outs, sc = oracle_layer("bf16-d128", ref_cache)
+    BH = w.B * w.H
+    dev, _ = attn_inputs(w, x, outs)
+    kvar = np.stack([orc.variances(x["k"][h], outs[h]["pk"], outs[h]["ok"]) for h in range(BH)])
+    plain, _ = sv.sparse_attn(*dev, sc)
+    zero, _ = sv.sparse_attn(*dev, sc, k_vars=f32(reshape4(kvar, w)), strength=0.0)
+    assert torch.equal(plain, zero)
