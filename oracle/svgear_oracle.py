@@ -43,6 +43,13 @@ raised by strength * sigma^2 / 2 with sigma^2 = (1/d) sum_i q_i^2 Var(k_i),
 the per-coordinate population variance of the cluster's keys.  ``variances``
 and the ``kvar`` / ``strength`` arguments of ``attend`` implement it;
 strength 0 is the plain method.
+
+Top-p budget (SVG2 summary, "Centroid-Based Top-p Selection"; FrontierCS
+blog, budget paragraph): ``topp_probs`` estimates each block's share P' of
+the attention mass from the centroids, ``topp_select`` is SVG2's own router
+(clusters by P' until the shares taken reach p) and ``route_topp`` with
+error_ranked=True gives each query cluster that selection's keys as its
+budget and spends them by error per pair instead of a fixed density.
 """
 from __future__ import annotations
 
@@ -260,6 +267,101 @@ def route(qbar, q_offsets, Kp, Vp, kbar, vbar, k_offsets, scale, density):
     e, _ = probe_errors(qbar, Kp, Vp, kbar, vbar, k_offsets, scale, q_nonempty=q_sizes > 0)
     r = ratios(e, q_sizes, k_sizes)
     return r, select(r, q_sizes, k_sizes, density, Kp.shape[0])
+
+
+# --------------------------------------------------------------------------
+# 4b. the SVG2 top-p budget and the score-ranked router
+# --------------------------------------------------------------------------
+def topp_probs(qbar, kbar, k_sizes, scale) -> np.ndarray:
+    """Estimated attention mass P'[i, j] of key cluster j for query cluster i,
+    as float32 (SVG2 summary, "Centroid-Based Top-p Selection").
+
+    The centroid score is S_ij = scale * q_bar_i . k_bar_j, and
+    P'_ij = |K_j| e^{S_ij} / sum_l |K_l| e^{S_il}: each key of cluster j is
+    taken to score S_ij, so the numerator estimates the cluster's total weight
+    and each row sums to 1.  Empty key clusters (|K_j| = 0) get 0 and do not
+    take part in the row maximum used to keep the exponentials finite.  The
+    selection compares these float32 values."""
+    k_sizes = np.asarray(k_sizes)
+    S = scale * (np.asarray(qbar, F64) @ np.asarray(kbar, F64).T)
+    live = k_sizes > 0
+    P = np.zeros(S.shape, F64)
+    for i in range(S.shape[0]):
+        m = S[i, live].max()
+        w = np.where(live, k_sizes * np.exp(np.where(live, S[i] - m, 0.0)), 0.0)
+        P[i] = w / w.sum()
+    return P.astype(np.float32)
+
+
+def topp_select_row(P_row: np.ndarray, k_sizes: np.ndarray, p: float) -> np.ndarray:
+    """Top-p selection of one query cluster's key clusters (SVG2 summary,
+    "Centroid-Based Top-p Selection", steps 1-3).
+
+    Order the non-empty key clusters by (P' descending, index ascending) and
+    take them while the P' already taken, summed in that order in float64,
+    is below p; the cluster whose P' reaches p is included.  p >= 1 takes
+    every non-empty cluster (a sum of rounded terms may touch 1 early)."""
+    k_sizes = np.asarray(k_sizes)
+    cand = [j for j in range(P_row.shape[0]) if k_sizes[j] > 0]
+    cand.sort(key=lambda j: (-float(P_row[j]), j))
+    sel = np.zeros(P_row.shape[0], dtype=np.uint8)
+    p = float(np.float32(p))
+    cum = 0.0
+    for j in cand:
+        if p < 1.0 and cum >= p:
+            break
+        sel[j] = 1
+        cum += float(P_row[j])
+    return sel
+
+
+def topp_select(P: np.ndarray, q_sizes, k_sizes, p: float) -> np.ndarray:
+    """The SVG2 router's mask [Cq, Ck]; rows of empty query clusters are zero."""
+    mask = np.zeros(P.shape, dtype=np.uint8)
+    for i in range(P.shape[0]):
+        if q_sizes[i] > 0:
+            mask[i] = topp_select_row(P[i], k_sizes, p)
+    return mask
+
+
+def topp_budgets(topp_mask: np.ndarray, k_sizes) -> np.ndarray:
+    """Key budget per query cluster from a top-p selection (FrontierCS blog
+    on SVG-EAR, the budget paragraph: the token pairs in the blocks holding a
+    fraction p of the estimated weight).  Row i's pairs are |Q_i| times its
+    selected keys, so the budget is kept in keys: int64 [Cq]."""
+    return (np.asarray(topp_mask, np.int64) * np.asarray(k_sizes, np.int64)[None, :]).sum(axis=1)
+
+
+def select_budgets(r: np.ndarray, q_sizes, k_sizes, budgets) -> np.ndarray:
+    """Greedy fill of each row to its own key budget (the same fill as
+    ``select_row``: ratio descending, crossing block included)."""
+    mask = np.zeros(r.shape, dtype=np.uint8)
+    for i in range(r.shape[0]):
+        if q_sizes[i] > 0:
+            mask[i] = select_row(r[i], k_sizes, float(budgets[i]))
+    return mask
+
+
+def route_topp(qbar, q_offsets, Kp, Vp, kbar, vbar, k_offsets, scale, p, error_ranked=True):
+    """Routing under the SVG2 budget.
+
+    error_ranked=False: the SVG2 router itself, top-p over P'.
+    error_ranked=True:  SVG-EAR's use of that budget (FrontierCS blog, budget
+    paragraph): each query cluster gets the keys of its top-p selection and
+    spends them on the blocks with the highest error per pair.
+    Returns (P' float32 [Cq, Ck], ratios float32 [Cq, Ck] or None,
+    budgets int64 [Cq], mask [Cq, Ck])."""
+    q_sizes = np.diff(np.asarray(q_offsets))
+    k_sizes = np.diff(np.asarray(k_offsets))
+    P = topp_probs(qbar, kbar, k_sizes, scale)
+    P[q_sizes == 0] = 0.0
+    tmask = topp_select(P, q_sizes, k_sizes, p)
+    budgets = topp_budgets(tmask, k_sizes)
+    if not error_ranked:
+        return P, None, budgets, tmask
+    e, _ = probe_errors(qbar, Kp, Vp, kbar, vbar, k_offsets, scale, q_nonempty=q_sizes > 0)
+    r = ratios(e, q_sizes, k_sizes)
+    return P, r, budgets, select_budgets(r, q_sizes, k_sizes, budgets)
 
 
 # --------------------------------------------------------------------------

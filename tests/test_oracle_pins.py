@@ -402,3 +402,167 @@ def test_variance_correction_is_second_order_and_neutral_at_zero():
         assert np.all(plain_w <= exact * (1 + 1e-12))          # Jensen: the plain guess is low
         worse += int(np.sum(np.abs(corr_w - exact) > np.abs(plain_w - exact)))
     assert worse == 0
+
+
+# ---------------------------------------------------------------- top-p budget and the SVG2 router
+def test_toy_topp_shares_tie_and_the_two_routers_split():
+    """Blog toy: both centroids score 1 and both clusters hold two keys, so the
+    estimated weights tie; with room for one cluster the score-ranked router
+    keeps A (tie to the lower index) while the error-ranked one keeps B."""
+    g, q, K, V, lab = toy()
+    assert g["printed"]["estimated_weight_ranking"] == "tie"
+    perm, off = orc.permute(lab, 2)
+    kbar, vbar = orc.means(K, perm, off), orc.means(V, perm, off)
+    sizes = np.diff(off)
+    P = orc.topp_probs(q, kbar, sizes, 1.0)
+    assert P.tolist() == [[0.5, 0.5]]
+    q_off = np.array([0, 1])
+    # p = 0.5: the first cluster's share already reaches p, so one cluster's keys
+    _, _, bud, m_score = orc.route_topp(q, q_off, K[perm], V[perm], kbar, vbar, off, 1.0, 0.5, error_ranked=False)
+    assert m_score.tolist() == [[1, 0]] and bud.tolist() == [2]
+    _, r, bud2, m_err = orc.route_topp(q, q_off, K[perm], V[perm], kbar, vbar, off, 1.0, 0.5, error_ranked=True)
+    assert bud2.tolist() == [2]
+    assert {"A": [[1, 0]], "B": [[0, 1]]}[g["printed"]["choice_with_room_for_one_cluster"]] == m_err.tolist()
+    # p just above one cluster's share needs both
+    _, _, bud3, m3 = orc.route_topp(q, q_off, K[perm], V[perm], kbar, vbar, off, 1.0, 0.6, error_ranked=False)
+    assert m3.tolist() == [[1, 1]] and bud3.tolist() == [4]
+
+
+def onehot_mass(qbar, K, lab, C, scale):
+    """Dense attention mass per cluster from the library: attend with values
+    that are the one-hot cluster indicator."""
+    Vh = np.eye(C)[lab]
+    return sdpa64(qbar, K, Vh, scale)
+
+
+def test_topp_probs_equal_dense_mass_for_singleton_and_identical_clusters():
+    """P' estimates each key cluster's share of the attention mass.  It is exact
+    when every key of a cluster equals the centroid: singleton clusters give the
+    dense softmax probabilities, and clusters of identical keys their summed
+    probability (the |K_j| factor).  Checked against torch's fp64 attention."""
+    rng = np.random.default_rng(21)
+    D, scale = 8, 1 / np.sqrt(8)
+    qbar = rng.standard_normal((4, D))
+    # singletons
+    K = rng.standard_normal((12, D))
+    lab = np.arange(12)
+    perm, off = orc.permute(lab, 12)
+    P = orc.topp_probs(qbar, orc.means(K, perm, off), np.diff(off), scale)
+    np.testing.assert_allclose(P, onehot_mass(qbar, K, lab, 12, scale), rtol=1e-6, atol=1e-9)
+    # identical members, unequal sizes, one empty cluster
+    cent = rng.standard_normal((5, D))
+    lab = np.array([0, 0, 0, 1, 3, 3, 4, 4, 4, 4, 4, 0])
+    K = cent[lab]
+    perm, off = orc.permute(lab, 5)
+    sizes = np.diff(off)
+    assert sizes[2] == 0
+    P = orc.topp_probs(qbar, orc.means(K, perm, off), sizes, scale)
+    np.testing.assert_allclose(P, onehot_mass(qbar, K, lab, 5, scale), rtol=1e-6, atol=1e-9)
+    assert (P[:, 2] == 0).all()
+    np.testing.assert_allclose(P.astype(np.float64).sum(axis=1), 1.0, rtol=0, atol=1e-6)
+
+
+def test_topp_probs_survive_large_scores():
+    """Scores far beyond exp's range still give finite shares (the row maximum
+    is taken over non-empty clusters only)."""
+    qbar = np.array([[1.0]])
+    kbar = np.array([[900.0], [899.0], [0.0]])
+    P = orc.topp_probs(qbar, kbar, np.array([1, 2, 0]), 1.0)
+    e = np.exp(-1.0)
+    np.testing.assert_allclose(P[0], [1 / (1 + 2 * e), 2 * e / (1 + 2 * e), 0.0], rtol=1e-6)
+
+
+def brute_topp_size(P_row, sizes, p):
+    """Fewest non-empty clusters whose shares sum to at least p (enumeration)."""
+    import itertools
+    live = [j for j in range(len(sizes)) if sizes[j] > 0]
+    for k in range(1, len(live) + 1):
+        if max(sum(float(P_row[j]) for j in c) for c in itertools.combinations(live, k)) >= p:
+            return k
+    return len(live)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topp_select_is_the_smallest_set_reaching_p_by_brute_force(seed):
+    rng = np.random.default_rng(100 + seed)
+    C = 7
+    sizes = rng.integers(0, 4, C)
+    sizes[rng.integers(0, C)] = 2
+    kbar = rng.standard_normal((C, 3)) * 2
+    qbar = rng.standard_normal((1, 3))
+    P = orc.topp_probs(qbar, kbar, sizes, 1.0)[0]
+    prev = np.zeros(C, np.uint8)
+    for p in (0.05, 0.3, 0.5, 0.77, 0.9, 0.999, 1.0):
+        sel = orc.topp_select_row(P, sizes, p)
+        assert (sel[sizes == 0] == 0).all()
+        if p < 1.0:
+            assert sel.sum() == brute_topp_size(P, sizes, float(np.float32(p)))
+            assert sum(float(P[j]) for j in np.flatnonzero(sel)) >= float(np.float32(p))
+        else:
+            assert (sel[sizes > 0] == 1).all()
+        # the selection is a prefix of the share order: nothing left out beats what is in
+        live_out = (sel == 0) & (sizes > 0)
+        if live_out.any() and sel.any():
+            assert P[sel == 1].min() >= P[live_out].max()
+        assert (sel >= prev).all()          # nested in p
+        prev = sel
+
+
+def test_topp_hand_example():
+    sizes = np.array([3, 1, 0, 4, 2])
+    P = np.array([0.25, 0.5, 0.0, 0.125, 0.125], dtype=np.float32)
+    # order 1 (0.5), 0 (0.25), 3 and 4 (tie at 0.125, lower index first)
+    assert orc.topp_select_row(P, sizes, 0.5).tolist() == [0, 1, 0, 0, 0]
+    assert orc.topp_select_row(P, sizes, 0.6).tolist() == [1, 1, 0, 0, 0]
+    assert orc.topp_select_row(P, sizes, 0.8).tolist() == [1, 1, 0, 1, 0]
+    assert orc.topp_select_row(P, sizes, 1.0).tolist() == [1, 1, 0, 1, 1]
+    m = orc.topp_select(P[None].repeat(2, 0), np.array([5, 0]), sizes, 0.8)
+    assert m.tolist() == [[1, 1, 0, 1, 0], [0, 0, 0, 0, 0]]
+    assert orc.topp_budgets(m, sizes).tolist() == [8, 0]
+
+
+def test_error_ranked_budget_reduces_to_top_p_when_rankings_agree():
+    """Spending the top-p keys in the top-p order selects the top-p set again;
+    with one common budget it is the density router."""
+    h = small_head(9, N=384, D=16, comps=8, Cq=6, Ck=16)
+    q, k, v = h["q"], h["k"], h["v"]
+    _, lq = orc.lloyd(q, h["cq0"], 3)
+    _, lk = orc.lloyd(k, h["ck0"], 3)
+    pq, oq = orc.permute(lq, 6)
+    pk, ok = orc.permute(lk, 16)
+    qbar, kbar = orc.means(q, pq, oq), orc.means(k, pk, ok)
+    qs, ks = np.diff(oq), np.diff(ok)
+    P = orc.topp_probs(qbar, kbar, ks, 0.25)
+    for p in (0.3, 0.6, 0.9):
+        tm = orc.topp_select(P, qs, ks, p)
+        assert (orc.select_budgets(P, qs, ks, orc.topp_budgets(tm, ks)) == tm).all()
+    r = np.random.default_rng(3).random(P.shape).astype(np.float32)
+    same = np.full(6, float(np.float32(0.3)) * 384)
+    assert (orc.select_budgets(r, qs, ks, same) == orc.select(r, qs, ks, 0.3, 384)).all()
+
+
+def test_route_topp_budgets_and_bounds():
+    h = small_head(10, N=512, D=16, comps=10, Cq=6, Ck=20)
+    q, k, v = h["q"], h["k"], h["v"]
+    _, lq = orc.lloyd(q, h["cq0"], 3)
+    _, lk = orc.lloyd(k, h["ck0"], 3)
+    pq, oq = orc.permute(lq, 6)
+    pk, ok = orc.permute(lk, 20)
+    qbar, kbar, vbar = orc.means(q, pq, oq), orc.means(k, pk, ok), orc.means(v, pk, ok)
+    ks = np.diff(ok)
+    prev = None
+    for p in (0.5, 0.8, 0.9, 1.0):
+        P, r, bud, m = orc.route_topp(qbar, oq, k[pk], v[pk], kbar, vbar, ok, 0.25, p)
+        Ps, _, bud_s, ms = orc.route_topp(qbar, oq, k[pk], v[pk], kbar, vbar, ok, 0.25, p, error_ranked=False)
+        assert (Ps == P).all() and (bud_s == bud).all()
+        assert (bud == (ms.astype(np.int64) * ks).sum(axis=1)).all()
+        for i in range(6):
+            keys = int((m[i].astype(np.int64) * ks).sum())
+            assert bud[i] <= keys < bud[i] + ks.max()
+            sel, uns = r[i][m[i] == 1], r[i][(m[i] == 0) & (ks > 0)]
+            if uns.size:
+                assert sel.min() >= uns.max()
+        if prev is not None:
+            assert (bud >= prev).all()
+        prev = bud
+    assert (prev == 512).all()
