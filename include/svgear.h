@@ -159,6 +159,54 @@ svgear_status svgear_route(const float* q_means, const int32_t* q_offsets, int C
                            size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
+ * svgear_route_topp -- routing under the SVG2 top-p budget.
+ *
+ * SVG2 summary, "Centroid-Based Top-p Selection": the centroid score
+ * S_ij = q_bar_i.k_bar_j * scale gives each key cluster an estimated share of
+ * query cluster i's attention mass, P'_ij = |K_j| e^{S_ij} / sum_l |K_l| e^{S_il};
+ * clusters are taken in descending P' until the shares taken reach top_p.
+ * FrontierCS blog on SVG-EAR, budget paragraph: SVG-EAR keeps that selection's
+ * token pairs as the budget and spends them on the blocks with the most error
+ * per pair.
+ *
+ * Readings fixed here: P' is evaluated in fp64 relative to the row's largest
+ * S over non-empty clusters and rounded to float32; non-empty key clusters
+ * are ordered by (P' desc, j asc) and their shares are added in that order in
+ * double, a cluster being taken while the sum before it is < top_p, so the
+ * cluster that reaches top_p is included; top_p = 1 takes every non-empty
+ * cluster.  Row i's budget is the number of keys in its top-p clusters
+ * (pairs = |Q_i| times that).  With error_ranked = 1 the mask is the greedy
+ * fill of svgear_route (ratio desc, j asc, taken while the keys before are
+ * < the row's budget, crossing block included) with the row's own budget in
+ * place of density * N; with error_ranked = 0 the mask is the top-p selection
+ * itself (the SVG2 router).  Rows of empty query clusters are all zero.
+ *
+ *   q_means .. scale   as for svgear_route.   top_p in (0, 1].
+ *   error_ranked 0 or 1, as above.
+ *   probs_in   nullable [B,H,Cq,Ck] float32: when given, P' is taken from it
+ *              instead of the centroids.
+ *   scores_in  nullable [B,H,Cq,Ck] float32, error_ranked = 1 only: ratios
+ *              given, the probe is skipped.
+ *   probs_out  nullable [B,H,Cq,Ck] float32 OUT: the P' used (0 for empty
+ *              key clusters and rows of empty query clusters).
+ *   scores_out nullable [B,H,Cq,Ck] float32 OUT, error_ranked = 1 only.
+ *   budget_out nullable [B,H,Cq] int32 OUT: keys per row of the top-p set.
+ *   mask       [B,H,Cq,Ck] uint8 OUT.
+ * Pointers that the chosen inputs make unnecessary may be null: q_means and
+ * k_means when probs_in is given and no probe runs; k_perm, v_perm, v_means
+ * unless error_ranked = 1 without scores_in.  ws: at least
+ * svgear_route_workspace(...) bytes.  Asynchronous on stream.
+ * ---------------------------------------------------------------------- */
+svgear_status svgear_route_topp(const float* q_means, const int32_t* q_offsets, int Cq,
+                                const void* k_perm, const void* v_perm, svgear_dtype dt,
+                                const float* k_means, const float* v_means,
+                                const int32_t* k_offsets, int Ck, int B, int H, int N, int D,
+                                float scale, float top_p, int error_ranked,
+                                const float* probs_in, const float* scores_in, float* probs_out,
+                                float* scores_out, int32_t* budget_out, uint8_t* mask, void* ws,
+                                size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
  * svgear_sparse_attn -- dynamic-block-size sparse attention with centroid
  * compensation, output in original token order.
  *

@@ -266,12 +266,143 @@ __global__ void __launch_bounds__(256) rt_main_kernel(const T* __restrict__ kp, 
 // One workgroup per (batch, head, query cluster): ratios r_ij, then the
 // greedy fill.  Keys sort as (r descending, j ascending) by a bitonic sort of
 // (~bits(r) << 32 | j); empty key clusters sort last and are never taken.
+// Sort key of a non-negative score: larger scores first, ties to the lower
+// index; NaN sorts first so that it cannot hide.
+__device__ __forceinline__ uint64_t desc_key(float r, int j) {
+  const uint32_t hi = (r != r) ? 0xFFFFFFFFu : ~__float_as_uint(r == 0.f ? 0.f : r);
+  return ((uint64_t)hi << 32) | (uint32_t)j;
+}
+
+// Ascending bitonic sort of P (a power of two) keys in LDS by a 256-thread block.
+__device__ __forceinline__ void block_sort_keys(uint64_t* s_key, int P) {
+  const int tid = threadIdx.x;
+  for (int k = 2; k <= P; k <<= 1) {
+    for (int s = k >> 1; s > 0; s >>= 1) {
+      for (int t = tid; t < P; t += 256) {
+        const int o = t ^ s;
+        if (o > t) {
+          const uint64_t a = s_key[t], b = s_key[o];
+          const bool up = (t & k) == 0;
+          if ((a > b) == up) { s_key[t] = b; s_key[o] = a; }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__device__ __forceinline__ double readlane_d(double v, int l) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// SVG2 top-p over the centroid shares of one query cluster (SVG2 summary,
+// "Centroid-Based Top-p Selection").  P'_j = n_j e^{S_j - M} / sum_l n_l e^{S_l - M}
+// in fp64, M the largest S_j over non-empty clusters, rounded to fp32 (or taken
+// from probs_in).  Non-empty clusters are ordered by (P' desc, j asc); one wave
+// adds the shares in that order in fp64, one term at a time, and a cluster is
+// taken while the sum before it is < p (p >= 1 takes them all).  Writes the
+// mask row (nullable), the row's key budget = keys taken (nullable) and P'
+// (nullable).
+__global__ void __launch_bounds__(256) rt_topp_kernel(const float* __restrict__ sbar, const float* __restrict__ probs_in,
+                                                      const int32_t* __restrict__ qoff, const int32_t* __restrict__ koff,
+                                                      int Cq, int Ck, double p, float* __restrict__ probs_out,
+                                                      int32_t* __restrict__ budget, uint8_t* __restrict__ mask) {
+  __shared__ uint64_t s_key[SEL_MAX];
+  __shared__ float s_p[SEL_MAX];
+  __shared__ int s_n[SEL_MAX];
+  __shared__ double s_sum[4];
+  __shared__ float s_max[4];
+  __shared__ int s_take[2];
+  const int bh = blockIdx.y, i = blockIdx.x, tid = threadIdx.x;
+  const int32_t* qo = qoff + (size_t)bh * (Cq + 1);
+  const int32_t* ko = koff + (size_t)bh * (Ck + 1);
+  const size_t row = (size_t)bh * Cq + i;
+  if (qo[i + 1] == qo[i]) {
+    for (int j = tid; j < Ck; j += 256) {
+      if (mask) mask[row * Ck + j] = 0;
+      if (probs_out) probs_out[row * Ck + j] = 0.f;
+    }
+    if (tid == 0 && budget) budget[row] = 0;
+    return;
+  }
+  for (int j = tid; j < Ck; j += 256) s_n[j] = ko[j + 1] - ko[j];
+  if (probs_in) {
+    for (int j = tid; j < Ck; j += 256) s_p[j] = probs_in[row * Ck + j];
+  } else {
+    const float* srow = sbar + row * Ck;
+    float m = -INFINITY;
+    for (int j = tid; j < Ck; j += 256)
+      if (ko[j + 1] > ko[j]) m = fmaxf(m, srow[j]);
+    m = wave_max_f(m);
+    if (lane_id() == 0) s_max[wave_id()] = m;
+    __syncthreads();
+    const double M = (double)fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
+    double sum = 0.0;
+    for (int j = tid; j < Ck; j += 256) {
+      const int n = s_n[j];
+      if (n > 0) sum += (double)n * exp((double)srow[j] - M);
+    }
+    sum = wave_sum_d(sum);
+    if (lane_id() == 0) s_sum[wave_id()] = sum;
+    __syncthreads();
+    const double tot = (s_sum[0] + s_sum[1]) + (s_sum[2] + s_sum[3]);
+    for (int j = tid; j < Ck; j += 256) {
+      const int n = s_n[j];
+      s_p[j] = n > 0 ? (float)((double)n * exp((double)srow[j] - M) / tot) : 0.f;
+    }
+  }
+  __syncthreads();
+  if (probs_out)
+    for (int j = tid; j < Ck; j += 256) probs_out[row * Ck + j] = s_p[j];
+  int P = 1;
+  while (P < Ck) P <<= 1;
+  for (int j = tid; j < P; j += 256) s_key[j] = (j < Ck && s_n[j] > 0) ? desc_key(s_p[j], j) : ~0ull;
+  __syncthreads();
+  block_sort_keys(s_key, P);
+  if (tid < SV_WAVE) {
+    double cum = 0.0;
+    int taken = 0, keys = 0;
+    bool stop = false;
+    for (int t0 = 0; t0 < P && !stop; t0 += SV_WAVE) {
+      const int t = t0 + tid;
+      const uint64_t key = t < P ? s_key[t] : ~0ull;
+      const bool valid = key != ~0ull;
+      const int j = (int)(uint32_t)key;
+      const double pv = valid ? (double)s_p[j] : 0.0;
+      const int nv = valid ? s_n[j] : 0;
+      const uint64_t vb = ballot(valid);
+      for (int l = 0; l < SV_WAVE; ++l) {
+        if (!((vb >> l) & 1ull) || (p < 1.0 && cum >= p)) { stop = true; break; }
+        cum += readlane_d(pv, l);
+        keys += __builtin_amdgcn_readlane(nv, l);
+        ++taken;
+      }
+    }
+    if (tid == 0) { s_take[0] = taken; s_take[1] = keys; }
+  }
+  __syncthreads();
+  const int T = s_take[0];
+  if (mask) {
+    uint8_t* mrow = mask + row * Ck;
+    for (int t = tid; t < P; t += 256) {
+      const uint64_t key = s_key[t];
+      if (key != ~0ull) mrow[(int)(uint32_t)key] = t < T ? 1 : 0;
+    }
+    for (int j = tid; j < Ck; j += 256)
+      if (s_n[j] == 0) mrow[j] = 0;
+  }
+  if (tid == 0 && budget) budget[row] = s_take[1];
+}
+
 __global__ void __launch_bounds__(256) rt_select_kernel(const float* __restrict__ part, const float* __restrict__ t1part,
                                                         const int32_t* __restrict__ pstart, const float* __restrict__ sbar,
                                                         const int32_t* __restrict__ qoff, const int32_t* __restrict__ koff,
                                                         const float* __restrict__ scores_in, int Cq, int Ck, int maxp,
-                                                        double budget, float* __restrict__ scores_out,
-                                                        uint8_t* __restrict__ mask) {
+                                                        double budget, const int32_t* __restrict__ row_budget,
+                                                        float* __restrict__ scores_out, uint8_t* __restrict__ mask) {
   __shared__ uint64_t s_key[SEL_MAX];
   __shared__ float s_mu[SEL_MAX];
   __shared__ float s_e[SEL_MAX];
@@ -335,29 +466,12 @@ __global__ void __launch_bounds__(256) rt_select_kernel(const float* __restrict_
   }
   __syncthreads();
   for (int j = tid; j < P; j += 256) {
-    uint64_t key = ~0ull;
-    if (j < Ck && ko[j + 1] > ko[j]) {
-      const float r = s_e[j];
-      const uint32_t hi = (r != r) ? 0xFFFFFFFFu : ~__float_as_uint(r == 0.f ? 0.f : r);
-      key = ((uint64_t)hi << 32) | (uint32_t)j;
-    }
-    s_key[j] = key;
+    s_key[j] = (j < Ck && ko[j + 1] > ko[j]) ? desc_key(s_e[j], j) : ~0ull;
     if (srow && j < Ck) srow[j] = s_e[j];
   }
   __syncthreads();
-  for (int k = 2; k <= P; k <<= 1) {
-    for (int s = k >> 1; s > 0; s >>= 1) {
-      for (int t = tid; t < P; t += 256) {
-        const int o = t ^ s;
-        if (o > t) {
-          const uint64_t a = s_key[t], b = s_key[o];
-          const bool up = (t & k) == 0;
-          if ((a > b) == up) { s_key[t] = b; s_key[o] = a; }
-        }
-      }
-      __syncthreads();
-    }
-  }
+  block_sort_keys(s_key, P);
+  const double bud = row_budget ? (double)row_budget[(size_t)bh * Cq + i] : budget;
   // cumulative keys before each sorted position; each thread owns a run
   const int per = (P + 255) / 256;
   const int t0 = tid * per;
@@ -372,7 +486,7 @@ __global__ void __launch_bounds__(256) rt_select_kernel(const float* __restrict_
     const uint64_t key = s_key[t];
     if (key == ~0ull) continue;
     const int jj = (int)(uint32_t)key;
-    mrow[jj] = ((double)before < budget) ? 1 : 0;
+    mrow[jj] = ((double)before < bud) ? 1 : 0;
     before += ko[jj + 1] - ko[jj];
   }
   // empty key clusters (sorted last with the all-ones key) are never taken
@@ -383,7 +497,7 @@ __global__ void __launch_bounds__(256) rt_select_kernel(const float* __restrict_
 // ---------------------------------------------------------------- host side
 struct RtPlan {
   int BH, Cqp, maxp;
-  size_t off_qhi, off_qlo, off_sbar, off_ps, off_part, off_t1, total;
+  size_t off_qhi, off_qlo, off_sbar, off_ps, off_part, off_t1, off_bud, total;
 };
 
 static RtPlan rt_plan(int B, int H, int N, int D, int Cq, int Ck) {
@@ -398,8 +512,39 @@ static RtPlan rt_plan(int B, int H, int N, int D, int Cq, int Ck) {
   p.off_ps = cv.used; cv.take<int32_t>((size_t)p.BH * (Ck + 1));
   p.off_part = cv.used; cv.take<float>((size_t)p.BH * p.maxp * Cq * 3);
   p.off_t1 = cv.used; cv.take<float>((size_t)p.BH * p.maxp);
+  p.off_bud = cv.used; cv.take<int32_t>((size_t)p.BH * Cq);
   p.total = cv.used;
   return p;
+}
+
+static void launch_sbar(const float* q_means, const float* k_means, int BH, int Cq, int Ck, int D, float scale,
+                        float* sbar, hipStream_t stream) {
+  hipLaunchKernelGGL(rt_sbar_kernel, dim3(cdiv(Ck, 64), cdiv(Cq, 16), BH), dim3(256), 0, stream, q_means, k_means, Cq,
+                     Ck, D, scale, sbar);
+}
+
+// The probe: q_bar hi/lo split, key pieces, per-(piece, query cluster) partial errors.
+static void launch_probe(const RtPlan& p, const float* q_means, const void* k_perm, const void* v_perm, svgear_dtype dt,
+                         const float* k_means, const float* v_means, const int32_t* k_offsets, int Cq, int Ck, int BH,
+                         int N, int D, float scale, bf16* qh, bf16* ql, int32_t* ps, float* part, float* t1,
+                         hipStream_t stream) {
+  if (D == 128)
+    hipLaunchKernelGGL((rt_prep_kernel<128>), dim3(cdiv(p.Cqp * D, 256), BH), dim3(256), 0, stream, q_means, Cq, p.Cqp,
+                       qh, ql);
+  else
+    hipLaunchKernelGGL((rt_prep_kernel<64>), dim3(cdiv(p.Cqp * D, 256), BH), dim3(256), 0, stream, q_means, Cq, p.Cqp,
+                       qh, ql);
+  hipLaunchKernelGGL(chunk_list_kernel, dim3(BH), dim3(1024), 0, stream, k_offsets, Ck, RT_PIECE, ps);
+#define RT_MAIN(T, DD)                                                                                              \
+  hipLaunchKernelGGL((rt_main_kernel<T, DD>), dim3(p.maxp, BH), dim3(256), 0, stream, (const T*)k_perm,          \
+                     (const T*)v_perm, k_means, v_means, k_offsets, ps, qh, ql, N, Cq, p.Cqp, Ck, p.maxp, scale, part, \
+                     t1)
+  if (dt == SVGEAR_BF16) {
+    if (D == 128) RT_MAIN(bf16, 128); else RT_MAIN(bf16, 64);
+  } else {
+    if (D == 128) RT_MAIN(float, 128); else RT_MAIN(float, 64);
+  }
+#undef RT_MAIN
 }
 
 }  // namespace svg
@@ -436,30 +581,62 @@ extern "C" svgear_status svgear_route(const float* q_means, const int32_t* q_off
   int32_t* ps = reinterpret_cast<int32_t*>(w + p.off_ps);
   float* part = reinterpret_cast<float*>(w + p.off_part);
   float* t1 = reinterpret_cast<float*>(w + p.off_t1);
-  const int BH = B * H;
   const double budget = (double)density * (double)N;
   if (!scores_in) {
-    if (D == 128)
-      hipLaunchKernelGGL((rt_prep_kernel<128>), dim3(cdiv(p.Cqp * D, 256), BH), dim3(256), 0, stream, q_means, Cq,
-                         p.Cqp, qh, ql);
-    else
-      hipLaunchKernelGGL((rt_prep_kernel<64>), dim3(cdiv(p.Cqp * D, 256), BH), dim3(256), 0, stream, q_means, Cq,
-                         p.Cqp, qh, ql);
-    hipLaunchKernelGGL(rt_sbar_kernel, dim3(cdiv(Ck, 64), cdiv(Cq, 16), BH), dim3(256), 0, stream, q_means, k_means,
-                       Cq, Ck, D, scale, sbar);
-    hipLaunchKernelGGL(chunk_list_kernel, dim3(BH), dim3(1024), 0, stream, k_offsets, Ck, RT_PIECE, ps);
-#define RT_MAIN(T, DD)                                                                                              \
-  hipLaunchKernelGGL((rt_main_kernel<T, DD>), dim3(p.maxp, BH), dim3(256), 0, stream, (const T*)k_perm,          \
-                     (const T*)v_perm, k_means, v_means, k_offsets, ps, qh, ql, N, Cq, p.Cqp, Ck, p.maxp, scale, part, \
-                     t1)
-    if (dt == SVGEAR_BF16) {
-      if (D == 128) RT_MAIN(bf16, 128); else RT_MAIN(bf16, 64);
-    } else {
-      if (D == 128) RT_MAIN(float, 128); else RT_MAIN(float, 64);
-    }
-#undef RT_MAIN
+    launch_sbar(q_means, k_means, B * H, Cq, Ck, D, scale, sbar, stream);
+    launch_probe(p, q_means, k_perm, v_perm, dt, k_means, v_means, k_offsets, Cq, Ck, B * H, N, D, scale, qh, ql, ps,
+                 part, t1, stream);
   }
-  hipLaunchKernelGGL(rt_select_kernel, dim3(Cq, BH), dim3(256), 0, stream, part, t1, ps, sbar, q_offsets, k_offsets,
-                     scores_in, Cq, Ck, p.maxp, budget, scores_out, mask);
+  hipLaunchKernelGGL(rt_select_kernel, dim3(Cq, B * H), dim3(256), 0, stream, part, t1, ps, sbar, q_offsets,
+                     k_offsets, scores_in, Cq, Ck, p.maxp, budget, nullptr, scores_out, mask);
   return check_launch("svgear_route");
+}
+
+extern "C" svgear_status svgear_route_topp(const float* q_means, const int32_t* q_offsets, int Cq, const void* k_perm,
+                                           const void* v_perm, svgear_dtype dt, const float* k_means,
+                                           const float* v_means, const int32_t* k_offsets, int Ck, int B, int H, int N,
+                                           int D, float scale, float top_p, int error_ranked, const float* probs_in,
+                                           const float* scores_in, float* probs_out, float* scores_out,
+                                           int32_t* budget_out, uint8_t* mask, void* ws, size_t ws_bytes,
+                                           hipStream_t stream) {
+  svgear_status st = check_common("route_topp", dt, B, H, N, D);
+  if (st != SVGEAR_OK) return st;
+  if (Cq < 1 || Cq > N || Cq > SVGEAR_MAX_CLUSTERS || Ck < 1 || Ck > N || Ck > SVGEAR_MAX_CLUSTERS)
+    return fail(SVGEAR_ERR_INVALID_ARG, "route_topp: Cq=%d, Ck=%d must be in [1, min(N=%d, %d)]", Cq, Ck, N,
+                SVGEAR_MAX_CLUSTERS);
+  if (!(scale > 0.f) || !(scale < INFINITY))
+    return fail(SVGEAR_ERR_INVALID_ARG, "route_topp: scale must be > 0 and finite");
+  if (!(top_p > 0.f && top_p <= 1.f)) return fail(SVGEAR_ERR_INVALID_ARG, "route_topp: top_p must be in (0, 1]");
+  if (error_ranked != 0 && error_ranked != 1)
+    return fail(SVGEAR_ERR_INVALID_ARG, "route_topp: error_ranked must be 0 or 1");
+  if (!error_ranked && (scores_in || scores_out))
+    return fail(SVGEAR_ERR_INVALID_ARG, "route_topp: ratios exist only with error_ranked = 1");
+  if (!q_offsets || !k_offsets || !mask) return fail(SVGEAR_ERR_INVALID_ARG, "route_topp: null pointer");
+  const bool need_sbar = !probs_in || (error_ranked && !scores_in);
+  const bool need_probe = error_ranked && !scores_in;
+  if (need_sbar && (!q_means || !k_means)) return fail(SVGEAR_ERR_INVALID_ARG, "route_topp: null pointer");
+  if (need_probe && (!k_perm || !v_perm || !v_means)) return fail(SVGEAR_ERR_INVALID_ARG, "route_topp: null pointer");
+  RtPlan p = rt_plan(B, H, N, D, Cq, Ck);
+  st = check_ws("route_topp", ws, ws_bytes, p.total);
+  if (st != SVGEAR_OK) return st;
+  char* w = static_cast<char*>(ws);
+  bf16* qh = reinterpret_cast<bf16*>(w + p.off_qhi);
+  bf16* ql = reinterpret_cast<bf16*>(w + p.off_qlo);
+  float* sbar = reinterpret_cast<float*>(w + p.off_sbar);
+  int32_t* ps = reinterpret_cast<int32_t*>(w + p.off_ps);
+  float* part = reinterpret_cast<float*>(w + p.off_part);
+  float* t1 = reinterpret_cast<float*>(w + p.off_t1);
+  int32_t* bud = budget_out ? budget_out : reinterpret_cast<int32_t*>(w + p.off_bud);
+  const int BH = B * H;
+  if (need_sbar) launch_sbar(q_means, k_means, BH, Cq, Ck, D, scale, sbar, stream);
+  hipLaunchKernelGGL(rt_topp_kernel, dim3(Cq, BH), dim3(256), 0, stream, probs_in ? nullptr : sbar, probs_in,
+                     q_offsets, k_offsets, Cq, Ck, (double)top_p, probs_out, bud, error_ranked ? nullptr : mask);
+  if (error_ranked) {
+    if (need_probe)
+      launch_probe(p, q_means, k_perm, v_perm, dt, k_means, v_means, k_offsets, Cq, Ck, BH, N, D, scale, qh, ql, ps,
+                   part, t1, stream);
+    hipLaunchKernelGGL(rt_select_kernel, dim3(Cq, BH), dim3(256), 0, stream, part, t1, ps, sbar, q_offsets, k_offsets,
+                       scores_in, Cq, Ck, p.maxp, 0.0, bud, scores_out, mask);
+  }
+  return check_launch("svgear_route_topp");
 }

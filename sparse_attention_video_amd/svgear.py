@@ -27,6 +27,7 @@ EXPORTS = (
     "svgear_route_workspace", "svgear_route",
     "svgear_sparse_attn_workspace", "svgear_sparse_attn",
     "svgear_centroid_variances", "svgear_sparse_attn_var",
+    "svgear_route_topp",
 )
 
 _lib = None
@@ -69,6 +70,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.svgear_centroid_variances.restype = I
     lib.svgear_sparse_attn_var.argtypes = [P, P, P, I, P, P, I, P, I, P, P, P, F, P, I, I, I, I, F, P, P, P, Z, P]
     lib.svgear_sparse_attn_var.restype = I
+    lib.svgear_route_topp.argtypes = [P, P, I, P, P, I, P, P, P, I, I, I, I, I, F, F, I, P, P, P, P, P, P, P, Z, P]
+    lib.svgear_route_topp.restype = I
     _lib = lib
     return lib
 
@@ -189,6 +192,42 @@ def route(q_means, q_offsets, k_perm, v_perm, k_means, v_means, k_offsets, scale
                                             _ptr(scores if want_scores else None), _ptr(mask), _ptr(ws), ws.numel(),
                                             _stream(dev)))
     return (scores if want_scores else None), mask
+
+
+def route_topp(q_means, q_offsets, k_perm, v_perm, k_means, v_means, k_offsets, scale: float, top_p: float,
+               error_ranked: bool = True, probs_in: Optional[torch.Tensor] = None,
+               scores_in: Optional[torch.Tensor] = None, want_probs: bool = True, want_scores: bool = False,
+               want_budget: bool = True, N: Optional[int] = None, D: Optional[int] = None, ws=None):
+    """Routing under the SVG2 top-p budget.  Returns (probs [B,H,Cq,Ck] fp32 or
+    None, scores [B,H,Cq,Ck] fp32 or None, budget [B,H,Cq] int32 or None,
+    mask [B,H,Cq,Ck] uint8).  N and D default to k_perm's shape."""
+    dev = _dev(q_offsets, k_offsets)
+    B, H, Cq1 = q_offsets.shape
+    Cq, Ck = Cq1 - 1, k_offsets.shape[2] - 1
+    if k_perm is not None:
+        _dev(k_perm)
+        N, D, dt = int(k_perm.shape[2]), int(k_perm.shape[3]), _dtype(k_perm)
+    else:
+        if N is None or D is None:
+            raise ValueError("N and D are needed when k_perm is not given")
+        dt = F32
+    for t in (q_means, v_perm, k_means, v_means, probs_in, scores_in):
+        if t is not None:
+            _dev(t)
+    mk = lambda shape, dtype: torch.empty(shape, dtype=dtype, device=dev)
+    mask = mk((B, H, Cq, Ck), torch.uint8)
+    probs = mk((B, H, Cq, Ck), torch.float32) if want_probs else None
+    scores = mk((B, H, Cq, Ck), torch.float32) if (want_scores and error_ranked) else None
+    budget = mk((B, H, Cq), torch.int32) if want_budget else None
+    lib = load()
+    need = lib.svgear_route_workspace(B, H, N, D, Cq, Ck)
+    ws = ws if ws is not None else _workspace(need, dev)
+    _check("svgear_route_topp",
+           lib.svgear_route_topp(_ptr(q_means), _ptr(q_offsets), Cq, _ptr(k_perm), _ptr(v_perm), dt, _ptr(k_means),
+                                 _ptr(v_means), _ptr(k_offsets), Ck, B, H, N, D, float(scale), float(top_p),
+                                 1 if error_ranked else 0, _ptr(probs_in), _ptr(scores_in), _ptr(probs),
+                                 _ptr(scores), _ptr(budget), _ptr(mask), _ptr(ws), ws.numel(), _stream(dev)))
+    return probs, scores, budget, mask
 
 
 def centroid_variances(x: torch.Tensor, perm: torch.Tensor, offsets: torch.Tensor, means: torch.Tensor, vars=None,

@@ -60,3 +60,52 @@ def mean_bound(X, perm, offsets):
 def oracle_stage_inputs(q, k, v, cq0, ck0, iters, density, scale):
     """Run the oracle layer for one head (all intermediates)."""
     return orc.layer(q, k, v, cq0, ck0, iters, density, scale)
+
+
+def topp_near_tie_row(P_row, k_sizes, mask_row, p, tol=2e-4):
+    """Whether a top-p row (oracle shares P_row, oracle selection mask_row) sits
+    within tol of a different selection: the shares summed before or through
+    the boundary cluster nearly equal p, or the boundary share nearly ties
+    with the first share left out.  Only such rows may differ when the GPU
+    computes its own shares."""
+    k_sizes = np.asarray(k_sizes)
+    order = [j for j in range(len(k_sizes)) if k_sizes[j] > 0]
+    order.sort(key=lambda j: (-float(P_row[j]), j))
+    Ps = np.array([float(P_row[j]) for j in order])
+    cum = np.concatenate([[0.0], np.cumsum(Ps)])
+    T = int(np.asarray(mask_row)[order].sum())
+    if p >= 1.0 or T == 0:
+        return False
+    near = abs(cum[T] - p) <= tol or abs(cum[T - 1] - p) <= tol
+    if T < len(order):
+        near = near or Ps[T] >= (1.0 - tol) * Ps[T - 1]
+    return bool(near)
+
+
+def check_topp_masks(mask_gpu, P_o, mask_o, k_sizes, p, max_rows=None):
+    """GPU top-p masks from the GPU's own shares: rows may differ from the
+    oracle's only where the oracle's boundary is a near tie, and then in at most
+    four clusters.  Returns the rows that differ."""
+    rows = np.flatnonzero((np.asarray(mask_gpu) != np.asarray(mask_o)).any(axis=1))
+    for i in rows:
+        assert topp_near_tie_row(P_o[i], k_sizes, mask_o[i], p), i
+        assert (mask_gpu[i] != mask_o[i]).sum() <= 4, i
+    if max_rows is not None:
+        assert rows.size <= max_rows, rows
+    return rows
+
+
+def check_ratio_masks(mask_gpu, r_o, mask_o, rows=None, rel=4e-3):
+    """Masks filled from the GPU's own ratios may differ from the oracle's only
+    at ratio near-ties with the row's selection threshold."""
+    rowmax = r_o.max(axis=1).astype(np.float64)
+    diff_rows = np.flatnonzero((np.asarray(mask_gpu) != np.asarray(mask_o)).any(axis=1))
+    n = 0
+    for i in diff_rows:
+        if rows is not None and i not in rows:
+            continue
+        thr = r_o[i][mask_o[i] == 1].min()
+        diff = np.flatnonzero(mask_gpu[i] != mask_o[i])
+        n += diff.size
+        assert np.all(np.abs(r_o[i][diff] - thr) <= rel * thr + 1e-7 * rowmax[i]), (i, diff)
+    return n

@@ -28,7 +28,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared()
-    assert len(names) == 12
+    assert len(names) == 13
     for n in names:
         assert hasattr(lib, n), n
     from sparse_attention_video_amd import svgear
@@ -93,6 +93,17 @@ def test_route_and_attn_validation(lib):
     assert V(0, F, 1.0) == 3                 # valid so far, no workspace
     assert lib.svgear_centroid_variances(F, 0, 1, 1, 100, 64, 4, F, F, None, F, None, 0, None) == 1
     assert lib.svgear_centroid_variances(F, 0, 1, 1, 100, 64, 4, F, F, F, F, None, 0, None) == 3
+    # top-p routing: p in (0, 1], error_ranked in {0, 1}, ratios only with error ranking
+    T = lambda p, er, scores_in=None, mask=F, k_perm=F: lib.svgear_route_topp(
+        F, F, 4, k_perm, F, 0, F, F, F, 8, 1, 1, 100, 64, ctypes.c_float(0.125), ctypes.c_float(p), er, None,
+        scores_in, None, None, None, mask, None, 0, None)
+    assert T(0.0, 1) == 1 and T(1.5, 1) == 1 and T(float("nan"), 0) == 1
+    assert T(0.9, 2) == 1                    # error_ranked not 0/1
+    assert T(0.9, 0, scores_in=F) == 1       # ratios with the score router
+    assert T(0.9, 1, mask=None) == 1         # no mask
+    assert T(0.9, 1, k_perm=None) == 1       # the probe needs the keys
+    assert T(0.9, 0, k_perm=None) == 3       # the score router does not; no workspace
+    assert T(1.0, 1) == 3
 
 
 def test_fault_injection_returns_injected_without_work():

@@ -29,7 +29,8 @@ import torch
 
 from oracle import svgear_oracle as orc
 from synth.gen import WORKLOADS, head_inputs
-from tests.helpers import check_labels_near_ties, f32, host, i32, mean_bound, to_dev
+from tests.helpers import (check_labels_near_ties, check_ratio_masks, check_topp_masks, f32, host, i32, mean_bound,
+                           to_dev)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 
@@ -385,3 +386,50 @@ def test_full_attention_variance_corrected(sv):
     O, LSE = orc.attend(x["q"], x["k"], x["v"], ref["pq"], ref["oq"], ref["pk"], ref["ok"], ref["kbar"],
                         ref["vbar"], ref["mask"], ref["scale"], rows=rows, kvar=kvar_h, strength=1.0)
     check_attention_rows(w, h, out, lse, O, LSE, rows)
+
+
+def test_full_route_topp(sv):
+    """SVG2 top-p budget at the Wan layer size (p = 0.9, the budget the blog
+    quotes, and 0.5): shares within fp32 rounding, masks and budgets exact
+    from the oracle's shares and ratios, both routers; then attention on the
+    error-ranked top-p mask."""
+    w, h, dev, x, L, cq, ck, ref = full_case(sv, "wan")
+    t = teacher_forced_device(w, h, dev, x, L, ref)
+    b, hh = bh_index(w, h)
+    sc = ref["scale"]
+    qs, ks = np.diff(ref["oq"]), np.diff(ref["ok"])
+    P_o = orc.topp_probs(ref["qbar"], ref["kbar"], ks, sc)
+    P_o[qs == 0] = 0.0
+    args = (t["qm"], t["oq"], t["kp"], t["vp"], t["km"], t["vm"], t["ok"], sc)
+    zeros = lambda: torch.zeros((w.B, w.H, w.Cq, w.Ck), dtype=torch.float32, device="cuda")
+    pin, rin = forced(zeros(), w, h, f32(P_o)), forced(zeros(), w, h, f32(ref["ratio"]))
+    for p in (0.9, 0.5):
+        tm_o = orc.topp_select(P_o, qs, ks, p)
+        b_o = orc.topp_budgets(tm_o, ks)
+        m1_o = orc.select_budgets(ref["ratio"], qs, ks, b_o)
+        probs, _, bud0, m0 = sv.route_topp(*args, p, error_ranked=False)
+        _, _, bud1, m1 = sv.route_topp(*args, p, error_ranked=True)
+        probs, bud0, m0, bud1, m1 = (host(a[b, hh]) for a in (probs, bud0, m0, bud1, m1))
+        assert (np.abs(probs - P_o) <= 1e-4 * P_o + 1e-37).all(), np.abs(probs - P_o).max()
+        diff_rows = check_topp_masks(m0, P_o, tm_o, ks, p, max_rows=2)
+        same = np.setdiff1d(np.arange(w.Cq), diff_rows)
+        np.testing.assert_array_equal(bud0[same], b_o[same])
+        np.testing.assert_array_equal(bud1, bud0)
+        nd = check_ratio_masks(m1, ref["ratio"], m1_o, rows=same)
+        _, _, bud2, m2 = sv.route_topp(*args, p, error_ranked=False, probs_in=pin)
+        _, _, bud3, m3 = sv.route_topp(*args, p, error_ranked=True, probs_in=pin, scores_in=rin)
+        np.testing.assert_array_equal(host(m2[b, hh]), tm_o)
+        np.testing.assert_array_equal(host(bud2[b, hh]), b_o)
+        np.testing.assert_array_equal(host(bud3[b, hh]), b_o)
+        np.testing.assert_array_equal(host(m3[b, hh]), m1_o)
+        dens = lambda m: float((qs * (m.astype(np.int64) * ks[None, :]).sum(1)).sum()) / float(w.N) ** 2
+        say(f"wan: top-p {p}: realised density score-ranked {dens(tm_o):.4f}, error-ranked {dens(m1_o):.4f}; "
+            f"{diff_rows.size} near-tie rows, {nd} near-tie blocks")
+        if p == 0.9:
+            mask = forced(L.mask, w, h, torch.from_numpy(m1_o.astype(np.uint8)).cuda())
+            out, lse = sv.sparse_attn(t["qp"], t["kp"], t["vp"], t["pq"], t["oq"], t["ok"], t["km"], t["vm"],
+                                      mask, sc, want_lse=True)
+            rows = ref["rows"]
+            O, LSE = orc.attend(x["q"], x["k"], x["v"], ref["pq"], ref["oq"], ref["pk"], ref["ok"],
+                                ref["kbar"], ref["vbar"], m1_o, sc, rows=rows)
+            check_attention_rows(w, h, out, lse, O, LSE, rows)

@@ -17,7 +17,8 @@ import torch
 
 from oracle import svgear_oracle as orc
 from synth.gen import WORKLOADS, layer_inputs, scaled
-from tests.helpers import check_labels_near_ties, f32, host, i32, mean_bound, to_dev
+from tests.helpers import (check_labels_near_ties, check_ratio_masks, check_topp_masks, f32, host, i32, mean_bound,
+                           to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -360,3 +361,117 @@ def test_sparse_attn_variance_strength_zero_is_plain(sv, ref_cache):
     plain, _ = sv.sparse_attn(*dev, sc)
     zero, _ = sv.sparse_attn(*dev, sc, k_vars=f32(reshape4(kvar, w)), strength=0.0)
     assert torch.equal(plain, zero)
+
+
+# ------------------------------------------------------------------ top-p budget (SVG2) routing
+def topp_oracle(qbar, oq, kbar, ok, sc, p):
+    qs, ks = np.diff(oq), np.diff(ok)
+    P = orc.topp_probs(qbar, kbar, ks, sc)
+    P[qs == 0] = 0.0
+    tm = orc.topp_select(P, qs, ks, p)
+    return P, tm, orc.topp_budgets(tm, ks)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("p", [0.5, 0.9, 1.0])
+def test_route_topp_teacher_forced(sv, name, p, ref_cache):
+    """Shares within fp32 rounding of the oracle's; given the oracle's float32
+    shares and ratios, masks and budgets are bit-exact in both modes."""
+    w, x, outs, sc = oracle_layer(name, ref_cache)
+    BH = w.B * w.H
+    g = lambda key: np.stack([o[key] for o in outs])
+    pk = g("pk")
+    Kp = np.stack([x["k"][h][pk[h]] for h in range(BH)])
+    Vp = np.stack([x["v"][h][pk[h]] for h in range(BH)])
+    qbar, kbar, vbar, oq, ok, r_all = g("qbar"), g("kbar"), g("vbar"), g("oq"), g("ok"), g("ratio")
+    args = (f32(reshape4(qbar, w)), i32(reshape4(oq, w)), to_dev(reshape4(Kp, w), w.dtype),
+            to_dev(reshape4(Vp, w), w.dtype), f32(reshape4(kbar, w)), f32(reshape4(vbar, w)), i32(reshape4(ok, w)))
+    ref = [topp_oracle(qbar[h], oq[h], kbar[h], ok[h], sc, p) for h in range(BH)]
+    P_all = np.stack([t[0] for t in ref])
+    shp = lambda t: host(t).reshape(BH, *t.shape[2:])
+    # the GPU's own shares
+    probs, _, bud0, m0 = sv.route_topp(*args, sc, p, error_ranked=False)
+    probs1, scores1, bud1, m1 = sv.route_topp(*args, sc, p, error_ranked=True, want_scores=True)
+    probs, probs1, bud0, bud1, m0, m1 = map(shp, (probs, probs1, bud0, bud1, m0, m1))
+    scores1 = shp(scores1)
+    np.testing.assert_array_equal(probs, probs1)
+    np.testing.assert_array_equal(bud0, bud1)
+    for h in range(BH):
+        P_o, tm_o, b_o = ref[h]
+        ks, qs = np.diff(ok[h]), np.diff(oq[h])
+        assert (np.abs(probs[h] - P_o) <= 1e-4 * P_o + 1e-37).all(), np.abs(probs[h] - P_o).max()
+        diff_rows = check_topp_masks(m0[h], P_o, tm_o, ks, p)
+        same = np.setdiff1d(np.arange(w.Cq), diff_rows)
+        np.testing.assert_array_equal(bud0[h][same], b_o[same])
+        np.testing.assert_array_equal(bud0[h], (m0[h].astype(np.int64) * ks).sum(axis=1))
+        m1_o = orc.select_budgets(r_all[h], qs, ks, b_o)
+        check_ratio_masks(m1[h], r_all[h], m1_o, rows=same)
+    # bit-exact from the oracle's float32 shares and ratios
+    pin, rin = f32(reshape4(P_all, w)), f32(reshape4(r_all, w))
+    probs2, _, bud2, m2 = sv.route_topp(*args, sc, p, error_ranked=False, probs_in=pin)
+    _, _, bud3, m3 = sv.route_topp(*args, sc, p, error_ranked=True, probs_in=pin, scores_in=rin)
+    probs2, bud2, m2, bud3, m3 = map(shp, (probs2, bud2, m2, bud3, m3))
+    np.testing.assert_array_equal(probs2, P_all)
+    for h in range(BH):
+        P_o, tm_o, b_o = ref[h]
+        qs, ks = np.diff(oq[h]), np.diff(ok[h])
+        np.testing.assert_array_equal(m2[h], tm_o)
+        np.testing.assert_array_equal(bud2[h], b_o)
+        np.testing.assert_array_equal(bud3[h], b_o)
+        np.testing.assert_array_equal(m3[h], orc.select_budgets(r_all[h], qs, ks, b_o))
+        if p == 1.0:
+            assert (m2[h][qs > 0][:, ks > 0] == 1).all()
+
+
+def test_route_topp_hand_example(sv):
+    """Hand-built shares with ties, an empty key cluster and an empty query
+    cluster, in both modes, against the oracle's selection."""
+    N, Cq, Ck = 10, 3, 5
+    ok = np.array([[[0, 3, 4, 4, 8, 10]]], dtype=np.int32)        # sizes 3, 1, 0, 4, 2
+    oq = np.array([[[0, 6, 6, 10]]], dtype=np.int32)              # query cluster 1 is empty
+    P = np.array([[[[0.25, 0.5, 0.0, 0.125, 0.125], [0.2, 0.2, 0.0, 0.3, 0.3],
+                    [0.1, 0.1, 0.0, 0.1, 0.7]]]], dtype=np.float32)
+    r = np.array([[[[0.5, 0.9, 0.0, 0.7, 0.1], [1, 1, 0, 1, 1], [0.3, 0.2, 0.0, 0.1, 0.0]]]], dtype=np.float32)
+    kp = torch.zeros((1, 1, N, 64), dtype=torch.float32, device="cuda")
+    qs, ks = np.diff(oq[0, 0]), np.diff(ok[0, 0])
+    for p in (0.5, 0.6, 0.8, 1.0):
+        probs, _, bud, m = sv.route_topp(None, i32(oq), kp, None, None, None, i32(ok), 0.125, p,
+                                         error_ranked=False, probs_in=f32(P))
+        tm = orc.topp_select(P[0, 0], qs, ks, p)
+        np.testing.assert_array_equal(host(m)[0, 0], tm)
+        np.testing.assert_array_equal(host(bud)[0, 0], orc.topp_budgets(tm, ks))
+        assert host(m)[0, 0][1].sum() == 0 and host(bud)[0, 0][1] == 0
+        _, _, bud1, m1 = sv.route_topp(None, i32(oq), kp, None, None, None, i32(ok), 0.125, p,
+                                       error_ranked=True, probs_in=f32(P), scores_in=f32(r))
+        np.testing.assert_array_equal(host(m1)[0, 0], orc.select_budgets(r[0, 0], qs, ks, orc.topp_budgets(tm, ks)))
+    # p = 0.8.  Row 0: order 1 (0.5), 0 (0.25), then 3 and 4 tie at 0.125 and 3 goes
+    # first; 0.875 >= 0.8 stops before 4.  Row 2: float32 0.7 + 0.1 summed in double
+    # is 0.79999999, below float32 0.8 (0.80000001), so a second 0.1 share is taken.
+    _, _, _, m = sv.route_topp(None, i32(oq), kp, None, None, None, i32(ok), 0.125, 0.8, error_ranked=False,
+                               probs_in=f32(P))
+    assert host(m)[0, 0].tolist() == [[1, 1, 0, 1, 0], [0, 0, 0, 0, 0], [1, 1, 0, 0, 1]]
+
+
+@pytest.mark.parametrize("name", ["bf16-d128"])
+def test_route_topp_then_attention(sv, name, ref_cache):
+    """The top-p masks drive the same attention kernel: output within the bf16
+    tolerance of the oracle attending with the oracle's top-p mask."""
+    w, x, outs, sc = oracle_layer(name, ref_cache)
+    BH = w.B * w.H
+    g = lambda key: np.stack([o[key] for o in outs])
+    qbar, kbar, oq, ok, r_all = g("qbar"), g("kbar"), g("oq"), g("ok"), g("ratio")
+    masks = []
+    for h in range(BH):
+        P_o, _, b_o = topp_oracle(qbar[h], oq[h], kbar[h], ok[h], sc, 0.9)
+        masks.append(orc.select_budgets(r_all[h], np.diff(oq[h]), np.diff(ok[h]), b_o))
+    m = np.stack(masks)
+    dev, m = attn_inputs(w, x, outs, m)
+    out, _ = sv.sparse_attn(*dev, sc)
+    out = host(out).reshape(BH, w.N, w.D)
+    amax, amean = ATOL[w.dtype]
+    for h in range(BH):
+        o = outs[h]
+        O, _ = orc.attend(x["q"][h], x["k"][h], x["v"][h], o["pq"], o["oq"], o["pk"], o["ok"], o["kbar"], o["vbar"],
+                          m[h], sc)
+        err = np.abs(out[h] - O)
+        assert err.max() <= amax and err.mean() <= amean, (err.max(), err.mean())
