@@ -53,6 +53,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--attn-only", action="store_true", help="after one layer, time only the attention pass")
     ap.add_argument("--attn-reps", type=int, default=5)
+    ap.add_argument("--no-variants", action="store_true", help="skip the variant-path timings")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="first run a plain device copy of this many MiB (calibrates HBM byte counters)")
     return ap.parse_args()
@@ -116,6 +117,41 @@ def cpu_baseline(w, h0, scale):
             "sample": f"1 of {heads} heads in full ({w.iters} Lloyd rounds of Q and K, permute, means, route, "
                       f"attention for all {w.N} rows), scaled x{heads}",
             "measured_s": round(sec, 2)}
+
+
+def variants(sv, L, w, k, scale, ev, reps=5, top_p=0.9):
+    """Timings of the variant paths on the same layer state (outside the step):
+    routing under the SVG2 top-p budget (both rankers) with the density each
+    realises, and variance-corrected compensation (key variances + attention)."""
+    import torch
+
+    def timed(fn):
+        fn()
+        a, b = ev(), ev()
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            out = fn()
+        b.record()
+        torch.cuda.synchronize()
+        return round(a.elapsed_time(b) / reps, 3), out
+
+    qoff, koff = L.oq.cpu().numpy(), L.ok.cpu().numpy()
+    res = {"top_p": top_p}
+    for name, er in (("route_topp_error_ranked", True), ("route_topp_score_ranked", False)):
+        t, (_, _, _, mask) = timed(lambda: sv.route_topp(L.qm, L.oq, L.kp, L.vp, L.km, L.vm, L.ok, scale, top_p,
+                                                         error_ranked=er, want_probs=False, want_budget=False,
+                                                         ws=L.ws))
+        _, sel, _ = algorithmic_flops(mask.cpu().numpy(), qoff, koff, w.D)
+        res[name] = {"ms": t, "realized_density": round(sel / (w.B * w.H * float(w.N) ** 2), 4)}
+    if w.dtype == "bf16":
+        kv = torch.empty_like(L.km)
+        t_var, _ = timed(lambda: sv.centroid_variances(k, L.pk, L.ok, L.km, vars=kv, ws=L.ws))
+        t_att, _ = timed(lambda: sv.sparse_attn(L.qp, L.kp, L.vp, L.pq, L.oq, L.ok, L.km, L.vm, L.mask, scale,
+                                                out=L.out, ws=L.ws, k_vars=kv, strength=1.0))
+        res["centroid_variances_k"] = {"ms": t_var}
+        res["sparse_attn_variance_corrected"] = {"ms": t_att, "strength": 1.0}
+    return res
 
 
 def main():
@@ -242,6 +278,8 @@ def main():
         "realized_density": round(pairs_sel / (BH * float(w.N) ** 2), 4),
         "pseudo_pair_fraction": round(pairs_comp / max(1, pairs_sel + pairs_comp), 4),
     }
+    if not args.attn_only and not args.no_variants:
+        res["variants"] = variants(sv, L, w, k, scale, ev)
     if not args.no_cpu_baseline and not args.attn_only:
         print("# timing the oracle on the host", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, h0, scale)

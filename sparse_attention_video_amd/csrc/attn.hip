@@ -583,12 +583,14 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
       rowoff[i] = (uint32_t)(p < nkeys ? tc_base + (p - tc_pre) : 0) * (uint32_t)ROWB;
     }
   };
+  // a 32-bit per-lane offset from the head's base keeps the loads in the
+  // scalar-base form (4 address bytes per lane instead of 8)
   auto issue = [&](const uint32_t* rowoff, char* dK, char* dV) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int g = w * NI + i;
-      load_lds16(kb + rowoff[i] + (chK[i] << 4), dK + g * 1024);
-      load_lds16(vb + rowoff[i] + (chV << 4), dV + g * 1024);
+      load_lds16(kb + (uint32_t)(rowoff[i] + (uint32_t)(chK[i] << 4)), dK + g * 1024);
+      load_lds16(vb + (uint32_t)(rowoff[i] + (uint32_t)(chV << 4)), dV + g * 1024);
     }
   };
 
