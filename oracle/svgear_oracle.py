@@ -44,6 +44,13 @@ the per-coordinate population variance of the cluster's keys.  ``variances``
 and the ``kvar`` / ``strength`` arguments of ``attend`` implement it;
 strength 0 is the plain method.
 
+k-means++ seeding (SVG2 summary, "Efficient System-Algorithm Co-Design"):
+``kmeanspp`` draws cold-start centroids by D^2 sampling from caller-given
+uniform 64-bit words.  Readings: squared distances summed in coordinate
+order in float64 without fused operations, sampling weights floor(D^2 2^k)
+as exact integers, inverse-CDF draws, uniform fallback once every distance
+is 0.
+
 Top-p budget (SVG2 summary, "Centroid-Based Top-p Selection"; FrontierCS
 blog, budget paragraph): ``topp_probs`` estimates each block's share P' of
 the attention mass from the centroids, ``topp_select`` is SVG2's own router
@@ -52,6 +59,8 @@ error_ranked=True gives each query cluster that selection's keys as its
 budget and spends them by error per pair instead of a fixed density.
 """
 from __future__ import annotations
+
+import math
 
 import numpy as np
 
@@ -107,6 +116,75 @@ def lloyd(X: np.ndarray, C0: np.ndarray, iters: int):
         labels = assign(X, C)
         C = update(X, labels, C)
     return C, labels
+
+
+# --------------------------------------------------------------------------
+# 1b. k-means++ cold seeding (SVG2 summary, "Efficient System-Algorithm
+#     Co-Design": a cold start uses k-means++ initialisation)
+# --------------------------------------------------------------------------
+def sqdist_seq(X: np.ndarray, c: np.ndarray) -> np.ndarray:
+    """Squared distance of every row of X to c, summed over the coordinates in
+    index order in float64, one rounding per product and one per sum (no fused
+    multiply-add).  The seeding's random choices depend on these values, so the
+    order of operations is fixed here and on the GPU alike."""
+    X = np.asarray(X, F64)
+    c = np.asarray(c, F64)
+    acc = np.zeros(X.shape[0], F64)
+    for d in range(X.shape[1]):
+        diff = X[:, d] - c[d]
+        acc = acc + diff * diff
+    return acc
+
+
+def pp_scale(d2_first: np.ndarray) -> int:
+    """Exponent k of the fixed-point sampling weights floor(D^2 * 2^k): the
+    largest k with N * max D^2 * 2^k < 2^62, taken from the distances to the
+    first seed (later distances only shrink, so every later sum fits)."""
+    m = float(np.max(d2_first))
+    if m == 0.0:
+        return 0
+    _, e = math.frexp(float(len(d2_first)) * m)     # N * m < 2^e
+    return 62 - e
+
+
+def pp_weights(d2: np.ndarray, k: int) -> np.ndarray:
+    """D^2 as exact non-negative integers floor(D^2 * 2^k) (uint64)."""
+    return np.floor(np.ldexp(np.asarray(d2, F64), k)).astype(np.uint64)
+
+
+def pp_draw(weights: np.ndarray, word: int):
+    """Index drawn with probability weight / total by inverting the cumulative
+    sum at target = floor(word * total / 2^64), word a uniform 64-bit integer:
+    the first index whose inclusive prefix exceeds the target.  None when every
+    weight is 0."""
+    total = int(np.sum(weights, dtype=np.uint64))
+    if total == 0:
+        return None
+    target = (int(word) * total) >> 64
+    cum = np.cumsum(weights, dtype=np.uint64)
+    return int(np.searchsorted(cum, np.uint64(target), side="right"))
+
+
+def kmeanspp(X: np.ndarray, words: np.ndarray, C: int):
+    """k-means++ seeds (D^2 sampling): the first seed is token
+    floor(words[0] * N / 2^64); each later seed c is drawn with probability
+    proportional to the squared distance to the nearest seed so far, using
+    words[c].  When every remaining distance is 0 (fewer distinct rows than
+    seeds) the draw falls back to the uniform rule.  Returns (seeds as float64
+    rows [C, D], their token indices [C])."""
+    X = np.asarray(X, F64)
+    N = X.shape[0]
+    chosen = [(int(words[0]) * N) >> 64]
+    d2 = sqdist_seq(X, X[chosen[0]])
+    k = pp_scale(d2)
+    for c in range(1, C):
+        t = pp_draw(pp_weights(d2, k), int(words[c]))
+        if t is None:
+            t = (int(words[c]) * N) >> 64
+        chosen.append(t)
+        d2 = np.minimum(d2, sqdist_seq(X, X[t]))
+    idx = np.asarray(chosen, dtype=np.int64)
+    return X[idx].copy(), idx
 
 
 def inertia(X: np.ndarray, C: np.ndarray, labels: np.ndarray) -> float:

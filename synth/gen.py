@@ -23,6 +23,8 @@ Recipe, per head h with ``r = numpy.random.default_rng([seed, h])``:
   C distinct token rows, r.choice(N, C, replace=False), one draw each for Q and
   K.  The denoising-step sequence drifts the means by 0.02 N(0, 1) per step
   (draws from default_rng([seed, h, step])) with labels and noise fixed.
+  The words a k-means++ seeding consumes (one uniform 64-bit integer per
+  seed) come from default_rng([seed, h, 11, 0 for Q / 1 for K]).
 """
 from __future__ import annotations
 
@@ -155,6 +157,13 @@ def head_inputs(w: Workload, bh: int, step: int = 0):
         "ck0": k[d.init_k].astype(np.float32),
         "labels_q": d.a, "labels_k": d.b,   # generating components (diagnostics only)
     }
+
+
+def seed_words(w: Workload, bh: int, which: str, C: int) -> np.ndarray:
+    """C uniform 64-bit words for the k-means++ seeding of one head's Q
+    (which = "q") or K ("k"), from default_rng([seed, bh, 11, 0 or 1])."""
+    r = np.random.default_rng([w.seed, bh, 11, 0 if which == "q" else 1])
+    return r.integers(0, np.iinfo(np.uint64).max, size=C, dtype=np.uint64, endpoint=True)
 
 
 def layer_inputs(w: Workload, heads: Optional[Sequence[int]] = None, step: int = 0):

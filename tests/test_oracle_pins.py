@@ -566,3 +566,77 @@ def test_route_topp_budgets_and_bounds():
             assert (bud >= prev).all()
         prev = bud
     assert (prev == 512).all()
+
+
+# ---------------------------------------------------------------- k-means++ seeding
+def test_kmeanspp_hand_example():
+    """Integer points, so every distance and weight is exact: (0,0), (1,0),
+    (0,2), (3,0).  Word 0 picks token 0; D^2 = (0, 1, 4, 9) with cumulative
+    (0, 1, 5, 14); a word of 2^62 targets 14/4 = 3.5, which falls in token 2's
+    range [1, 5); then D^2 = (0, 1, 0, 9), cumulative (0, 1, 1, 10), and 2^63
+    targets 5, in token 3's range [1, 10)."""
+    X = np.array([[0, 0], [1, 0], [0, 2], [3, 0]], float)
+    seeds, idx = orc.kmeanspp(X, np.array([0, 2**62, 2**63], dtype=np.uint64), 3)
+    assert idx.tolist() == [0, 2, 3]
+    np.testing.assert_array_equal(seeds, X[[0, 2, 3]])
+    # the edges of the ranges: 2^60 targets 0.875 (token 1), the largest word
+    # targets just below 14 (token 3); the first seed takes floor(word * N / 2^64)
+    assert orc.kmeanspp(X, np.array([0, 2**60], dtype=np.uint64), 2)[1].tolist() == [0, 1]
+    assert orc.kmeanspp(X, np.array([0, 2**64 - 1], dtype=np.uint64), 2)[1].tolist() == [0, 3]
+    assert orc.kmeanspp(X, np.array([3 * 2**62, 0], dtype=np.uint64), 2)[1].tolist() == [3, 0]
+
+
+def test_kmeanspp_distance_order_and_scale():
+    rng = np.random.default_rng(31)
+    X = rng.standard_normal((300, 24))
+    c = X[17]
+    from scipy.spatial.distance import cdist
+    d2 = orc.sqdist_seq(X, c)
+    np.testing.assert_allclose(d2, cdist(X, c[None], "sqeuclidean")[:, 0], rtol=1e-13, atol=0)
+    k = orc.pp_scale(d2)
+    assert len(d2) * d2.max() * 2.0**k < 2.0**62 <= 2 * len(d2) * d2.max() * 2.0**k
+    w = orc.pp_weights(d2, k)
+    assert int(np.sum(w, dtype=np.uint64)) < 2**62 and w[17] == 0
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_kmeanspp_picks_one_point_per_separated_blob(seed):
+    """Eight tight blobs 100 apart: D^2 sampling lands in a new blob at every
+    step with probability > 1 - 1e-4, whereas uniform picks would repeat a blob
+    with probability 1 - 8!/8^8 > 0.99."""
+    rng = np.random.default_rng(200 + seed)
+    centers = 100.0 * np.eye(8)
+    X = np.concatenate([ctr + 0.01 * rng.standard_normal((20, 8)) for ctr in centers])
+    words = rng.integers(0, np.iinfo(np.uint64).max, size=8, dtype=np.uint64, endpoint=True)
+    _, idx = orc.kmeanspp(X, words, 8)
+    assert sorted((idx // 20).tolist()) == list(range(8))
+
+
+def test_kmeanspp_distinct_rows_are_each_taken_once_and_duplicates_fall_back():
+    rng = np.random.default_rng(5)
+    X = rng.standard_normal((12, 4))
+    words = rng.integers(0, np.iinfo(np.uint64).max, size=12, dtype=np.uint64, endpoint=True)
+    assert sorted(orc.kmeanspp(X, words, 12)[1].tolist()) == list(range(12))
+    # three distinct rows, four copies each: the first three seeds cover them,
+    # then every distance is 0 and the draw is uniform: floor(word * N / 2^64)
+    Y = np.repeat(rng.standard_normal((3, 4)), 4, axis=0)
+    words = np.array([0, 2**63, 2**62, 2**63 + 5, 2**62 * 3], dtype=np.uint64)
+    seeds, idx = orc.kmeanspp(Y, words, 5)
+    assert sorted({int(i) // 4 for i in idx[:3]}) == [0, 1, 2]
+    assert idx[3] == ((2**63 + 5) * 12) >> 64 and idx[4] == (3 * 2**62 * 12) >> 64
+
+
+def test_kmeanspp_second_seed_follows_the_d2_law():
+    """Frequencies of the second seed over many words against D^2 / sum D^2
+    (distances from scipy), within five binomial standard deviations."""
+    from scipy.spatial.distance import cdist
+    X = np.array([[0.0, 0.0], [1.0, 0.5], [2.0, -1.0], [0.3, 0.3], [-1.5, 2.0]])
+    p = cdist(X, X[:1], "sqeuclidean")[:, 0]
+    p = p / p.sum()
+    rng = np.random.default_rng(8)
+    n = 6000
+    counts = np.zeros(5)
+    for wd in rng.integers(0, np.iinfo(np.uint64).max, size=n, dtype=np.uint64, endpoint=True):
+        counts[orc.kmeanspp(X, np.array([0, wd], dtype=np.uint64), 2)[1][1]] += 1
+    assert counts[0] == 0
+    assert np.all(np.abs(counts / n - p) <= 5 * np.sqrt(p * (1 - p) / n) + 1e-12)
