@@ -119,10 +119,11 @@ def cpu_baseline(w, h0, scale):
             "measured_s": round(sec, 2)}
 
 
-def variants(sv, L, w, k, scale, ev, reps=5, top_p=0.9):
+def variants(sv, L, w, q, k, scale, ev, reps=5, top_p=0.9):
     """Timings of the variant paths on the same layer state (outside the step):
     routing under the SVG2 top-p budget (both rankers) with the density each
-    realises, and variance-corrected compensation (key variances + attention)."""
+    realises, k-means++ cold seeding of Q and K, and variance-corrected
+    compensation (key variances + attention)."""
     import torch
 
     def timed(fn):
@@ -144,6 +145,21 @@ def variants(sv, L, w, k, scale, ev, reps=5, top_p=0.9):
                                                          ws=L.ws))
         _, sel, _ = algorithmic_flops(mask.cpu().numpy(), qoff, koff, w.D)
         res[name] = {"ms": t, "realized_density": round(sel / (w.B * w.H * float(w.N) ** 2), 4)}
+    # k-means++ cold seeding of Q and K (one call each, every head)
+    from synth.gen import seed_words
+    for which, x, C in (("q", q, w.Cq), ("k", k, w.Ck)):
+        words = np.stack([seed_words(w, i, which, C) for i in range(w.B * w.H)])
+        wd = torch.from_numpy(words.view(np.int64)).reshape(w.B, w.H, C).to(x.device)
+        cent = torch.empty((w.B, w.H, C, w.D), dtype=torch.float32, device=x.device)
+        chosen = torch.empty((w.B, w.H, C), dtype=torch.int32, device=x.device)
+        sv.kmeanspp(x, wd, C, centroids=cent, chosen=chosen)
+        a, b = ev(), ev()
+        torch.cuda.synchronize()
+        a.record()
+        sv.kmeanspp(x, wd, C, centroids=cent, chosen=chosen)
+        b.record()
+        torch.cuda.synchronize()
+        res[f"kmeanspp_{which}"] = {"ms": round(a.elapsed_time(b), 3), "seeds": C}
     if w.dtype == "bf16":
         kv = torch.empty_like(L.km)
         t_var, _ = timed(lambda: sv.centroid_variances(k, L.pk, L.ok, L.km, vars=kv, ws=L.ws))
@@ -279,7 +295,7 @@ def main():
         "pseudo_pair_fraction": round(pairs_comp / max(1, pairs_sel + pairs_comp), 4),
     }
     if not args.attn_only and not args.no_variants:
-        res["variants"] = variants(sv, L, w, k, scale, ev)
+        res["variants"] = variants(sv, L, w, q, k, scale, ev)
     if not args.no_cpu_baseline and not args.attn_only:
         print("# timing the oracle on the host", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(w, h0, scale)

@@ -31,8 +31,9 @@
  *     non-OK status.  No call aborts or throws.
  *   - Results are bitwise deterministic run to run (no float atomics).
  *   - Setting the environment variable SVGEAR_FAULT to one of kmeans,
- *     centroids, route, attn makes that call return SVGEAR_ERR_INJECTED
- *     without queuing work (for testing a caller's dense fallback).
+ *     kmeanspp, centroids, centroid_variances, route, route_topp, attn makes
+ *     that call return SVGEAR_ERR_INJECTED without queuing work (for testing
+ *     a caller's dense fallback; attn covers both attention entry points).
  */
 #ifndef SVGEAR_H
 #define SVGEAR_H
@@ -117,6 +118,39 @@ size_t svgear_centroids_workspace(int B, int H, int N, int D, int C);
 svgear_status svgear_centroids(const void* x, svgear_dtype dt, int B, int H, int N, int D, int C,
                                const int32_t* perm, const int32_t* offsets, void* x_perm,
                                float* means, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * svgear_kmeanspp -- k-means++ cold seeding (D^2 sampling) of C centroids
+ * per (batch, head), for a cold svgear_kmeans start.
+ *
+ * SVG2 summary, "Efficient System-Algorithm Co-Design": without a cached
+ * start, k-means begins from k-means++ initial centroids.  Seed 0 is uniform;
+ * each later seed is drawn with probability proportional to the squared
+ * distance to the nearest seed so far.  The randomness is the caller's: one
+ * uniform 64-bit word per seed.
+ *
+ * Exact rules (so that any implementation following them picks the same
+ * tokens): D^2 is summed over the coordinates in index order in fp64 with one
+ * rounding per product and per sum; the weights are floor(D^2 * 2^k) as
+ * uint64, k the largest integer with N * max D^2 * 2^k < 2^62 for the
+ * distances to seed 0; seed c (c >= 1) is the first token whose inclusive
+ * prefix of weights exceeds floor(words[c] * total / 2^64); seed 0, and any
+ * seed drawn when every weight is 0 (fewer distinct rows than seeds), is
+ * token floor(words[c] * N / 2^64).  Inputs must be finite.
+ *
+ *   x          [B,H,N,D] dtype dt.
+ *   words      [B,H,C] uint64, device: uniform random words, one per seed.
+ *   centroids  [B,H,C,D] float32 OUT: the seeds' rows (exact copies).
+ *   chosen     nullable [B,H,C] int32 OUT: the seeds' token indices.
+ *   ws         at least svgear_kmeanspp_workspace(B, H, N, D) bytes
+ *              (8 bytes per token plus per-tile sums).
+ * Limits as svgear_kmeans (1 <= C <= min(N, SVGEAR_MAX_CLUSTERS)).  Launches
+ * about 2 C kernels on stream; deterministic.
+ * ---------------------------------------------------------------------- */
+size_t svgear_kmeanspp_workspace(int B, int H, int N, int D);
+svgear_status svgear_kmeanspp(const void* x, svgear_dtype dt, int B, int H, int N, int D, int C,
+                              const uint64_t* words, float* centroids, int32_t* chosen, void* ws,
+                              size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * svgear_route -- error-aware routing: probe error / block cost, greedy

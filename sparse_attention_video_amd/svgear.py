@@ -28,6 +28,7 @@ EXPORTS = (
     "svgear_sparse_attn_workspace", "svgear_sparse_attn",
     "svgear_centroid_variances", "svgear_sparse_attn_var",
     "svgear_route_topp",
+    "svgear_kmeanspp_workspace", "svgear_kmeanspp",
 )
 
 _lib = None
@@ -72,6 +73,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.svgear_sparse_attn_var.restype = I
     lib.svgear_route_topp.argtypes = [P, P, I, P, P, I, P, P, P, I, I, I, I, I, F, F, I, P, P, P, P, P, P, P, Z, P]
     lib.svgear_route_topp.restype = I
+    lib.svgear_kmeanspp_workspace.argtypes = [I, I, I, I]
+    lib.svgear_kmeanspp_workspace.restype = Z
+    lib.svgear_kmeanspp.argtypes = [P, I, I, I, I, I, I, P, P, P, P, Z, P]
+    lib.svgear_kmeanspp.restype = I
     _lib = lib
     return lib
 
@@ -192,6 +197,24 @@ def route(q_means, q_offsets, k_perm, v_perm, k_means, v_means, k_offsets, scale
                                             _ptr(scores if want_scores else None), _ptr(mask), _ptr(ws), ws.numel(),
                                             _stream(dev)))
     return (scores if want_scores else None), mask
+
+
+def kmeanspp(x: torch.Tensor, words: torch.Tensor, C: int, centroids=None, chosen=None, ws=None):
+    """k-means++ seeds from one uniform 64-bit word per seed (words: [B,H,C]
+    int64 or uint64 tensor, bits taken as unsigned).  Returns (centroids
+    [B,H,C,D] fp32, chosen [B,H,C] int32)."""
+    dev = _dev(x, words)
+    B, H, N, D = x.shape
+    if tuple(words.shape) != (B, H, C) or words.element_size() != 8 or not words.is_contiguous():
+        raise ValueError("words must be a contiguous [B, H, C] tensor of 64-bit integers")
+    centroids = centroids if centroids is not None else torch.empty((B, H, C, D), dtype=torch.float32, device=dev)
+    chosen = chosen if chosen is not None else torch.empty((B, H, C), dtype=torch.int32, device=dev)
+    lib = load()
+    need = lib.svgear_kmeanspp_workspace(B, H, N, D)
+    ws = ws if ws is not None else _workspace(need, dev)
+    _check("svgear_kmeanspp", lib.svgear_kmeanspp(_ptr(x), _dtype(x), B, H, N, D, C, _ptr(words), _ptr(centroids),
+                                                  _ptr(chosen), _ptr(ws), ws.numel(), _stream(dev)))
+    return centroids, chosen
 
 
 def route_topp(q_means, q_offsets, k_perm, v_perm, k_means, v_means, k_offsets, scale: float, top_p: float,

@@ -28,7 +28,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared()
-    assert len(names) == 13
+    assert len(names) == 15
     for n in names:
         assert hasattr(lib, n), n
     from sparse_attention_video_amd import svgear
@@ -104,6 +104,11 @@ def test_route_and_attn_validation(lib):
     assert T(0.9, 1, k_perm=None) == 1       # the probe needs the keys
     assert T(0.9, 0, k_perm=None) == 3       # the score router does not; no workspace
     assert T(1.0, 1) == 3
+    # k-means++ seeding: C in [1, N], words and centroids required
+    K = lambda C, words=F, cent=F: lib.svgear_kmeanspp(F, 0, 1, 1, 100, 64, C, words, cent, None, None, 0, None)
+    assert K(0) == 1 and K(101) == 1 and K(5, words=None) == 1 and K(5, cent=None) == 1
+    assert K(5) == 3 and K(100) == 3
+    assert lib.svgear_kmeanspp_workspace(1, 40, 75600, 128) >= 40 * 75600 * 8
 
 
 def test_fault_injection_returns_injected_without_work():

@@ -433,3 +433,24 @@ def test_full_route_topp(sv):
             O, LSE = orc.attend(x["q"], x["k"], x["v"], ref["pq"], ref["oq"], ref["pk"], ref["ok"],
                                 ref["kbar"], ref["vbar"], m1_o, sc, rows=rows)
             check_attention_rows(w, h, out, lse, O, LSE, rows)
+
+
+def test_full_kmeanspp_seeding(sv):
+    """k-means++ seeds for every head of the Wan layer (C_q for Q, C_k for K);
+    the sampled head's seed indices bit-exact against the oracle."""
+    from synth.gen import seed_words
+    w, h, dev, x, L, cq, ck, ref = full_case(sv, "wan")
+    b, hh = bh_index(w, h)
+    BH = w.B * w.H
+    for which, C in (("q", w.Cq), ("k", w.Ck)):
+        words = np.stack([seed_words(w, i, which, C) for i in range(BH)])
+        wd = torch.from_numpy(words.view(np.int64)).reshape(w.B, w.H, C).cuda()
+        t0 = time.time()
+        cent, chosen = sv.kmeanspp(dev[which], wd, C)
+        torch.cuda.synchronize()
+        say(f"wan: k-means++ seeding of {which} ({C} seeds, {BH} heads) on the GPU: {time.time() - t0:.3f}s")
+        t0 = time.time()
+        seeds, idx = orc.kmeanspp(x[which], words[h], C)
+        say(f"wan: oracle seeding of head {h} ({which}): {time.time() - t0:.1f}s")
+        np.testing.assert_array_equal(host(chosen[b, hh]), idx)
+        np.testing.assert_array_equal(host(cent[b, hh]).astype(np.float64), seeds)

@@ -475,3 +475,51 @@ def test_route_topp_then_attention(sv, name, ref_cache):
                           m[h], sc)
         err = np.abs(out[h] - O)
         assert err.max() <= amax and err.mean() <= amean, (err.max(), err.mean())
+
+
+# ------------------------------------------------------------------ k-means++ seeding
+def words_dev(words, w):
+    return torch.from_numpy(np.ascontiguousarray(words).view(np.int64)).reshape(w.B, w.H, -1).cuda()
+
+
+@pytest.mark.parametrize("name", list(CASES))
+@pytest.mark.parametrize("which", ["q", "k"])
+def test_kmeanspp_matches_oracle(sv, name, which):
+    """Every seed index bit-exact (the rules fix every rounding), every seed row
+    an exact copy, over all heads, several tiles and a ragged tail."""
+    from synth.gen import seed_words
+    w, x = make(name)
+    BH = w.B * w.H
+    C = w.Cq if which == "q" else w.Ck
+    words = np.stack([seed_words(w, h, which, C) for h in range(BH)])
+    cent, chosen = sv.kmeanspp(to_dev(reshape4(x[which], w), w.dtype), words_dev(words, w), C)
+    cent, chosen = host(cent).reshape(BH, C, w.D), host(chosen).reshape(BH, C)
+    for h in range(BH):
+        seeds, idx = orc.kmeanspp(x[which][h], words[h], C)
+        np.testing.assert_array_equal(chosen[h], idx)
+        np.testing.assert_array_equal(cent[h].astype(np.float64), seeds)
+
+
+def test_kmeanspp_edge_cases(sv):
+    """One seed; as many seeds as rows (each row once); rows repeated so every
+    distance reaches 0 before the last seed (uniform fallback)."""
+    rng = np.random.default_rng(77)
+    N, D = 300, 64
+    X = rng.standard_normal((1, 1, N, D)).astype(np.float32)
+    words = rng.integers(0, np.iinfo(np.uint64).max, size=(1, 1, N), dtype=np.uint64, endpoint=True)
+    W = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int64)).cuda()
+    xd = torch.from_numpy(X).cuda()
+    for C in (1, 7, N):
+        cent, chosen = sv.kmeanspp(xd, W(words[:, :, :C]), C)
+        seeds, idx = orc.kmeanspp(X[0, 0], words[0, 0, :C], C)
+        np.testing.assert_array_equal(host(chosen)[0, 0], idx)
+        np.testing.assert_array_equal(host(cent)[0, 0].astype(np.float64), seeds)
+    assert sorted(host(chosen)[0, 0].tolist()) == list(range(N))
+    Y = np.repeat(rng.standard_normal((5, 128)).astype(np.float32), 60, axis=0)[None, None]   # N = 300
+    yb = to_dev(Y[0, 0], "bf16")[None, None]
+    Yr = host(yb)[0, 0]
+    for C in (5, 9):
+        cent, chosen = sv.kmeanspp(yb, W(words[:, :, :C]), C)
+        seeds, idx = orc.kmeanspp(Yr, words[0, 0, :C], C)
+        np.testing.assert_array_equal(host(chosen)[0, 0], idx)
+        assert len({int(i) // 60 for i in idx[:5]}) == 5
