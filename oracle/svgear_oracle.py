@@ -51,6 +51,11 @@ order in float64 without fused operations, sampling weights floor(D^2 2^k)
 as exact integers, inverse-CDF draws, uniform fallback once every distance
 is 0.
 
+FP8 variant (SVG2 summary, results: SVG2 + FP8): ``quantize_e4m3`` gives a
+slice's e4m3fn codes and power-of-two scale; the FP8 attention is ``attend``
+on the dequantized Q and K (the products of the exact blocks then equal the
+kernel's e4m3 products), with the values and the cluster means unquantized.
+
 Top-p budget (SVG2 summary, "Centroid-Based Top-p Selection"; FrontierCS
 blog, budget paragraph): ``topp_probs`` estimates each block's share P' of
 the attention mass from the centroids, ``topp_select`` is SVG2's own router
@@ -537,6 +542,40 @@ def attend_bruteforce(Q, K, V, q_labels, k_labels, kbar, vbar, mask, scale):
         w = np.array([np.exp(s - mx) for s in logits])
         O[t] = (w[:, None] * np.array(vals)).sum(0) / w.sum()
     return O
+
+
+# --------------------------------------------------------------------------
+# 6. e4m3 quantisation for the FP8 attention variant (SVG2 summary, results:
+#    SVG2 + FP8 on HunyuanVideo; the pages give no scheme)
+# --------------------------------------------------------------------------
+def e4m3_exponent(amax: float) -> int:
+    """Smallest integer e with amax <= 448 * 2^e (448: the largest finite
+    e4m3fn value); 0 for amax = 0.  From amax = f 2^E with 0.5 <= f < 1 and
+    448 = 0.875 * 2^9."""
+    if not amax > 0.0:
+        return 0
+    f, E = math.frexp(float(amax))
+    return E - 9 if f <= 0.875 else E - 8
+
+
+def quantize_e4m3(X: np.ndarray):
+    """One (batch, head) slice to e4m3fn codes with one power-of-two scale:
+    codes = round-to-nearest-even e4m3fn of X * 2^-e (scaled in float32, which
+    is exact), X ~ decode(codes) * 2^e.  The rounding is torch's float32 ->
+    float8_e4m3fn conversion.  Returns (codes uint8, e)."""
+    import torch
+    X32 = np.asarray(X, np.float32)
+    e = e4m3_exponent(float(np.max(np.abs(X32)))) if X32.size else 0
+    scaled = np.ldexp(X32, -e).astype(np.float32)
+    codes = torch.from_numpy(np.ascontiguousarray(scaled)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    return codes, e
+
+
+def dequantize_e4m3(codes: np.ndarray, e: int) -> np.ndarray:
+    """decode(codes) * 2^e in float64 (exact)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8)).view(torch.float8_e4m3fn)
+    return np.ldexp(t.double().numpy(), e)
 
 
 # --------------------------------------------------------------------------

@@ -640,3 +640,53 @@ def test_kmeanspp_second_seed_follows_the_d2_law():
         counts[orc.kmeanspp(X, np.array([0, wd], dtype=np.uint64), 2)[1][1]] += 1
     assert counts[0] == 0
     assert np.all(np.abs(counts / n - p) <= 5 * np.sqrt(p * (1 - p) / n) + 1e-12)
+
+
+# ---------------------------------------------------------------- e4m3 quantisation (FP8 variant)
+def e4m3_value(code: int) -> float:
+    """OCP e4m3fn from its definition: 1 sign, 4 exponent (bias 7), 3 mantissa
+    bits; exponent field 0 is subnormal; S.1111.111 is NaN; no infinities."""
+    s, E, M = code >> 7, (code >> 3) & 15, code & 7
+    if E == 15 and M == 7:
+        return float("nan")
+    v = (M / 8.0) * 2.0 ** -6 if E == 0 else (1 + M / 8.0) * 2.0 ** (E - 7)
+    return -v if s else v
+
+
+def test_e4m3_codes_follow_the_format_definition():
+    codes = np.arange(256, dtype=np.uint8)
+    dec = orc.dequantize_e4m3(codes, 0)
+    ref = np.array([e4m3_value(c) for c in range(256)])
+    assert np.array_equal(np.isnan(dec), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(dec[ok], ref[ok])
+    assert np.nanmax(dec) == 448.0 and dec[1] == 2.0 ** -9
+    # every finite value quantises to itself (scale 2^0 since the max is 448)
+    fin = ref[ok]
+    c, e = orc.quantize_e4m3(fin)
+    assert e == 0 and np.array_equal(orc.dequantize_e4m3(c, e), fin)
+
+
+def test_e4m3_rounding_is_nearest_even_with_exact_ties():
+    # 1 + 1/16 lies halfway between 1 (mantissa 000) and 1.125 (001): even -> 1;
+    # 1 + 3/16 between 1.125 (001) and 1.25 (010): even -> 1.25; the same in
+    # the subnormal range: 3 * 2^-10 between 2^-9 (001) and 2^-8 (010) -> 2^-8
+    x = np.array([448.0, 1.0625, 1.1875, 3 * 2.0 ** -10, -1.0625, 1.0625 + 2 ** -20], np.float32)
+    c, e = orc.quantize_e4m3(x)
+    assert e == 0
+    np.testing.assert_array_equal(orc.dequantize_e4m3(c, e), [448.0, 1.0, 1.25, 2.0 ** -8, -1.0, 1.125])
+
+
+def test_e4m3_scale_rule_and_error_bound():
+    assert orc.e4m3_exponent(448.0) == 0 and orc.e4m3_exponent(448.0001) == 1
+    assert orc.e4m3_exponent(224.0) == -1 and orc.e4m3_exponent(0.0) == 0
+    rng = np.random.default_rng(3)
+    for scale in (1e-3, 0.7, 5.0, 3e4):
+        X = (rng.standard_normal((64, 32)) * scale).astype(np.float32)
+        c, e = orc.quantize_e4m3(X)
+        a = float(np.abs(X).max())
+        assert 224.0 < a * 2.0 ** -e <= 448.0
+        Y = orc.dequantize_e4m3(c, e)
+        big = np.abs(X) >= 2.0 ** (e - 6)                 # normal range of the codes
+        assert np.all(np.abs(Y[big] - X[big]) <= 2.0 ** -4 * np.abs(X[big]))
+        assert np.all(np.abs(Y[~big] - X[~big]) <= 2.0 ** (e - 10))   # half a subnormal step
