@@ -122,8 +122,9 @@ def cpu_baseline(w, h0, scale):
 def variants(sv, L, w, q, k, scale, ev, reps=5, top_p=0.9):
     """Timings of the variant paths on the same layer state (outside the step):
     routing under the SVG2 top-p budget (both rankers) with the density each
-    realises, k-means++ cold seeding of Q and K, and variance-corrected
-    compensation (key variances + attention)."""
+    realises, k-means++ cold seeding of Q and K, the FP8 attention variant
+    (e4m3 Q'/K' quantisation + attention) and variance-corrected compensation
+    (key variances + attention)."""
     import torch
 
     def timed(fn):
@@ -161,6 +162,17 @@ def variants(sv, L, w, q, k, scale, ev, reps=5, top_p=0.9):
         torch.cuda.synchronize()
         res[f"kmeanspp_{which}"] = {"ms": round(a.elapsed_time(b), 3), "seeds": C}
     if w.dtype == "bf16":
+        # FP8 variant: e4m3 Q' and K' (per-head power-of-two scales), bf16 V'
+        q8, qe = sv.quantize_fp8(L.qp)
+        k8, ke = sv.quantize_fp8(L.kp)
+        t_q, _ = timed(lambda: (sv.quantize_fp8(L.qp, x8=q8, exps=qe), sv.quantize_fp8(L.kp, x8=k8, exps=ke)))
+        o8 = torch.empty_like(L.out)
+        t_a8, _ = timed(lambda: sv.sparse_attn_fp8(q8, qe, k8, ke, L.vp, L.pq, L.oq, L.ok, L.km, L.vm, L.mask, scale,
+                                                   out=o8, ws=L.ws))
+        flops, _, _ = algorithmic_flops(L.mask.cpu().numpy(), qoff, koff, w.D)
+        res["sparse_attn_fp8"] = {"ms": t_a8, "quantize_qk_ms": t_q,
+                                  "tflops": round(flops / (t_a8 * 1e-3) / 1e12, 1),
+                                  "max_abs_diff_vs_bf16": round(float((o8.float() - L.out.float()).abs().max()), 4)}
         kv = torch.empty_like(L.km)
         t_var, _ = timed(lambda: sv.centroid_variances(k, L.pk, L.ok, L.km, vars=kv, ws=L.ws))
         t_att, _ = timed(lambda: sv.sparse_attn(L.qp, L.kp, L.vp, L.pq, L.oq, L.ok, L.km, L.vm, L.mask, scale,

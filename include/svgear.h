@@ -31,9 +31,10 @@
  *     non-OK status.  No call aborts or throws.
  *   - Results are bitwise deterministic run to run (no float atomics).
  *   - Setting the environment variable SVGEAR_FAULT to one of kmeans,
- *     kmeanspp, centroids, centroid_variances, route, route_topp, attn makes
- *     that call return SVGEAR_ERR_INJECTED without queuing work (for testing
- *     a caller's dense fallback; attn covers both attention entry points).
+ *     kmeanspp, centroids, centroid_variances, route, route_topp, attn,
+ *     quantize_fp8 makes that call return SVGEAR_ERR_INJECTED without queuing
+ *     work (for testing a caller's dense fallback; attn covers every attention
+ *     entry point).
  */
 #ifndef SVGEAR_H
 #define SVGEAR_H
@@ -315,6 +316,44 @@ svgear_status svgear_sparse_attn_var(const void* q_perm, const void* k_perm, con
                                      const uint8_t* mask, int B, int H, int N, int D, float scale,
                                      void* out, float* lse, void* ws, size_t ws_bytes,
                                      hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * FP8 variant (SVG2 summary, results on HunyuanVideo: SVG2 combined with
+ * FP8 quantisation, 2.30x -> 2.55x end to end).  The pages give no scheme;
+ * here Q' and K' are stored as OCP e4m3fn codes with one power-of-two scale
+ * per (batch, head), the exact blocks' scores are e4m3 matrix products with
+ * fp32 accumulation, and V, the weights and the pseudo-keys stay as in the
+ * bf16 path.
+ * ---------------------------------------------------------------------- */
+
+/* svgear_quantize_fp8 -- x8 = e4m3fn(x * 2^-e) rounded to nearest even, with
+ * e = exps[b,h] the smallest integer such that max|x| over the slice <= 448 * 2^e
+ * (0 for an all-zero slice), so x ~ decode(x8) * 2^e.  The scaling by 2^-e is
+ * exact; the e4m3 rounding is the only one.
+ *   x          [B,H,N,D] dtype dt (finite values).
+ *   x8         [B,H,N,D] uint8 OUT: the e4m3fn codes.
+ *   exps       [B,H] int32 OUT.
+ *   ws         at least svgear_quantize_fp8_workspace(B, H) bytes. */
+size_t svgear_quantize_fp8_workspace(int B, int H);
+svgear_status svgear_quantize_fp8(const void* x, svgear_dtype dt, int B, int H, int N, int D,
+                                  uint8_t* x8, int32_t* exps, void* ws, size_t ws_bytes,
+                                  hipStream_t stream);
+
+/* svgear_sparse_attn_fp8 -- svgear_sparse_attn with q = decode(q8) * 2^q_exp
+ * and k = decode(k8) * 2^k_exp (outputs of svgear_quantize_fp8 on the
+ * permuted Q' and K'); v_perm is bf16; k_means and v_means are the fp32 means
+ * of the unquantised keys and values.  The exact blocks' scores are
+ * scale * 2^(q_exp + k_exp) * (e4m3 codes product, fp32 accumulation); a
+ * skipped cluster's score is scale * q.k_bar_j + ln n_j with the dequantised
+ * q.  Same workspace, layouts, tile list and output as svgear_sparse_attn
+ * (out bf16 in original token order, lse nullable). */
+svgear_status svgear_sparse_attn_fp8(const uint8_t* q8, const int32_t* q_exp, const uint8_t* k8,
+                                     const int32_t* k_exp, const void* v_perm,
+                                     const int32_t* q_perm_idx, const int32_t* q_offsets, int Cq,
+                                     const int32_t* k_offsets, int Ck, const float* k_means,
+                                     const float* v_means, const uint8_t* mask, int B, int H, int N,
+                                     int D, float scale, void* out, float* lse, void* ws,
+                                     size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

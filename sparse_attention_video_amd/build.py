@@ -10,7 +10,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsvgear.so")
-SOURCES = ["api.hip", "kmeans.hip", "route.hip", "attn.hip", "seed.hip"]
+SOURCES = ["api.hip", "kmeans.hip", "route.hip", "attn.hip", "seed.hip", "quant.hip"]
 ARCH = os.environ.get("SVGEAR_ARCH", "gfx950")
 
 # Packed fp32 instructions are kept out of the device code on purpose.

@@ -438,6 +438,21 @@ __device__ __forceinline__ bf16x8 vt_frag(const char* p0, const char* p1) {
   return __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// e4m3 products: A and B are 32 bytes per lane (row / column l % 32, k range
+// 32 (l / 32) .. + 31 of the 64), fp32 accumulate; no block scaling
+typedef int at_v8i __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ f32x16 mfma_fp8(const at_v8i& a, const at_v8i& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// fp8 K tile: rows of D bytes, 16-byte chunks XOR-swizzled so that 16 rows
+// read at one chunk fall on 16 different 4-bank groups
+template <int D>
+struct AtTile8 {
+  static constexpr int ROWB = D, CH = D / 16, RPI = 64 / CH, NI = 16 / RPI, KK = D / 64;
+  static __device__ __forceinline__ int swz(int r) { return (r / (256 / ROWB)) & (CH - 1); }
+};
+
 template <int D>
 struct AtTile {
   static constexpr int ROWB = 2 * D, CH = D / 8, RPI = 64 / CH, NI = CH / 4;
@@ -448,7 +463,7 @@ struct AtTile {
 
 // VAR: skipped clusters' scores also gain vcoef * sum_i q_i^2 kvars[j][i]
 // (variance-corrected compensation; vcoef in log2 units).
-template <int D, bool VAR = false>
+template <int D, bool VAR = false, bool F8 = false>
 __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restrict__ qp, const bf16* __restrict__ kp,
                                                            const bf16* __restrict__ vp, const int32_t* __restrict__ qidx,
                                                            const int32_t* __restrict__ qoff,
@@ -459,8 +474,10 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
                                                            const uint8_t* __restrict__ mask, int N, float sl2,
                                                            bf16* __restrict__ out, float* __restrict__ lse,
                                                            int maxt, int BHn, const float* __restrict__ kvars,
-                                                           float vcoef) {
+                                                           float vcoef, const int32_t* __restrict__ qexp,
+                                                           const int32_t* __restrict__ kexp) {
   using TL = AtTile<D>;
+  using T8 = AtTile8<D>;
   constexpr int KS = D / 16, DT = D / 32, ROWB = TL::ROWB, CH = TL::CH, RPI = TL::RPI, NI = TL::NI;
   __shared__ __attribute__((aligned(1024))) char sK0[TL::BYTES];
   __shared__ __attribute__((aligned(1024))) char sK1[TL::BYTES];
@@ -522,18 +539,62 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
   const int nreal = (nkeys + AT_BN - 1) / AT_BN;
   const int npseudo = (ncomp + AT_BN - 1) / AT_BN;
 
+  // F8: qp and kp hold e4m3 bytes (D per row) with per-head power-of-two
+  // scales 2^qexp, 2^kexp; real-tile scores use scale 2^(qexp+kexp) sl2 and
+  // pseudo-tile scores (q against the fp32 means) 2^qexp sl2
   const bf16* qb = qp + (size_t)bh * N * D;
-  const char* kb = reinterpret_cast<const char*>(kp + (size_t)bh * N * D);
+  const char* kb = F8 ? reinterpret_cast<const char*>(kp) + (size_t)bh * N * D
+                      : reinterpret_cast<const char*>(kp + (size_t)bh * N * D);
+  const char* q8b = reinterpret_cast<const char*>(qp) + (size_t)bh * N * D;
   const char* vb = reinterpret_cast<const char*>(vp + (size_t)bh * N * D);
+  float sl2r = sl2, sl2p = sl2;
+  if constexpr (F8) {
+    sl2r = ldexpf(sl2, qexp[bh] + kexp[bh]);
+    sl2p = ldexpf(sl2, qexp[bh]);
+  }
   const int qrow = row0 + 32 * w + col;
   const bool qok = qrow < rowEnd;
   bf16x8 bq[KS];
+  at_v8i bq8[F8 ? T8::KK : 1];
+  if constexpr (!F8) {
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    bf16x8 v = {};
-    if (qok) v = *reinterpret_cast<const bf16x8*>(qb + (size_t)qrow * D + 16 * ks + 8 * half);
-    bq[ks] = v;
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 v = {};
+      if (qok) v = *reinterpret_cast<const bf16x8*>(qb + (size_t)qrow * D + 16 * ks + 8 * half);
+      bq[ks] = v;
+    }
+  } else {
+    // B operand of the e4m3 products: dims 64 kk + 32 half .. + 31 of the query row
+#pragma unroll
+    for (int kk = 0; kk < T8::KK; ++kk) {
+      at_v8i v = {};
+      if (qok) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(q8b + (size_t)qrow * D + 64 * kk + 32 * half);
+        const u32x4 b = *reinterpret_cast<const u32x4*>(q8b + (size_t)qrow * D + 64 * kk + 32 * half + 16);
+        v = at_v8i{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+      }
+      bq8[kk] = v;
+    }
   }
+  // bf16 Q fragments from the e4m3 bytes (exact), for the pseudo tiles
+  auto load_bq_from_fp8 = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 v = {};
+      if (qok) {
+        const uint2 raw = *reinterpret_cast<const uint2*>(q8b + (size_t)qrow * D + 16 * ks + 8 * half);
+        v[0] = (bf16)__builtin_amdgcn_cvt_f32_fp8((int)raw.x, 0);
+        v[1] = (bf16)__builtin_amdgcn_cvt_f32_fp8((int)raw.x, 1);
+        v[2] = (bf16)__builtin_amdgcn_cvt_f32_fp8((int)raw.x, 2);
+        v[3] = (bf16)__builtin_amdgcn_cvt_f32_fp8((int)raw.x, 3);
+        v[4] = (bf16)__builtin_amdgcn_cvt_f32_fp8((int)raw.y, 0);
+        v[5] = (bf16)__builtin_amdgcn_cvt_f32_fp8((int)raw.y, 1);
+        v[6] = (bf16)__builtin_amdgcn_cvt_f32_fp8((int)raw.y, 2);
+        v[7] = (bf16)__builtin_amdgcn_cvt_f32_fp8((int)raw.y, 3);
+      }
+      bq[ks] = v;
+    }
+  };
   f32x16 o[DT];
 #pragma unroll
   for (int t = 0; t < DT; ++t) o[t] = f32x16{};
@@ -556,6 +617,14 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
       const int chunk = 4 * t + 2 * g1 + ((j >> 1) & 1);
       aV[t] = (4 * half + r4) * ROWB + ((chunk ^ TL::swzV(r4)) << 4) + ((j & 1) << 3);
     }
+  }
+  // e4m3 K A-fragment: row sub*32 + col, chunks 4 kk + 2 half + {0, 1}
+  int aK8[F8 ? T8::KK : 1][2];
+  if constexpr (F8) {
+#pragma unroll
+    for (int kk = 0; kk < T8::KK; ++kk)
+#pragma unroll
+      for (int q = 0; q < 2; ++q) aK8[kk][q] = col * T8::ROWB + (((4 * kk + 2 * half + q) ^ T8::swz(col)) << 4);
   }
   // direct-to-LDS loads: instruction i of wave w fills rows (w NI + i) RPI + L / CH
   const int lq = lane / CH, lslot = lane % CH;
@@ -583,14 +652,42 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
       rowoff[i] = (uint32_t)(p < nkeys ? tc_base + (p - tc_pre) : 0) * (uint32_t)ROWB;
     }
   };
+  // e4m3 K rows: instruction j of wave w fills rows (w NI8 + j) RPI8 + L / CH8
+  // (the same 16-row band as the V rows of wave w), with a cursor of its own
+  const int lq8 = lane / T8::CH, lslot8 = lane % T8::CH;
+  int chK8[F8 ? T8::NI : 1];
+  if constexpr (F8) {
+#pragma unroll
+    for (int j = 0; j < T8::NI; ++j) chK8[j] = lslot8 ^ T8::swz((w * T8::NI + j) * T8::RPI + lq8);
+  }
+  int uc = 0, uc_base = nsel > 0 ? sSelStart[0] : 0, uc_pre = 0;
+  int uc_nxt = nsel > 1 ? sSelPre[1] : 0x7fffffff;
+  auto sources8 = [&](int kt, uint32_t* rowoff) {
+#pragma unroll
+    for (int j = 0; j < (F8 ? T8::NI : 1); ++j) {
+      const int p = kt * AT_BN + (w * T8::NI + j) * T8::RPI + lq8;
+      while (p >= uc_nxt) {
+        ++uc;
+        uc_base = sSelStart[uc];
+        uc_pre = uc_nxt;
+        uc_nxt = uc + 1 < nsel ? sSelPre[uc + 1] : 0x7fffffff;
+      }
+      rowoff[j] = (uint32_t)(p < nkeys ? uc_base + (p - uc_pre) : 0) * (uint32_t)T8::ROWB;
+    }
+  };
   // a 32-bit per-lane offset from the head's base keeps the loads in the
   // scalar-base form (4 address bytes per lane instead of 8)
-  auto issue = [&](const uint32_t* rowoff, char* dK, char* dV) {
+  auto issue = [&](const uint32_t* rowoff, const uint32_t* rowoff8, char* dK, char* dV) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int g = w * NI + i;
-      load_lds16(kb + (uint32_t)(rowoff[i] + (uint32_t)(chK[i] << 4)), dK + g * 1024);
+      if constexpr (!F8) load_lds16(kb + (uint32_t)(rowoff[i] + (uint32_t)(chK[i] << 4)), dK + g * 1024);
       load_lds16(vb + (uint32_t)(rowoff[i] + (uint32_t)(chV << 4)), dV + g * 1024);
+    }
+    if constexpr (F8) {
+#pragma unroll
+      for (int j = 0; j < T8::NI; ++j)
+        load_lds16(kb + (uint32_t)(rowoff8[j] + (uint32_t)(chK8[j] << 4)), dK + (w * T8::NI + j) * 1024);
     }
   };
 
@@ -603,7 +700,18 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
   // bias first.
   auto compute = [&](const char* Kh, const char* Vh, int lim, bool pseudo, auto&& mid) {
     f32x16 s[2] = {f32x16{}, f32x16{}};
-    {
+    if (F8 && !pseudo) {
+#pragma unroll
+      for (int kk = 0; kk < T8::KK; ++kk)
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+          const char* r = Kh + sub * 32 * T8::ROWB;
+          const u32x4 a = *reinterpret_cast<const u32x4*>(r + aK8[kk][0]);
+          const u32x4 b = *reinterpret_cast<const u32x4*>(r + aK8[kk][1]);
+          const at_v8i fa = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+          s[sub] = mfma_fp8(fa, bq8[kk], s[sub]);
+        }
+    } else {
       // fragments of step ks + 1 are read before the products of step ks
       bf16x8 fr[2][2];
       fr[0][0] = *reinterpret_cast<const bf16x8*>(Kh + aK[0]);
@@ -628,7 +736,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[sub][r] = fmaf(s[sub][r], sl2, sBias[sub * 32 + c_row(r, half)]);
+        for (int r = 0; r < 16; ++r) s[sub][r] = fmaf(s[sub][r], sl2p, sBias[sub * 32 + c_row(r, half)]);
       if constexpr (VAR) {
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub)
@@ -650,7 +758,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
     mx = max_halves(mx);
-    if (!pseudo) mx *= sl2;
+    if (!pseudo) mx *= sl2r;
     const bool grow = mx > m_run + AT_LAZY;
     if (ballot(grow)) {
       const float m_new = grow ? mx : m_run;
@@ -662,7 +770,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
     }
-    const float sc = pseudo ? 1.f : sl2;
+    const float sc = pseudo ? 1.f : sl2r;
     const float nm = -m_run;
     const at_bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
@@ -691,9 +799,10 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
   // ---- selected keys: packed 64-key tiles, double buffered, loop unrolled by
   // two so each half reads one fixed buffer
   if (nreal > 0) {
-    uint32_t ro[NI];
+    uint32_t ro[NI], ro8[F8 ? T8::NI : 1];
     sources(0, ro);
-    issue(ro, sK0, sV0);
+    if constexpr (F8) sources8(0, ro8);
+    issue(ro, ro8, sK0, sV0);
     // the Q fragments and tile 0 are in: later waits only cover the prefetch
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -701,12 +810,14 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
       // the next tile's loads go out while this tile's S^T products run; past
       // the last tile they fetch row 0 into the idle buffer, which is never read
       sources(kt + 1, ro);
-      compute(sK0, sV0, nkeys - kt * AT_BN, false, [&] { issue(ro, sK1, sV1); });
+      if constexpr (F8) sources8(kt + 1, ro8);
+      compute(sK0, sV0, nkeys - kt * AT_BN, false, [&] { issue(ro, ro8, sK1, sV1); });
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (kt + 1 < nreal) {
         sources(kt + 2, ro);
-        compute(sK1, sV1, nkeys - (kt + 1) * AT_BN, false, [&] { issue(ro, sK0, sV0); });
+        if constexpr (F8) sources8(kt + 2, ro8);
+        compute(sK1, sV1, nkeys - (kt + 1) * AT_BN, false, [&] { issue(ro, ro8, sK0, sV0); });
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
       }
@@ -718,6 +829,9 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
   constexpr int NUNIT = (AT_BN / 4) * (D / 8);
   const bool has_unit = tid < NUNIT;
   const int g4 = tid & 15, d0 = (tid >> 4) * 8;
+  if constexpr (F8) {
+    if (npseudo > 0) load_bq_from_fp8();
+  }
   bf16x8 q2[VAR ? KS : 1];
   if constexpr (VAR) {
 #pragma unroll
@@ -834,7 +948,8 @@ template <typename T, int D>
 static void launch_attn(const void* q, const void* k, const void* v, const int32_t* qidx, const int32_t* qoff,
                         const int32_t* ts, int Cq, const int32_t* koff, int Ck, const float* km, const float* vm,
                         const uint8_t* mask, int BH, int N, float sl2, void* out, float* lse, int maxt,
-                        const float* kvars, float vcoef, hipStream_t st) {
+                        const float* kvars, float vcoef, const int32_t* qexp, const int32_t* kexp,
+                        hipStream_t st) {
   if constexpr (sizeof(T) == 2) {
     const size_t lds = (size_t)(3 * Ck + 1) * sizeof(int);  // cluster lists; the tiles are static
     const int total = round_up(maxt * BH, AT_XCDS);
@@ -843,17 +958,27 @@ static void launch_attn(const void* q, const void* k, const void* v, const int32
                                 (int)lds);
       hipLaunchKernelGGL((attn_bf16_kernel<D, true>), dim3(total), dim3(256), lds, st, (const bf16*)q,
                          (const bf16*)k, (const bf16*)v, qidx, qoff, ts, Cq, koff, Ck, km, vm, mask, N, sl2,
-                         (bf16*)out, lse, maxt, BH, kvars, vcoef);
+                         (bf16*)out, lse, maxt, BH, kvars, vcoef, (const int32_t*)nullptr,
+                         (const int32_t*)nullptr);
+    } else if (qexp) {
+      (void)hipFuncSetAttribute((const void*)attn_bf16_kernel<D, false, true>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      hipLaunchKernelGGL((attn_bf16_kernel<D, false, true>), dim3(total), dim3(256), lds, st, (const bf16*)q,
+                         (const bf16*)k, (const bf16*)v, qidx, qoff, ts, Cq, koff, Ck, km, vm, mask, N, sl2,
+                         (bf16*)out, lse, maxt, BH, (const float*)nullptr, 0.f, qexp, kexp);
     } else {
       (void)hipFuncSetAttribute((const void*)attn_bf16_kernel<D, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                 (int)lds);
       hipLaunchKernelGGL((attn_bf16_kernel<D, false>), dim3(total), dim3(256), lds, st, (const bf16*)q,
                          (const bf16*)k, (const bf16*)v, qidx, qoff, ts, Cq, koff, Ck, km, vm, mask, N, sl2,
-                         (bf16*)out, lse, maxt, BH, (const float*)nullptr, 0.f);
+                         (bf16*)out, lse, maxt, BH, (const float*)nullptr, 0.f, (const int32_t*)nullptr,
+                         (const int32_t*)nullptr);
     }
   } else {
     (void)kvars;
     (void)vcoef;
+    (void)qexp;
+    (void)kexp;
     using L = AttnLds<T, D>;
     const size_t lds = L::fixed + (size_t)(3 * Ck + 1) * sizeof(int);
     (void)hipFuncSetAttribute((const void*)attn_kernel<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -878,7 +1003,8 @@ static svgear_status sparse_attn_impl(const void* q_perm, const void* k_perm, co
                                       const int32_t* k_offsets, int Ck, const float* k_means, const float* v_means,
                                       const float* k_vars, float strength, const uint8_t* mask, int B, int H, int N,
                                       int D, float scale, void* out, float* lse, void* ws, size_t ws_bytes,
-                                      hipStream_t stream) {
+                                      hipStream_t stream, const int32_t* q_exp = nullptr,
+                                      const int32_t* k_exp = nullptr) {
   svgear_status st = check_common("attn", dt, B, H, N, D);
   if (st != SVGEAR_OK) return st;
   if (Cq < 1 || Cq > N || Cq > SVGEAR_MAX_CLUSTERS || Ck < 1 || Ck > N || Ck > SVGEAR_MAX_CLUSTERS)
@@ -900,17 +1026,17 @@ static svgear_status sparse_attn_impl(const void* q_perm, const void* k_perm, co
   if (dt == SVGEAR_BF16) {
     if (D == 128)
       launch_attn<bf16, 128>(q_perm, k_perm, v_perm, q_perm_idx, q_offsets, ts, Cq, k_offsets, Ck, k_means, v_means,
-                             mask, BH, N, sl2, out, lse, p.maxt, k_vars, vcoef, stream);
+                             mask, BH, N, sl2, out, lse, p.maxt, k_vars, vcoef, q_exp, k_exp, stream);
     else
       launch_attn<bf16, 64>(q_perm, k_perm, v_perm, q_perm_idx, q_offsets, ts, Cq, k_offsets, Ck, k_means, v_means,
-                            mask, BH, N, sl2, out, lse, p.maxt, k_vars, vcoef, stream);
+                            mask, BH, N, sl2, out, lse, p.maxt, k_vars, vcoef, q_exp, k_exp, stream);
   } else {
     if (D == 128)
       launch_attn<float, 128>(q_perm, k_perm, v_perm, q_perm_idx, q_offsets, ts, Cq, k_offsets, Ck, k_means, v_means,
-                              mask, BH, N, sl2, out, lse, p.maxt, k_vars, vcoef, stream);
+                              mask, BH, N, sl2, out, lse, p.maxt, k_vars, vcoef, q_exp, k_exp, stream);
     else
       launch_attn<float, 64>(q_perm, k_perm, v_perm, q_perm_idx, q_offsets, ts, Cq, k_offsets, Ck, k_means, v_means,
-                             mask, BH, N, sl2, out, lse, p.maxt, k_vars, vcoef, stream);
+                             mask, BH, N, sl2, out, lse, p.maxt, k_vars, vcoef, q_exp, k_exp, stream);
   }
   return check_launch("svgear_sparse_attn");
 }
@@ -938,4 +1064,16 @@ extern "C" svgear_status svgear_sparse_attn_var(const void* q_perm, const void* 
     return fail(SVGEAR_ERR_INVALID_ARG, "attn_var: strength must be >= 0 and finite");
   return sparse_attn_impl(q_perm, k_perm, v_perm, dt, q_perm_idx, q_offsets, Cq, k_offsets, Ck, k_means, v_means,
                           k_vars, strength, mask, B, H, N, D, scale, out, lse, ws, ws_bytes, stream);
+}
+
+extern "C" svgear_status svgear_sparse_attn_fp8(const uint8_t* q8, const int32_t* q_exp, const uint8_t* k8,
+                                                const int32_t* k_exp, const void* v_perm,
+                                                const int32_t* q_perm_idx, const int32_t* q_offsets, int Cq,
+                                                const int32_t* k_offsets, int Ck, const float* k_means,
+                                                const float* v_means, const uint8_t* mask, int B, int H, int N,
+                                                int D, float scale, void* out, float* lse, void* ws,
+                                                size_t ws_bytes, hipStream_t stream) {
+  if (!q_exp || !k_exp) return fail(SVGEAR_ERR_INVALID_ARG, "attn_fp8: null pointer");
+  return sparse_attn_impl(q8, k8, v_perm, SVGEAR_BF16, q_perm_idx, q_offsets, Cq, k_offsets, Ck, k_means, v_means,
+                          nullptr, 0.f, mask, B, H, N, D, scale, out, lse, ws, ws_bytes, stream, q_exp, k_exp);
 }

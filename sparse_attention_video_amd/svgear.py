@@ -29,6 +29,7 @@ EXPORTS = (
     "svgear_centroid_variances", "svgear_sparse_attn_var",
     "svgear_route_topp",
     "svgear_kmeanspp_workspace", "svgear_kmeanspp",
+    "svgear_quantize_fp8_workspace", "svgear_quantize_fp8", "svgear_sparse_attn_fp8",
 )
 
 _lib = None
@@ -77,6 +78,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.svgear_kmeanspp_workspace.restype = Z
     lib.svgear_kmeanspp.argtypes = [P, I, I, I, I, I, I, P, P, P, P, Z, P]
     lib.svgear_kmeanspp.restype = I
+    lib.svgear_quantize_fp8_workspace.argtypes = [I, I]
+    lib.svgear_quantize_fp8_workspace.restype = Z
+    lib.svgear_quantize_fp8.argtypes = [P, I, I, I, I, I, P, P, P, Z, P]
+    lib.svgear_quantize_fp8.restype = I
+    lib.svgear_sparse_attn_fp8.argtypes = [P, P, P, P, P, P, P, I, P, I, P, P, P, I, I, I, I, F, P, P, P, Z, P]
+    lib.svgear_sparse_attn_fp8.restype = I
     _lib = lib
     return lib
 
@@ -215,6 +222,44 @@ def kmeanspp(x: torch.Tensor, words: torch.Tensor, C: int, centroids=None, chose
     _check("svgear_kmeanspp", lib.svgear_kmeanspp(_ptr(x), _dtype(x), B, H, N, D, C, _ptr(words), _ptr(centroids),
                                                   _ptr(chosen), _ptr(ws), ws.numel(), _stream(dev)))
     return centroids, chosen
+
+
+def quantize_fp8(x: torch.Tensor, x8=None, exps=None, ws=None):
+    """e4m3fn codes [B,H,N,D] uint8 and per-(batch, head) exponents [B,H] int32."""
+    dev = _dev(x)
+    B, H, N, D = x.shape
+    x8 = x8 if x8 is not None else torch.empty((B, H, N, D), dtype=torch.uint8, device=dev)
+    exps = exps if exps is not None else torch.empty((B, H), dtype=torch.int32, device=dev)
+    lib = load()
+    need = lib.svgear_quantize_fp8_workspace(B, H)
+    ws = ws if ws is not None else _workspace(need, dev)
+    _check("svgear_quantize_fp8", lib.svgear_quantize_fp8(_ptr(x), _dtype(x), B, H, N, D, _ptr(x8), _ptr(exps),
+                                                          _ptr(ws), ws.numel(), _stream(dev)))
+    return x8, exps
+
+
+def sparse_attn_fp8(q8, q_exp, k8, k_exp, v_perm, q_perm_idx, q_offsets, k_offsets, k_means, v_means, mask,
+                    scale: float, want_lse: bool = False, out=None, lse=None, ws=None):
+    """FP8 variant: e4m3 Q'/K' (from quantize_fp8), bf16 V'.  Returns (out, lse or None)."""
+    dev = _dev(q8, q_exp, k8, k_exp, v_perm, q_perm_idx, q_offsets, k_offsets, k_means, v_means, mask)
+    B, H, N, D = v_perm.shape
+    Cq, Ck = q_offsets.shape[2] - 1, k_offsets.shape[2] - 1
+    if q8.dtype != torch.uint8 or k8.dtype != torch.uint8 or tuple(q8.shape) != (B, H, N, D):
+        raise ValueError("q8 and k8 must be uint8 [B, H, N, D] e4m3 codes")
+    if v_perm.dtype != torch.bfloat16:
+        raise ValueError("the FP8 variant takes bf16 values")
+    out = out if out is not None else torch.empty_like(v_perm)
+    if want_lse and lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    lib = load()
+    need = lib.svgear_sparse_attn_workspace(B, H, N, D, Cq, Ck)
+    ws = ws if ws is not None else _workspace(need, dev)
+    _check("svgear_sparse_attn_fp8",
+           lib.svgear_sparse_attn_fp8(_ptr(q8), _ptr(q_exp), _ptr(k8), _ptr(k_exp), _ptr(v_perm), _ptr(q_perm_idx),
+                                      _ptr(q_offsets), Cq, _ptr(k_offsets), Ck, _ptr(k_means), _ptr(v_means),
+                                      _ptr(mask), B, H, N, D, float(scale), _ptr(out), _ptr(lse if want_lse else None),
+                                      _ptr(ws), ws.numel(), _stream(dev)))
+    return out, (lse if want_lse else None)
 
 
 def route_topp(q_means, q_offsets, k_perm, v_perm, k_means, v_means, k_offsets, scale: float, top_p: float,

@@ -15,7 +15,7 @@ LIB = os.path.join(ROOT, "sparse_attention_video_amd", "libsvgear.so")
 
 def declared():
     src = open(HEADER).read()
-    return sorted(set(re.findall(r"\b(svgear_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(svgear_[a-z0-9_]+)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
@@ -28,7 +28,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared()
-    assert len(names) == 15
+    assert len(names) == 18
     for n in names:
         assert hasattr(lib, n), n
     from sparse_attention_video_amd import svgear
@@ -109,6 +109,13 @@ def test_route_and_attn_validation(lib):
     assert K(0) == 1 and K(101) == 1 and K(5, words=None) == 1 and K(5, cent=None) == 1
     assert K(5) == 3 and K(100) == 3
     assert lib.svgear_kmeanspp_workspace(1, 40, 75600, 128) >= 40 * 75600 * 8
+    # FP8 variant
+    assert lib.svgear_quantize_fp8(F, 0, 1, 1, 100, 64, None, F, None, 0, None) == 1
+    assert lib.svgear_quantize_fp8(F, 0, 1, 1, 100, 96, F, F, None, 0, None) == 1
+    assert lib.svgear_quantize_fp8(F, 0, 1, 1, 100, 64, F, F, None, 0, None) == 3
+    A8 = lambda qe: lib.svgear_sparse_attn_fp8(F, qe, F, F, F, F, F, 4, F, 8, F, F, F, 1, 1, 100, 64,
+                                               ctypes.c_float(0.125), F, None, None, 0, None)
+    assert A8(None) == 1 and A8(F) == 3
 
 
 def test_fault_injection_returns_injected_without_work():

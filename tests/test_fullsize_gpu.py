@@ -454,3 +454,28 @@ def test_full_kmeanspp_seeding(sv):
         say(f"wan: oracle seeding of head {h} ({which}): {time.time() - t0:.1f}s")
         np.testing.assert_array_equal(host(chosen[b, hh]), idx)
         np.testing.assert_array_equal(host(cent[b, hh]).astype(np.float64), seeds)
+
+
+def test_full_attention_fp8(sv):
+    """FP8 variant at the Wan layer size: Q' and K' quantised on the GPU (codes
+    and exponents of the sampled head bit-exact), attention on the sampled rows
+    against the oracle attending with the dequantised Q and K."""
+    w, h, dev, x, L, cq, ck, ref = full_case(sv, "wan")
+    t = teacher_forced_device(w, h, dev, x, L, ref)
+    b, hh = bh_index(w, h)
+    q8, qe = sv.quantize_fp8(t["qp"])
+    k8, ke = sv.quantize_fp8(t["kp"])
+    cq8, eq = orc.quantize_e4m3(x["q"])
+    ck8, ek = orc.quantize_e4m3(x["k"])
+    assert int(host(qe)[b, hh]) == eq and int(host(ke)[b, hh]) == ek
+    np.testing.assert_array_equal(host(q8[b, hh]), cq8[ref["pq"]])
+    np.testing.assert_array_equal(host(k8[b, hh]), ck8[ref["pk"]])
+    mask = forced(L.mask, w, h, torch.from_numpy(ref["mask"].astype(np.uint8)).cuda())
+    out, lse = sv.sparse_attn_fp8(q8, qe, k8, ke, t["vp"], t["pq"], t["oq"], t["ok"], t["km"], t["vm"], mask,
+                                  ref["scale"], want_lse=True)
+    rows = ref["rows"]
+    O, LSE = orc.attend(orc.dequantize_e4m3(cq8, eq), orc.dequantize_e4m3(ck8, ek), x["v"], ref["pq"], ref["oq"],
+                        ref["pk"], ref["ok"], ref["kbar"], ref["vbar"], ref["mask"], ref["scale"], rows=rows)
+    check_attention_rows(w, h, out, lse, O, LSE, rows)
+    qerr = np.abs(host(out[b, hh])[rows] - ref["O"][rows])
+    say(f"wan: fp8 vs unquantised attention on {rows.size} rows: max {qerr.max():.3e}, mean {qerr.mean():.3e}")

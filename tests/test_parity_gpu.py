@@ -523,3 +523,93 @@ def test_kmeanspp_edge_cases(sv):
         seeds, idx = orc.kmeanspp(Yr, words[0, 0, :C], C)
         np.testing.assert_array_equal(host(chosen)[0, 0], idx)
         assert len({int(i) // 60 for i in idx[:5]}) == 5
+
+
+# ------------------------------------------------------------------ FP8 variant
+@pytest.mark.parametrize("name", ["bf16-d128", "bf16-d64", "f32-d64"])
+def test_quantize_fp8_matches_oracle(sv, name):
+    """e4m3 codes and per-head exponents bit-exact (the scaling is exact and
+    both sides round to nearest even)."""
+    w, x = make(name)
+    BH = w.B * w.H
+    for key in ("q", "k"):
+        x8, ex = sv.quantize_fp8(to_dev(reshape4(x[key], w), w.dtype))
+        x8 = host(x8).reshape(BH, w.N, w.D)
+        ex = host(ex).reshape(BH)
+        for h in range(BH):
+            codes, e = orc.quantize_e4m3(x[key][h])
+            assert ex[h] == e
+            np.testing.assert_array_equal(x8[h], codes)
+
+
+def fp8_inputs(w, x, outs):
+    """Oracle e4m3 codes of Q and K per head (original order), their exponents
+    and dequantised values."""
+    BH = w.B * w.H
+    q8, k8, qe, ke, qd, kd = [], [], [], [], [], []
+    for h in range(BH):
+        cq, eq = orc.quantize_e4m3(x["q"][h])
+        ck, ek = orc.quantize_e4m3(x["k"][h])
+        q8.append(cq[outs[h]["pq"]])
+        k8.append(ck[outs[h]["pk"]])
+        qe.append(eq)
+        ke.append(ek)
+        qd.append(orc.dequantize_e4m3(cq, eq))
+        kd.append(orc.dequantize_e4m3(ck, ek))
+    dev8 = lambda a: torch.from_numpy(reshape4(np.stack(a), w)).cuda()
+    devi = lambda a: torch.tensor(np.array(a, np.int32).reshape(w.B, w.H)).cuda()
+    return dev8(q8), devi(qe), dev8(k8), devi(ke), qd, kd
+
+
+@pytest.mark.parametrize("name", ["bf16-d128", "bf16-d64"])
+@pytest.mark.parametrize("maskkind", ["routed", "dense", "none"])
+def test_sparse_attn_fp8_teacher_forced(sv, name, maskkind, ref_cache):
+    """FP8 attention against the oracle attending with the dequantised Q and
+    K (the same computation), at the bf16 path's tolerance; the error against
+    unquantised attention is reported."""
+    w, x, outs, sc = oracle_layer(name, ref_cache)
+    BH = w.B * w.H
+    m = np.stack([o["mask"] for o in outs])
+    if maskkind == "dense":
+        m = np.ones_like(m)
+    elif maskkind == "none":
+        m = np.zeros_like(m)
+    dev, m = attn_inputs(w, x, outs, m)
+    q8, qe, k8, ke, qd, kd = fp8_inputs(w, x, outs)
+    _, _, vp, pq, oq, ok, km, vm, mask = dev
+    out, lse = sv.sparse_attn_fp8(q8, qe, k8, ke, vp, pq, oq, ok, km, vm, mask, sc, want_lse=True)
+    out = host(out).reshape(BH, w.N, w.D)
+    lse = host(lse).reshape(BH, w.N)
+    amax, amean = ATOL["bf16"]
+    qerr = 0.0
+    for h in range(BH):
+        o = outs[h]
+        O, L = orc.attend(qd[h], kd[h], x["v"][h], o["pq"], o["oq"], o["pk"], o["ok"], o["kbar"], o["vbar"], m[h], sc)
+        err = np.abs(out[h] - O)
+        assert err.max() <= amax and err.mean() <= amean, (err.max(), err.mean())
+        assert np.abs(lse[h] - L).max() <= 1e-2
+        O0, _ = orc.attend(x["q"][h], x["k"][h], x["v"][h], o["pq"], o["oq"], o["pk"], o["ok"], o["kbar"],
+                           o["vbar"], m[h], sc)
+        qerr = max(qerr, float(np.abs(out[h] - O0).max()))
+    print(f"[fp8] {name}/{maskkind}: max |O_fp8 - O_unquantised| = {qerr:.3e}", flush=True)
+
+
+def test_sparse_attn_fp8_exact_codes_equal_bf16_path(sv, ref_cache):
+    """Inputs that are already e4m3 values with max|x| = 448 * 2^e quantise
+    exactly, so the FP8 path and the bf16 path attend to the same numbers."""
+    w, x, outs, sc = oracle_layer("bf16-d128", ref_cache)
+    BH = w.B * w.H
+    x2 = dict(x)
+    for key in ("q", "k"):
+        arr = []
+        for h in range(BH):
+            c, e = orc.quantize_e4m3(x[key][h])
+            arr.append(orc.dequantize_e4m3(c, e).astype(np.float32))
+        x2[key] = np.stack(arr)
+    dev, m = attn_inputs(w, x2, outs)
+    q8, qe, k8, ke, _, _ = fp8_inputs(w, x2, outs)
+    qp, kp, vp, pq, oq, ok, km, vm, mask = dev
+    o8, _ = sv.sparse_attn_fp8(q8, qe, k8, ke, vp, pq, oq, ok, km, vm, mask, sc)
+    ob, _ = sv.sparse_attn(qp, kp, vp, pq, oq, ok, km, vm, mask, sc)
+    d = (o8.float() - ob.float()).abs()
+    assert d.max().item() <= 2e-2 and d.mean().item() <= 2e-3
