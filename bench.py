@@ -40,6 +40,7 @@ ATTN_TRAFFIC = {
     "write_bytes": 0.774e9,
 }
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
 PEAK_F32_TFLOPS = 157.3
 
 
@@ -54,16 +55,44 @@ def parse():
     ap.add_argument("--attn-only", action="store_true", help="after one layer, time only the attention pass")
     ap.add_argument("--attn-reps", type=int, default=5)
     ap.add_argument("--no-variants", action="store_true", help="skip the variant-path timings")
+    ap.add_argument("--no-warm", action="store_true", help="skip the warm (cached-centroid) step timing")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="first run a plain device copy of this many MiB (calibrates HBM byte counters)")
     return ap.parse_args()
 
 
-def gen_inputs(w, heads):
+def gen_inputs(w, heads, step=0):
     from synth.gen import head_inputs
     with concurrent.futures.ThreadPoolExecutor(min(16, os.cpu_count() or 1)) as ex:
-        hs = list(ex.map(lambda h: head_inputs(w, h), range(heads)))
+        hs = list(ex.map(lambda h: head_inputs(w, h, step), range(heads)))
     return hs
+
+
+def stage_rooflines(w, stages, iters):
+    """Algorithmic rates of the non-attention stages against their bounds:
+    HBM bytes each stage must move (per the method, not per implementation) and
+    the k-means distance FLOPs."""
+    if not stages:
+        return {}
+    BH, N, D = w.B * w.H, w.N, w.D
+    el = 2 if w.dtype == "bf16" else 4
+    tensor = BH * N * D * el
+    out = {}
+    # centroids: gather-read and write Q, K, V once, read the permutations
+    cb = 3 * (2 * tensor + 4 * BH * N)
+    out["centroids_qkv"] = {"bound": "hbm", "bytes": cb, "GB_per_s": round(cb / (stages["centroids_qkv"] * 1e-3) / 1e9, 1),
+                            "frac": round(cb / (stages["centroids_qkv"] * 1e-3) / (PEAK_HBM_GBS * 1e9), 4)}
+    # route: read K' and V' once
+    rb = 2 * tensor
+    out["route"] = {"bound": "hbm", "bytes": rb, "GB_per_s": round(rb / (stages["route"] * 1e-3) / 1e9, 1),
+                    "frac": round(rb / (stages["route"] * 1e-3) / (PEAK_HBM_GBS * 1e9), 4)}
+    # k-means: 2 N C d FLOP per round for the distances
+    for which, C in (("kmeans_q", w.Cq), ("kmeans_k", w.Ck)):
+        fl = 2.0 * BH * N * C * D * iters
+        tf = fl / (stages[which] * 1e-3) / 1e12
+        out[which] = {"bound": "mfma", "flops": fl, "TFLOP_per_s": round(tf, 1),
+                      "frac": round(tf / PEAK_BF16_TFLOPS, 4), "ms_per_round": round(stages[which] / iters, 3)}
+    return out
 
 
 def to_device(hs, key, dtype, dev):
@@ -117,6 +146,36 @@ def cpu_baseline(w, h0, scale):
             "sample": f"1 of {heads} heads in full ({w.iters} Lloyd rounds of Q and K, permute, means, route, "
                       f"attention for all {w.N} rows), scaled x{heads}",
             "measured_s": round(sec, 2)}
+
+
+def warm_step(sv, L, w, cq, ck, scale, tdt, dev, ev, reps=5):
+    """The steady state of a denoising sequence: the next step's inputs (the
+    generator's drifted means) clustered with one round from the centroids
+    the cold step converged to (the centroid cache), then routed and attended."""
+    import torch
+    t0 = time.time()
+    hs = gen_inputs(w, w.B * w.H, step=1)
+    q1, k1, v1 = (to_device(hs, x, w.dtype, dev) for x in ("q", "k", "v"))
+    del hs
+    print(f"# next-step inputs generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    cq_cache, ck_cache = cq.clone(), ck.clone()
+    cqw, ckw = cq.clone(), ck.clone()
+
+    def one():
+        cqw.copy_(cq_cache)
+        ckw.copy_(ck_cache)
+        L.forward(q1, k1, v1, cqw, ckw, 1, w.density, scale)
+
+    one()
+    a, b = ev(), ev()
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        one()
+    b.record()
+    torch.cuda.synchronize()
+    return {"ms": round(a.elapsed_time(b) / reps, 3), "kmeans_rounds": 1, "steps": reps,
+            "inputs": "next denoising step (means drifted by 0.02 N(0, 1)), centroids cached from the cold step"}
 
 
 def variants(sv, L, w, q, k, scale, ev, reps=5, top_p=0.9):
@@ -303,9 +362,12 @@ def main():
                      "traffic": attn_traffic(w.name, not args.heads), "traffic_unit": "HBM bytes per launch",
                      "launch_ms": round(t_attn, 3), "flops_per_launch": flops},
         "stages_ms": stages,
+        "stage_rooflines": stage_rooflines(w, stages, w.iters),
         "realized_density": round(pairs_sel / (BH * float(w.N) ** 2), 4),
         "pseudo_pair_fraction": round(pairs_comp / max(1, pairs_sel + pairs_comp), 4),
     }
+    if not args.attn_only and not args.no_warm:
+        res["warm_step"] = warm_step(sv, L, w, cq, ck, scale, tdt, dev, ev)
     if not args.attn_only and not args.no_variants:
         res["variants"] = variants(sv, L, w, q, k, scale, ev)
     if not args.no_cpu_baseline and not args.attn_only:
