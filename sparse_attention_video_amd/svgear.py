@@ -376,9 +376,19 @@ class Layer:
         self.ws_k = _workspace(lib.svgear_kmeans_workspace(B, H, N, D, Ck), dev)
         self.side = torch.cuda.Stream(device=dev)
 
-    def forward(self, q, k, v, cq, ck, iters, density, scale=None):
+    def forward(self, q, k, v, cq, ck, iters, density, scale=None, top_p=None, router="error", strength=0.0,
+                fp8=False):
+        """One layer.  Variants (default off): ``top_p`` routes under the SVG2
+        top-p budget instead of ``density`` (``router`` "error": SVG-EAR spends
+        the budget by error; "score": SVG2's own router); ``strength`` > 0
+        adds the variance-corrected compensation (bf16); ``fp8`` runs the
+        attention with e4m3 Q'/K'."""
         B, H, N, D, Cq, Ck = self.shape
         scale = 1.0 / math.sqrt(D) if scale is None else scale
+        if router not in ("error", "score"):
+            raise ValueError("router must be 'error' or 'score'")
+        if fp8 and strength > 0.0:
+            raise ValueError("the FP8 variant has no variance-corrected form")
         main = torch.cuda.current_stream(self.side.device)
         self.side.wait_stream(main)
         with torch.cuda.stream(self.side):
@@ -388,8 +398,31 @@ class Layer:
         centroids(q, self.pq, self.oq, x_perm=self.qp, means=self.qm, ws=self.ws)
         centroids(k, self.pk, self.ok, x_perm=self.kp, means=self.km, ws=self.ws)
         centroids(v, self.pk, self.ok, x_perm=self.vp, means=self.vm, ws=self.ws)
-        route(self.qm, self.oq, self.kp, self.vp, self.km, self.vm, self.ok, scale, density, mask=self.mask,
-              scores=self.scores, ws=self.ws)
-        sparse_attn(self.qp, self.kp, self.vp, self.pq, self.oq, self.ok, self.km, self.vm, self.mask, scale,
-                    out=self.out, ws=self.ws)
+        if top_p is None:
+            route(self.qm, self.oq, self.kp, self.vp, self.km, self.vm, self.ok, scale, density, mask=self.mask,
+                  scores=self.scores, ws=self.ws)
+        else:
+            _, _, _, m = route_topp(self.qm, self.oq, self.kp, self.vp, self.km, self.vm, self.ok, scale, top_p,
+                                    error_ranked=(router == "error"), want_probs=False, want_budget=False,
+                                    ws=self.ws)
+            self.mask.copy_(m)
+        if fp8:
+            if not hasattr(self, "q8"):
+                self.q8 = torch.empty(self.qp.shape, dtype=torch.uint8, device=self.qp.device)
+                self.k8 = torch.empty_like(self.q8)
+                self.qe = torch.empty((B, H), dtype=torch.int32, device=self.qp.device)
+                self.ke = torch.empty_like(self.qe)
+            quantize_fp8(self.qp, x8=self.q8, exps=self.qe)
+            quantize_fp8(self.kp, x8=self.k8, exps=self.ke)
+            sparse_attn_fp8(self.q8, self.qe, self.k8, self.ke, self.vp, self.pq, self.oq, self.ok, self.km,
+                            self.vm, self.mask, scale, out=self.out, ws=self.ws)
+        elif strength > 0.0:
+            if not hasattr(self, "kv"):
+                self.kv = torch.empty_like(self.km)
+            centroid_variances(k, self.pk, self.ok, self.km, vars=self.kv, ws=self.ws)
+            sparse_attn(self.qp, self.kp, self.vp, self.pq, self.oq, self.ok, self.km, self.vm, self.mask, scale,
+                        out=self.out, ws=self.ws, k_vars=self.kv, strength=strength)
+        else:
+            sparse_attn(self.qp, self.kp, self.vp, self.pq, self.oq, self.ok, self.km, self.vm, self.mask, scale,
+                        out=self.out, ws=self.ws)
         return self.out

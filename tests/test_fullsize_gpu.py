@@ -318,6 +318,24 @@ def test_full_density_sweep(sv):
     qs, ks = np.diff(ref["oq"]), np.diff(ref["ok"])
     b, hh = bh_index(w, h)
     rows = ref["rows"]
+    # diagnostic (not gated; the pages compare the two rankings only on real
+    # models): the error-ranked mask against SVG2's score ranking (estimated
+    # share P') at the same key budget, and each one's attention error against
+    # full attention on the sampled rows
+    O_full = orc.full_attention(x["q"][rows], x["k"], x["v"], ref["scale"])
+    P_s = orc.topp_probs(ref["qbar"], ref["kbar"], ks, ref["scale"])
+    for rho in (0.10, 0.25):
+        m_err = orc.select(ref["ratio"], qs, ks, rho, w.N)
+        m_sc = orc.select(P_s, qs, ks, rho, w.N)
+        pairs = lambda m: (qs[:, None] * m * ks[None, :]).astype(np.float64)
+        overlap = float((pairs(m_err & m_sc)).sum() / pairs(m_err).sum())
+        mse = {}
+        for name_, m_ in (("error", m_err), ("score", m_sc)):
+            O_, _ = orc.attend(x["q"], x["k"], x["v"], ref["pq"], ref["oq"], ref["pk"], ref["ok"], ref["kbar"],
+                               ref["vbar"], m_, ref["scale"], rows=rows)
+            mse[name_] = float(((O_[rows] - O_full) ** 2).mean())
+        say(f"sweep: density {rho}: error-ranked vs score-ranked masks share {overlap:.3f} of the pairs; "
+            f"attention MSE vs full: error-ranked {mse['error']:.3e}, score-ranked {mse['score']:.3e}")
     for rho in w.densities:
         m_o = orc.select(ref["ratio"], qs, ks, rho, w.N)
         ndiff = check_route(sv, w, h, t, ref, rho, mask_ref=m_o)

@@ -613,3 +613,40 @@ def test_sparse_attn_fp8_exact_codes_equal_bf16_path(sv, ref_cache):
     ob, _ = sv.sparse_attn(qp, kp, vp, pq, oq, ok, km, vm, mask, sc)
     d = (o8.float() - ob.float()).abs()
     assert d.max().item() <= 2e-2 and d.mean().item() <= 2e-3
+
+
+@pytest.mark.parametrize("variant", ["topp-error", "topp-score", "variance", "fp8"])
+def test_layer_variants_are_the_composed_calls(sv, variant):
+    """Layer.forward with a variant option gives bit for bit what the
+    individual calls give in sequence (every call is deterministic)."""
+    w, x = make("bf16-d128")
+    sc = 1.0 / np.sqrt(w.D)
+    q, k, v = (to_dev(reshape4(x[key], w), "bf16") for key in ("q", "k", "v"))
+    cq0, ck0 = f32(reshape4(x["cq0"], w)), f32(reshape4(x["ck0"], w))
+    opts = {"topp-error": dict(top_p=0.9), "topp-score": dict(top_p=0.9, router="score"),
+            "variance": dict(strength=1.0), "fp8": dict(fp8=True)}[variant]
+    L = sv.Layer(w.B, w.H, w.N, w.D, w.Cq, w.Ck)
+    out = L.forward(q, k, v, cq0.clone(), ck0.clone(), 3, 0.3, sc, **opts).clone()
+    cq, ck = cq0.clone(), ck0.clone()
+    shp = lambda *s_, dt=torch.int32: torch.empty(s_, dtype=dt, device="cuda")
+    lq, pq, oq = shp(w.B, w.H, w.N), shp(w.B, w.H, w.N), shp(w.B, w.H, w.Cq + 1)
+    lk, pk, ok = shp(w.B, w.H, w.N), shp(w.B, w.H, w.N), shp(w.B, w.H, w.Ck + 1)
+    sv.kmeans(k, ck, 3, lk, pk, ok)
+    sv.kmeans(q, cq, 3, lq, pq, oq)
+    qp, qm = sv.centroids(q, pq, oq)
+    kp, km = sv.centroids(k, pk, ok)
+    vp, vm = sv.centroids(v, pk, ok)
+    if "top_p" in opts:
+        _, _, _, mask = sv.route_topp(qm, oq, kp, vp, km, vm, ok, sc, 0.9, error_ranked=(variant == "topp-error"))
+    else:
+        _, mask = sv.route(qm, oq, kp, vp, km, vm, ok, sc, 0.3)
+    if variant == "fp8":
+        q8, qe = sv.quantize_fp8(qp)
+        k8, ke = sv.quantize_fp8(kp)
+        ref, _ = sv.sparse_attn_fp8(q8, qe, k8, ke, vp, pq, oq, ok, km, vm, mask, sc)
+    elif variant == "variance":
+        kv = sv.centroid_variances(k, pk, ok, km)
+        ref, _ = sv.sparse_attn(qp, kp, vp, pq, oq, ok, km, vm, mask, sc, k_vars=kv, strength=1.0)
+    else:
+        ref, _ = sv.sparse_attn(qp, kp, vp, pq, oq, ok, km, vm, mask, sc)
+    assert torch.equal(out, ref)
