@@ -116,9 +116,25 @@ __global__ void __launch_bounds__(PP_TILE) pp_dist_kernel(const T* __restrict__ 
   const int t0 = tile * PP_TILE;
   const int rows = min(PP_TILE, N - t0);
   const char* src = reinterpret_cast<const char*>(x + ((size_t)bh * N + t0) * D);
-  for (int u = tid; u < rows * CPR; u += PP_TILE) {
-    const int r = u / CPR, cc = u - r * CPR;
-    *reinterpret_cast<u32x4*>(s_x + r * ST + cc * 16) = *reinterpret_cast<const u32x4*>(src + (size_t)u * 16);
+  // all of a thread's 16-byte loads of a batch are issued before any is stored
+  constexpr int PER = PP_TILE * CPR / PP_TILE;  // chunks per thread (CPR)
+  constexpr int BATCH = PER < 16 ? PER : 16;
+#pragma unroll
+  for (int b0 = 0; b0 < PER; b0 += BATCH) {
+    u32x4 v[BATCH];
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i) {
+      const int u = tid + (b0 + i) * PP_TILE;
+      v[i] = u < rows * CPR ? *reinterpret_cast<const u32x4*>(src + (size_t)u * 16) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i) {
+      const int u = tid + (b0 + i) * PP_TILE;
+      if (u < rows * CPR) {
+        const int r = u / CPR, cc = u - r * CPR;
+        *reinterpret_cast<u32x4*>(s_x + r * ST + cc * 16) = v[i];
+      }
+    }
   }
   __syncthreads();
   const int t = t0 + tid;
