@@ -423,7 +423,17 @@ __global__ void __launch_bounds__(256) km_hist_kernel(const int32_t* __restrict_
   __syncthreads();
   const int n0 = tile * SORT_TILE, n1 = min(N, n0 + SORT_TILE);
   const int32_t* lb = labels + (size_t)bh * N;
-  for (int n = n0 + threadIdx.x; n < n1; n += 256) atomicAdd(&h[lb[n]], 1);
+  // all of a thread's labels are loaded before the first count
+  constexpr int PER = SORT_TILE / 256;
+  int lab[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int n = n0 + threadIdx.x + 256 * i;
+    lab[i] = n < n1 ? lb[n] : -1;
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    if (lab[i] >= 0) atomicAdd(&h[lab[i]], 1);
   __syncthreads();
   int32_t* cnt = counts + ((size_t)bh * ntiles + tile) * C;
   for (int c = threadIdx.x; c < C; c += 256) cnt[c] = h[c];
@@ -440,17 +450,29 @@ __global__ void __launch_bounds__(1024) km_scan_kernel(int32_t* __restrict__ cou
   const int bh = blockIdx.x;
   if (threadIdx.x == 0) nmax[bh] = 0u;  // the assign kernel of this round has finished
   int32_t* cnt = counts + (size_t)bh * ntiles * C;
-  int tot[4], nch[4];
+  // the tile loops load SB tiles of all 4 clusters before using any, so the
+  // loads are in flight together rather than one latency each
+  constexpr int SB = 8;
+  int tot[4] = {0, 0, 0, 0}, nch[4];
   int sum = 0, csum = 0;
+  for (int t0 = 0; t0 < ntiles; t0 += SB) {
+    int v[4][SB];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int i = 0; i < SB; ++i) {
+        const int c = threadIdx.x * 4 + e;
+        v[e][i] = (c < C && t0 + i < ntiles) ? cnt[(size_t)(t0 + i) * C + c] : 0;
+      }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int i = 0; i < SB; ++i) tot[e] += v[e][i];
+  }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const int c = threadIdx.x * 4 + e;
-    int s = 0;
-    if (c < C)
-      for (int t = 0; t < ntiles; ++t) s += cnt[(size_t)t * C + c];
-    tot[e] = s;
-    nch[e] = (s + rows - 1) / rows;
-    sum += s;
+    nch[e] = (tot[e] + rows - 1) / rows;
+    sum += tot[e];
     csum += nch[e];
   }
   int total, ctotal;
@@ -458,21 +480,35 @@ __global__ void __launch_bounds__(1024) km_scan_kernel(int32_t* __restrict__ cou
   int cbase = block_exscan(csum, sm, &ctotal);
   int32_t* off = offsets + (size_t)bh * (C + 1);
   int32_t* cs = chunk_start + (size_t)bh * (C + 1);
+  int b[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int c = threadIdx.x * 4 + e;
     if (c < C) {
       off[c] = base;
       cs[c] = cbase;
-      int b = base;
-      for (int t = 0; t < ntiles; ++t) {
-        const int v = cnt[(size_t)t * C + c];
-        cnt[(size_t)t * C + c] = b;
-        b += v;
-      }
     }
+    b[e] = base;
     base += tot[e];
     cbase += nch[e];
+  }
+  for (int t0 = 0; t0 < ntiles; t0 += SB) {
+    int v[4][SB];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int i = 0; i < SB; ++i) {
+        const int c = threadIdx.x * 4 + e;
+        v[e][i] = (c < C && t0 + i < ntiles) ? cnt[(size_t)(t0 + i) * C + c] : 0;
+      }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+#pragma unroll
+      for (int i = 0; i < SB; ++i) {
+        const int c = threadIdx.x * 4 + e;
+        if (c < C && t0 + i < ntiles) cnt[(size_t)(t0 + i) * C + c] = b[e];
+        b[e] += v[e][i];
+      }
   }
   if (threadIdx.x == 0) {
     off[C] = total;
@@ -499,11 +535,22 @@ __global__ void __launch_bounds__(256) km_scatter_kernel(const int32_t* __restri
   const int q1 = min(N, q0 + SORT_TILE / 4);
   int32_t* mine = hw + w * C;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  // the wave's labels are loaded once, before either pass
+  constexpr int STEPS = SORT_TILE / 4 / SV_WAVE;
+  int labv[STEPS];
+#pragma unroll
+  for (int i = 0; i < STEPS; ++i) {
+    const int n = q0 + i * SV_WAVE + lane;
+    labv[i] = n < q1 ? lb[n] : 0;
+  }
   for (int pass = 0; pass < 2; ++pass) {
-    for (int n0 = q0; n0 < q1; n0 += SV_WAVE) {
+#pragma unroll
+    for (int i = 0; i < STEPS; ++i) {
+      const int n0 = q0 + i * SV_WAVE;
+      if (n0 >= q1) break;
       const int n = n0 + lane;
       const bool ok = n < q1;
-      const int lab = ok ? lb[n] : 0;
+      const int lab = labv[i];
       uint64_t peers = ballot(ok);
       for (int b = 0; b < ib; ++b) {
         const bool bit = (lab >> b) & 1;
@@ -628,8 +675,19 @@ __global__ void __launch_bounds__(256) km_finalize_kernel(const float* __restric
     if (!keep_empty) *out = 0.f;
     return;
   }
+  // chunks added in order; eight loads are issued before their adds
   float s = 0.f;
-  for (int k = cs[c]; k < cs[c + 1]; ++k) s += partial[((size_t)bh * maxch + k) * D + d];
+  int k = cs[c];
+  const int k1 = cs[c + 1];
+  const float* pp = partial + (size_t)bh * maxch * D + d;
+  for (; k + 8 <= k1; k += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = pp[(size_t)(k + j) * D];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s += v[j];
+  }
+  for (; k < k1; ++k) s += pp[(size_t)k * D];
   *out = s / (float)n;
 }
 
