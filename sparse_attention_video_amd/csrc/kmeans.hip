@@ -47,7 +47,17 @@ __global__ void __launch_bounds__(256) km_prep_kernel(const float* __restrict__ 
   const int bh = blockIdx.y, lane = lane_id(), w = wave_id();
   const float* cb = cent + (size_t)bh * C * D;
   double wmax = 0.0;
-  for (int rr = 0; rr < KM_PREP_ROWS / 4; ++rr) {
+  // the wave's rows are loaded before the first one is processed
+  constexpr int RR = KM_PREP_ROWS / 4;
+  float vals[RR][EPL];
+#pragma unroll
+  for (int rr = 0; rr < RR; ++rr) {
+    const int c = blockIdx.x * KM_PREP_ROWS + rr * 4 + w;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) vals[rr][e] = c < C ? cb[(size_t)c * D + lane + e * SV_WAVE] : 0.f;
+  }
+#pragma unroll
+  for (int rr = 0; rr < RR; ++rr) {
     const int c = blockIdx.x * KM_PREP_ROWS + rr * 4 + w;
     if (c >= Cpad) break;
     bf16* row = ops + ((size_t)bh * Cpad + c) * RW;
@@ -55,7 +65,7 @@ __global__ void __launch_bounds__(256) km_prep_kernel(const float* __restrict__ 
 #pragma unroll
     for (int e = 0; e < EPL; ++e) {
       const int d = lane + e * SV_WAVE;
-      const float v = c < C ? cb[(size_t)c * D + d] : 0.f;
+      const float v = vals[rr][e];
       bf16 hi, lo;
       split_bf16(-2.f * v, hi, lo);
       row[d] = hi;

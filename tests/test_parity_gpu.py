@@ -650,3 +650,41 @@ def test_layer_variants_are_the_composed_calls(sv, variant):
     else:
         ref, _ = sv.sparse_attn(qp, kp, vp, pq, oq, ok, km, vm, mask, sc)
     assert torch.equal(out, ref)
+
+
+def test_maximum_cluster_counts(sv):
+    """C_q = C_k = 4096, the largest count any call accepts, on 8,192 tokens
+    (clusters of one or two tokens): one k-means round, centroids, routing and
+    attention, each stage fed the oracle's previous stage."""
+    from synth.gen import layer_inputs
+    w = scaled(WORKLOADS["tiny"], B=1, H=1, N=8192, D=64, dtype="bf16", comps=64, zipf=1.1, Cq=4096, Ck=4096,
+               seed=23, density=0.3)
+    x = layer_inputs(w)
+    sc = 1.0 / 8.0
+    o = orc.layer(x["q"][0], x["k"][0], x["v"][0], x["cq0"][0], x["ck0"][0], 1, 0.3, sc)
+    dev = {key: to_dev(x[key][0][None, None], "bf16") for key in ("q", "k", "v")}
+    for which, C0, lkey, pkey, okey in (("q", x["cq0"][0], "lq", "pq", "oq"), ("k", x["ck0"][0], "lk", "pk", "ok")):
+        lab, perm, off = sv.kmeans(dev[which], f32(C0[None, None]), 1)
+        nbad = check_labels_near_ties(x[which][0], C0, host(lab)[0, 0], o[lkey])
+        if nbad == 0:
+            np.testing.assert_array_equal(host(perm)[0, 0], o[pkey])
+            np.testing.assert_array_equal(host(off)[0, 0], o[okey])
+    pq, oq, pk, ok = (i32(o[key][None, None]) for key in ("pq", "oq", "pk", "ok"))
+    qp, qm = sv.centroids(dev["q"], pq, oq)
+    kp, km = sv.centroids(dev["k"], pk, ok)
+    vp, vm = sv.centroids(dev["v"], pk, ok)
+    for mu, key, X, perm, off in ((qm, "qbar", x["q"][0], o["pq"], o["oq"]), (km, "kbar", x["k"][0], o["pk"], o["ok"]),
+                                  (vm, "vbar", x["v"][0], o["pk"], o["ok"])):
+        err = np.abs(host(mu)[0, 0] - o[key]).max(axis=1)
+        assert (err <= mean_bound(X, perm, off) + 1e-30).all()
+    qbar, kbar, vbar = (f32(o[key][None, None]) for key in ("qbar", "kbar", "vbar"))
+    _, mask = sv.route(qbar, oq, kp, vp, kbar, vbar, ok, sc, 0.3, scores_in=f32(o["ratio"][None, None]))
+    np.testing.assert_array_equal(host(mask)[0, 0], o["mask"])
+    scores, _ = sv.route(qbar, oq, kp, vp, kbar, vbar, ok, sc, 0.3)
+    r_o = o["ratio"].astype(np.float64)
+    rowmax = r_o.max(axis=1, keepdims=True)
+    assert (np.abs(host(scores)[0, 0] - r_o) <= 2e-3 * r_o + 1e-7 * rowmax + 1e-37).all()
+    m = torch.from_numpy(o["mask"][None, None].astype(np.uint8)).cuda()
+    out, _ = sv.sparse_attn(qp, kp, vp, pq, oq, ok, kbar, vbar, m, sc)
+    err = np.abs(host(out)[0, 0] - o["O"])
+    assert err.max() <= 2e-2 and err.mean() <= 2e-3, (err.max(), err.mean())
