@@ -392,9 +392,12 @@ __global__ void __launch_bounds__(256) attn_kernel(const T* __restrict__ qp, con
 // ---------------------------------------------------------------------------
 // bf16 path.  Same algorithm, arranged for throughput on gfx950:
 //  * K and V rows go straight from global memory into LDS
-//    (global_load_lds_dwordx4, no registers); the source row of every key
-//    position of a tile comes from a small table that wave 0 fills two tiles
-//    ahead by walking the selected-cluster list;
+//    (buffer_load_dwordx4 ... lds, no registers); each lane follows the key
+//    positions it loads with its own cursor over the selected-cluster list;
+//  * the exposed cost inside a tile is LDS latency (the LDS itself is ~30%
+//    busy), so K fragments are read two steps ahead of their products and
+//    the V^T fragments of each 16-key step one step ahead, the order pinned
+//    with scheduling groups;
 //  * tiles are unpadded, 16-byte chunks swizzled per row (see below); the
 //    S^T = K Q^T fragments are plain 16-byte reads, and the V^T fragments of
 //    O^T = V^T P^T come from row-major V through the transposing LDS read
@@ -426,9 +429,15 @@ typedef __bf16 at_bf16x2 __attribute__((ext_vector_type(2)));
 #define AT_LDS16(p) ((__attribute__((address_space(3))) bf16x4*)(p))
 
 // 16 bytes per lane from global memory straight into LDS: lane L's bytes land
-// at dst + 16 L (dst is the same for the whole wave)
-__device__ __forceinline__ void load_lds16(const char* src, char* dst) {
-  __builtin_amdgcn_global_load_lds(src, AT_LDS(dst), 16, 0, 0);
+// at dst + 16 L (dst is the same for the whole wave).  The buffer form is
+// counted on the vector-memory counter alone; the global (flat) form would
+// also make every later LDS-read wait a full drain, which defeats reading
+// fragments ahead.  Word 3 = 0x00020000: 32-bit data format, raw access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t lds_src(const char* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, 0x00020000);
+}
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t src, uint32_t off, char* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(src, AT_LDS(dst), 16, (int)off, 0, 0, 0);
 }
 
 // A fragment of V^T (8 keys at one dim) from two transposing reads of 4 keys each
@@ -675,19 +684,20 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
       rowoff[j] = (uint32_t)(p < nkeys ? uc_base + (p - uc_pre) : 0) * (uint32_t)T8::ROWB;
     }
   };
-  // a 32-bit per-lane offset from the head's base keeps the loads in the
-  // scalar-base form (4 address bytes per lane instead of 8)
+  // a 32-bit per-lane offset from the head's base (4 address bytes per lane)
+  const __amdgpu_buffer_rsrc_t rK = lds_src(kb, N * D * (F8 ? 1 : 2));
+  const __amdgpu_buffer_rsrc_t rV = lds_src(vb, N * D * 2);
   auto issue = [&](const uint32_t* rowoff, const uint32_t* rowoff8, char* dK, char* dV) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int g = w * NI + i;
-      if constexpr (!F8) load_lds16(kb + (uint32_t)(rowoff[i] + (uint32_t)(chK[i] << 4)), dK + g * 1024);
-      load_lds16(vb + (uint32_t)(rowoff[i] + (uint32_t)(chV << 4)), dV + g * 1024);
+      if constexpr (!F8) load_lds16(rK, rowoff[i] + (uint32_t)(chK[i] << 4), dK + g * 1024);
+      load_lds16(rV, rowoff[i] + (uint32_t)(chV << 4), dV + g * 1024);
     }
     if constexpr (F8) {
 #pragma unroll
       for (int j = 0; j < T8::NI; ++j)
-        load_lds16(kb + (uint32_t)(rowoff8[j] + (uint32_t)(chK8[j] << 4)), dK + (w * T8::NI + j) * 1024);
+        load_lds16(rK, rowoff8[j] + (uint32_t)(chK8[j] << 4), dK + (w * T8::NI + j) * 1024);
     }
   };
 
@@ -712,21 +722,42 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
           s[sub] = mfma_fp8(fa, bq8[kk], s[sub]);
         }
     } else {
-      // fragments of step ks + 1 are read before the products of step ks
-      bf16x8 fr[2][2];
-      fr[0][0] = *reinterpret_cast<const bf16x8*>(Kh + aK[0]);
-      fr[0][1] = *reinterpret_cast<const bf16x8*>(Kh + aK[0] + 32 * ROWB);
+      // fragments of step ks + 2 are read before the products of step ks
+      // (LDS latency exceeds the two products of one step)
+      bf16x8 fr[3][2];
+#pragma unroll
+      for (int ks = 0; ks < 2 && ks < KS; ++ks) {
+        fr[ks][0] = *reinterpret_cast<const bf16x8*>(Kh + aK[ks]);
+        fr[ks][1] = *reinterpret_cast<const bf16x8*>(Kh + aK[ks] + 32 * ROWB);
+      }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        if (ks + 1 < KS) {
-          fr[(ks + 1) & 1][0] = *reinterpret_cast<const bf16x8*>(Kh + aK[ks + 1]);
-          fr[(ks + 1) & 1][1] = *reinterpret_cast<const bf16x8*>(Kh + aK[ks + 1] + 32 * ROWB);
+        if (ks + 2 < KS) {
+          fr[(ks + 2) % 3][0] = *reinterpret_cast<const bf16x8*>(Kh + aK[ks + 2]);
+          fr[(ks + 2) % 3][1] = *reinterpret_cast<const bf16x8*>(Kh + aK[ks + 2] + 32 * ROWB);
         }
-        s[0] = mfma_bf16(fr[ks & 1][0], bq[ks], s[0]);
-        s[1] = mfma_bf16(fr[ks & 1][1], bq[ks], s[1]);
+        s[0] = mfma_bf16(fr[ks % 3][0], bq[ks], s[0]);
+        s[1] = mfma_bf16(fr[ks % 3][1], bq[ks], s[1]);
       }
     }
+    // V^T fragments of the first 16 keys: read now, used after the softmax
+    bf16x8 vf[2][DT];
+    if (!pseudo) {
+#pragma unroll
+      for (int t = 0; t < DT; ++t) vf[0][t] = vt_frag(Vh + aV[t], Vh + aV[t] + 8 * ROWB);
+    }
     mid();  // straight-line work that overlaps the products in flight
+    if (!F8 && !pseudo) {
+      // keep the read-ahead: the scheduler would otherwise sink each read to
+      // just before its product (mask bits: 0x100 LDS read, 0x008 MFMA)
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if (ks + 2 < KS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * DT, 0);
+    }
     if (pseudo) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
@@ -784,14 +815,33 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
         const at_bf16x2 pr = {pb[2 * e], pb[2 * e + 1]};
         l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
       }
+      if (pseudo) {
 #pragma unroll
-      for (int t = 0; t < DT; ++t) {
-        const char* base = Vh + aV[t] + 16 * st * ROWB;
-        o[t] = mfma_bf16(vt_frag(base, base + 8 * ROWB), pb, o[t]);
-        if (pseudo) {
+        for (int t = 0; t < DT; ++t) {
+          const char* base = Vh + aV[t] + 16 * st * ROWB;
+          o[t] = mfma_bf16(vt_frag(base, base + 8 * ROWB), pb, o[t]);
           const char* bl = sV1 + aV[t] + 16 * st * ROWB;
           o[t] = mfma_bf16(vt_frag(bl, bl + 8 * ROWB), pb, o[t]);
         }
+      } else {
+        // the next 16 keys' fragments are read before these products
+        if (st + 1 < 4) {
+#pragma unroll
+          for (int t = 0; t < DT; ++t) {
+            const char* base = Vh + aV[t] + 16 * (st + 1) * ROWB;
+            vf[(st + 1) & 1][t] = vt_frag(base, base + 8 * ROWB);
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < DT; ++t) o[t] = mfma_bf16(vf[st & 1][t], pb, o[t]);
+      }
+    }
+    if (!pseudo) {
+      // the next step's V^T reads go out before this step's products
+#pragma unroll
+      for (int st = 0; st < 4; ++st) {
+        if (st + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 2 * DT, 1);
+        __builtin_amdgcn_sched_group_barrier(0x008, DT, 1);
       }
     }
   };
