@@ -125,10 +125,13 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) 
   constexpr int RW = km_row<D>();          // operand row (bf16 elements)
   constexpr int SR = RW + 8;               // LDS row stride: an odd multiple of 16 bytes
   constexpr int U = RW / 8;                // 16-byte units per row
-  constexpr int NU = (32 * U + 255) / 256; // units per thread per 32-row chunk
-  __shared__ __attribute__((aligned(16))) bf16 s_ops[2][32 * SR];
+  constexpr int CHB = 32 * SR * 2;         // bytes of one staged chunk in LDS
+  constexpr int NJ = (CHB + 1023) / 1024;  // 1 KB direct-to-LDS loads per chunk
+  constexpr int NJW = (NJ + 3) / 4;        // per wave (load j = 4 k + wave)
+  __shared__ __attribute__((aligned(1024))) bf16 s_ops[2][NJ * 512];
 
-  const int bh = blockIdx.y, tid = threadIdx.x, lane = lane_id(), w = wave_id();
+  const int bh = blockIdx.y, tid = threadIdx.x, lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(wave_id());
   const int half = lane >> 5, col = lane & 31;
   const T* xb = x + (size_t)bh * N * D;
   const bf16* ob = ops + (size_t)bh * Cpad * RW;
@@ -187,30 +190,32 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) 
 #pragma unroll
     for (int k = 0; k < 4; ++k) key[t][k] = FLT_MAX;
 
-  // chunk staging: thread tid moves units tid + 256 k of the chunk (row, 16-byte
-  // column); offsets are fixed per thread, so loads are unconditional (a
-  // thread past the end reloads unit 0 and skips its store)
-  int goff[NU], loff[NU];
-  bool uok[NU];
+  // chunk staging straight from global memory into LDS (no registers): a
+  // chunk is 32 contiguous operand rows in global memory and 32 rows of
+  // stride SR in LDS.  Load j fills LDS bytes [1024 j, 1024 j + 1024) of the
+  // buffer, lane L the 16 bytes at o = 1024 j + 16 L: byte o % (2 SR) of row
+  // o / (2 SR).  Pad bytes (never read) take the chunk's first 16 bytes.
+  // The buffer form keeps the LDS-read waits of the products partial.
+  uint32_t goff[NJW];
 #pragma unroll
-  for (int k = 0; k < NU; ++k) {
-    const int v = tid + 256 * k;
-    uok[k] = v < 32 * U;
-    const int r = uok[k] ? v / U : 0, cu = uok[k] ? v - (v / U) * U : 0;
-    goff[k] = r * RW + cu * 8;
-    loff[k] = r * SR + cu * 8;
+  for (int k = 0; k < NJW; ++k) {
+    const int o = 1024 * (4 * k + w) + 16 * lane;
+    const int r = o / (2 * SR), cb = o - r * (2 * SR);
+    goff[k] = (o < CHB && cb < 2 * RW) ? (uint32_t)(r * 2 * RW + cb) : 0u;
   }
-  u32x4 pre[NU];
-  auto fetch = [&](int c0) {
-    const bf16* base = ob + (size_t)c0 * RW;
+  const __amdgpu_buffer_rsrc_t rops =
+      __builtin_amdgcn_make_buffer_rsrc((void*)ob, (short)0, Cpad * RW * 2, 0x00020000);
+  auto stage = [&](int c0, int buf) {
 #pragma unroll
-    for (int k = 0; k < NU; ++k) pre[k] = ld16(base + goff[k]);
+    for (int k = 0; k < NJW; ++k)
+      if (4 * k + w < NJ)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rops, (__attribute__((address_space(3))) void*)(&s_ops[buf][512 * (4 * k + w)]), 16, (int)goff[k],
+            c0 * RW * 2, 0, 0);
   };
-  auto store = [&](int buf) {
-#pragma unroll
-    for (int k = 0; k < NU; ++k)
-      if (uok[k]) st16(&s_ops[buf][loff[k]], pre[k]);
-  };
+  // this wave's staging loads have landed (vector-memory count 0; the export
+  // and LDS counts left at their maxima)
+  auto staged = [] { __builtin_amdgcn_s_waitcnt(0x0F70); };
 
   // extra K slots of the token side: (||x||^2 hi, lo, offset, 1, 1, 1)
   // the offset keeps V positive; it is set from a first window estimate below
@@ -218,8 +223,8 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) 
   const int kprod = D * (F32 ? 3 : 2) + KM_EXTRA;
   const float gam = (kprod * u) / (1.f - kprod * u);
   const int nchunk = Cpad / 32;
-  fetch(0);
-  store(0);
+  stage(0, 0);
+  staged();
   __syncthreads();
   const float cm_pre = sqrtf(__uint_as_float(nmax[bh])) * (1.f + 1e-5f);
   float E0[2], off[2];
@@ -248,30 +253,46 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) 
   }
   const float q = ldexpf(1.f, ib - 23);
 
+  // step i of the 2 KS + 1 products: the extra slots (i = 0), the hi part of
+  // -2c (1 .. KS), the lo part (KS + 1 .. 2 KS); each step's centroid
+  // fragment is read two steps ahead (LDS latency exceeds one step's products)
+  constexpr int NSTEP = 2 * KS + 1;
+  auto frag_off = [&](int i) {
+    return (i == 0 ? D : i <= KS ? 16 * (i - 1) : D + KM_EXTRA + 16 * (i - 1 - KS)) + 8 * half;
+  };
   auto mma = [&](int buf, f32x16& acc0, f32x16& acc1) {
     const bf16* R = &s_ops[buf][col * SR];
     acc0 = f32x16{};
     acc1 = f32x16{};
-    {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(R + D + 8 * half);
-      acc0 = mfma_bf16(a, bext[0], acc0);
-      acc1 = mfma_bf16(a, bext[1], acc1);
-    }
+    bf16x8 fr[3];
+    fr[0] = *reinterpret_cast<const bf16x8*>(R + frag_off(0));
+    fr[1] = *reinterpret_cast<const bf16x8*>(R + frag_off(1));
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(R + 16 * ks + 8 * half);
-      acc0 = mfma_bf16(a, bx[0][ks], acc0);
-      acc1 = mfma_bf16(a, bx[1][ks], acc1);
-      if constexpr (F32) {
-        acc0 = mfma_bf16(a, bxl[0][ks % (F32 ? KS : 1)], acc0);
-        acc1 = mfma_bf16(a, bxl[1][ks % (F32 ? KS : 1)], acc1);
+    for (int i = 0; i < NSTEP; ++i) {
+      if (i + 2 < NSTEP) fr[(i + 2) % 3] = *reinterpret_cast<const bf16x8*>(R + frag_off(i + 2));
+      const bf16x8 a = fr[i % 3];
+      if (i == 0) {
+        acc0 = mfma_bf16(a, bext[0], acc0);
+        acc1 = mfma_bf16(a, bext[1], acc1);
+      } else {
+        const int ks = (i - 1) % KS;
+        acc0 = mfma_bf16(a, bx[0][ks], acc0);
+        acc1 = mfma_bf16(a, bx[1][ks], acc1);
+        if (F32 && i <= KS) {
+          acc0 = mfma_bf16(a, bxl[0][ks % (F32 ? KS : 1)], acc0);
+          acc1 = mfma_bf16(a, bxl[1][ks % (F32 ? KS : 1)], acc1);
+        }
       }
     }
+    // pin the read-ahead (mask bits: 0x100 LDS read, 0x008 MFMA)
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(R + D + KM_EXTRA + 16 * ks + 8 * half);
-      acc0 = mfma_bf16(a, bx[0][ks], acc0);
-      acc1 = mfma_bf16(a, bx[1][ks], acc1);
+    for (int i = 0; i < NSTEP; ++i) {
+      if (i + 2 < NSTEP) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (F32 && i >= 1 && i <= KS)
+        __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+      else
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
   };
   // keys: the low ib bits of V's pattern carry the centroid index; keep the
@@ -296,11 +317,11 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) 
   for (int ci = 0; ci < nchunk; ++ci) {
     const int buf = ci & 1;
     const bool more = ci + 1 < nchunk;
-    if (more) fetch((ci + 1) * 32);
+    if (more) stage((ci + 1) * 32, buf ^ 1);
     f32x16 acc0, acc1;
     mma(buf, acc0, acc1);
     keys(ci * 32, acc0, acc1);
-    if (more) store(buf ^ 1);
+    if (more) staged();
     __syncthreads();
   }
 
