@@ -16,8 +16,9 @@
 // MFMA formulation: S^T = K Q^T (keys x queries) and O^T = V^T P^T, so that a
 // lane owns one query column of both, making the softmax statistics and the
 // rescale of O lane-local.  bf16: QK^T and PV on v_mfma_f32_32x32x16_bf16,
-// P rounded to bf16; the pseudo-keys' k_bar and v_bar (fp32) enter as bf16
-// hi + lo pairs.  fp32: v_mfma_f32_32x32x2f32 throughout.
+// P rounded to bf16; the pseudo-keys' k_bar and v_bar (fp32) enter rounded to
+// bf16 like the real keys and values (as bf16 hi + lo pairs in the variance
+// variant).  fp32: v_mfma_f32_32x32x2f32 throughout.
 #include <float.h>
 
 #include "common.h"
@@ -484,7 +485,9 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
                                                            bf16* __restrict__ out, float* __restrict__ lse,
                                                            int maxt, int BHn, const float* __restrict__ kvars,
                                                            float vcoef, const int32_t* __restrict__ qexp,
-                                                           const int32_t* __restrict__ kexp) {
+                                                           const int32_t* __restrict__ kexp,
+                                                           const bf16* __restrict__ pkx,
+                                                           const bf16* __restrict__ pvx) {
   using TL = AtTile<D>;
   using T8 = AtTile8<D>;
   constexpr int KS = D / 16, DT = D / 32, ROWB = TL::ROWB, CH = TL::CH, RPI = TL::RPI, NI = TL::NI;
@@ -499,6 +502,8 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
   int* sSelStart = sLists;        // [Ck]  first permuted row of the c-th selected cluster
   int* sSelPre = sSelStart + Ck;  // [Ck+1] key position where the c-th selected cluster begins
   int* sComp = sSelPre + Ck + 1;  // [Ck]  skipped non-empty clusters
+  // [Ck + 64] log2 n_j of the c-th skipped cluster (16-byte aligned)
+  float* sPBias = reinterpret_cast<float*>(sLists + ((3 * Ck + 1 + 3) & ~3));
 
   // Workgroups are dealt to the 8 XCDs round-robin by linear id; give each XCD
   // a contiguous range of (head, tile) so the tiles of one query cluster, which
@@ -706,11 +711,14 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
 
   // one tile of keys in LDS: S^T, online softmax, O^T += V^T P^T.  Real tiles
   // take the max on the raw scores (scale > 0) and fold the scale into one FMA
-  // per weight; pseudo tiles (hi in buffer 0, lo in buffer 1) add the log2 n_j
-  // bias first.
-  auto compute = [&](const char* Kh, const char* Vh, int lim, bool pseudo, auto&& mid) {
+  // per weight.  Pseudo tiles add the log2 n_j bias first; they come in two
+  // layouts: `pseudo` (the variance variant: hi parts of k_bar, v_bar in
+  // buffer 0, lo parts in buffer 1) and `pb` (bf16 k_bar, v_bar of skipped
+  // clusters 64 pt.. in the layout of a real tile, so these tiles stream
+  // through the same double-buffered loads).
+  auto compute = [&](const char* Kh, const char* Vh, int lim, bool pseudo, bool pbf, int pt, auto&& mid) {
     f32x16 s[2] = {f32x16{}, f32x16{}};
-    if (F8 && !pseudo) {
+    if (F8 && !pseudo && !pbf) {
 #pragma unroll
       for (int kk = 0; kk < T8::KK; ++kk)
 #pragma unroll
@@ -747,7 +755,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
       for (int t = 0; t < DT; ++t) vf[0][t] = vt_frag(Vh + aV[t], Vh + aV[t] + 8 * ROWB);
     }
     mid();  // straight-line work that overlaps the products in flight
-    if (!F8 && !pseudo) {
+    if ((!F8 || pbf) && !pseudo) {
       // keep the read-ahead: the scheduler would otherwise sink each read to
       // just before its product (mask bits: 0x100 LDS read, 0x008 MFMA)
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -774,6 +782,21 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
 #pragma unroll
           for (int r = 0; r < 16; ++r) s[sub][r] = fmaf(svt[sub][r], vcoef, s[sub][r]);
       }
+    } else if (pbf) {
+      // s[sub][r] = q.k_bar of skipped cluster 64 pt + sub*32 + c_row(r, half);
+      // -inf past the last one
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int c0 = 64 * pt + 32 * sub + 8 * g + 4 * half;
+          const f32x4 b = *reinterpret_cast<const f32x4*>(sPBias + c0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            s[sub][r] = c0 + e < ncomp ? fmaf(s[sub][r], sl2p, b[e]) : -INFINITY;
+          }
+        }
     } else if (lim < AT_BN) {
       // key index sub*32 + c_row(r, half) >= lim, with the lane's part moved to the right
       const int lh = lim - 4 * half;
@@ -789,7 +812,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
     mx = max_halves(mx);
-    if (!pseudo) mx *= sl2r;
+    if (!pseudo && !pbf) mx *= sl2r;
     const bool grow = mx > m_run + AT_LAZY;
     if (ballot(grow)) {
       const float m_new = grow ? mx : m_run;
@@ -801,7 +824,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
     }
-    const float sc = pseudo ? 1.f : sl2r;
+    const float sc = (pseudo || pbf) ? 1.f : sl2r;
     const float nm = -m_run;
     const at_bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
@@ -861,27 +884,77 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
       // the last tile they fetch row 0 into the idle buffer, which is never read
       sources(kt + 1, ro);
       if constexpr (F8) sources8(kt + 1, ro8);
-      compute(sK0, sV0, nkeys - kt * AT_BN, false, [&] { issue(ro, ro8, sK1, sV1); });
+      compute(sK0, sV0, nkeys - kt * AT_BN, false, false, 0, [&] { issue(ro, ro8, sK1, sV1); });
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (kt + 1 < nreal) {
         sources(kt + 2, ro);
         if constexpr (F8) sources8(kt + 2, ro8);
-        compute(sK1, sV1, nkeys - (kt + 1) * AT_BN, false, [&] { issue(ro, ro8, sK0, sV0); });
+        compute(sK1, sV1, nkeys - (kt + 1) * AT_BN, false, false, 0, [&] { issue(ro, ro8, sK0, sV0); });
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
       }
     }
   }
 
-  // ---- skipped non-empty clusters: pseudo-keys k_bar_j (hi, lo), v_bar_j (hi, lo), bias log2 n_j.
+  // ---- skipped non-empty clusters: pseudo-keys k_bar_j, v_bar_j, bias
+  // log2 n_j.  Without the variance term: the means as bf16 rows (prepared
+  // once per call), 64 clusters a tile, loaded straight into LDS and double
+  // buffered like the real tiles.
+  if constexpr (!VAR) {
+    const int np64 = (ncomp + AT_BN - 1) / AT_BN;
+    if (np64 > 0) {
+      if constexpr (F8) load_bq_from_fp8();
+      for (int c = tid; c < ncomp; c += 256) {
+        const int j = sComp[c];
+        sPBias[c] = log2f((float)(ko[j + 1] - ko[j]));
+      }
+      const __amdgpu_buffer_rsrc_t rPK = lds_src(reinterpret_cast<const char*>(pkx + (size_t)bh * Ck * D),
+                                                 Ck * D * 2);
+      const __amdgpu_buffer_rsrc_t rPV = lds_src(reinterpret_cast<const char*>(pvx + (size_t)bh * Ck * D),
+                                                 Ck * D * 2);
+      // row of tile position p: skipped cluster 64 pt + p
+      auto psources = [&](int ptile, uint32_t* rowoff) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const int c = AT_BN * ptile + (w * NI + i) * RPI + lq;
+          rowoff[i] = (uint32_t)(c < ncomp ? sComp[c] : 0) * (uint32_t)ROWB;
+        }
+      };
+      auto pissue = [&](const uint32_t* rowoff, char* dK, char* dV) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+          const int g = w * NI + i;
+          load_lds16(rPK, rowoff[i] + (uint32_t)(chK[i] << 4), dK + g * 1024);
+          load_lds16(rPV, rowoff[i] + (uint32_t)(chV << 4), dV + g * 1024);
+        }
+      };
+      uint32_t ro[NI];
+      psources(0, ro);
+      pissue(ro, sK0, sV0);
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      for (int pt = 0; pt < np64; pt += 2) {
+        // past the last tile the loads fetch cluster 0's rows into the idle
+        // buffer, which is never read
+        psources(pt + 1, ro);
+        compute(sK0, sV0, AT_BN, false, true, pt, [&] { pissue(ro, sK1, sV1); });
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (pt + 1 < np64) {
+          psources(pt + 2, ro);
+          compute(sK1, sV1, AT_BN, false, true, pt + 1, [&] { pissue(ro, sK0, sV0); });
+          __builtin_amdgcn_s_waitcnt(0);
+          __syncthreads();
+        }
+      }
+    }
+  }
+  // Variance variant: tiles of 64 clusters staged through registers.
   // Staging unit: keys 4 g4 .. 4 g4 + 3, dims d0 .. d0 + 7 (one 16-byte chunk per key).
   constexpr int NUNIT = (AT_BN / 4) * (D / 8);
   const bool has_unit = tid < NUNIT;
   const int g4 = tid & 15, d0 = (tid >> 4) * 8;
-  if constexpr (F8) {
-    if (npseudo > 0) load_bq_from_fp8();
-  }
   bf16x8 q2[VAR ? KS : 1];
   if constexpr (VAR) {
 #pragma unroll
@@ -889,7 +962,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
 #pragma unroll
       for (int e = 0; e < 8; ++e) q2[ks][e] = (bf16)((float)bq[ks][e] * (float)bq[ks][e]);
   }
-  for (int pt = 0; pt < npseudo; ++pt) {
+  for (int pt = 0; pt < (VAR ? npseudo : 0); ++pt) {
     if constexpr (VAR) {
       // the tile's key variances (bf16) through sK1 in the K layout, then
       // svt = Var_j . q^2 by the same products as S^T
@@ -956,7 +1029,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
       }
     }
     __syncthreads();
-    compute(sK0, sV0, AT_BN, true, [] {});
+    compute(sK0, sV0, AT_BN, true, false, 0, [] {});
     __syncthreads();
   }
 
@@ -981,17 +1054,45 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
 // ---------------------------------------------------------------- host side
 struct AtPlan {
   int BH, maxt;
-  size_t off_ts, total;
+  size_t off_ts, off_pk, off_pv, total;
 };
 
-static AtPlan at_plan(int B, int H, int N, int Cq) {
+static AtPlan at_plan(int B, int H, int N, int D, int Cq, int Ck) {
   AtPlan p;
   p.BH = B * H;
   p.maxt = cdiv(N, AT_BM) + Cq;
   Carver cv(nullptr);
   p.off_ts = cv.used; cv.take<int32_t>((size_t)p.BH * (Cq + 1));
+  p.off_pk = cv.used; cv.take<bf16>((size_t)p.BH * Ck * D);
+  p.off_pv = cv.used; cv.take<bf16>((size_t)p.BH * Ck * D);
   p.total = cv.used;
   return p;
+}
+
+// pseudo-key operands of the bf16 kernel: k_bar_j and v_bar_j rounded to
+// bf16 (nearest even), one row each like a row of K'/V'; thread u converts 8
+// elements of one mean
+template <int D>
+__global__ void __launch_bounds__(256) at_pseudo_ops_kernel(const float* __restrict__ km,
+                                                            const float* __restrict__ vm, int Ck,
+                                                            bf16* __restrict__ pk, bf16* __restrict__ pv) {
+  const int bh = blockIdx.y;
+  const int u = blockIdx.x * 256 + threadIdx.x;
+  if (u >= Ck * (D / 8)) return;
+  const size_t at = (size_t)bh * Ck * D + (size_t)u * 8;
+#pragma unroll
+  for (int which = 0; which < 2; ++which) {
+    const float* m = which ? vm : km;
+    const f32x4 a = *reinterpret_cast<const f32x4*>(m + at);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(m + at + 4);
+    bf16x8 h;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      h[e] = (bf16)a[e];
+      h[e + 4] = (bf16)b[e];
+    }
+    *reinterpret_cast<bf16x8*>((which ? pv : pk) + at) = h;
+  }
 }
 
 template <typename T, int D>
@@ -999,9 +1100,10 @@ static void launch_attn(const void* q, const void* k, const void* v, const int32
                         const int32_t* ts, int Cq, const int32_t* koff, int Ck, const float* km, const float* vm,
                         const uint8_t* mask, int BH, int N, float sl2, void* out, float* lse, int maxt,
                         const float* kvars, float vcoef, const int32_t* qexp, const int32_t* kexp,
-                        hipStream_t st) {
+                        const bf16* pk, const bf16* pv, hipStream_t st) {
   if constexpr (sizeof(T) == 2) {
-    const size_t lds = (size_t)(3 * Ck + 1) * sizeof(int);  // cluster lists; the tiles are static
+    // cluster lists and the skipped clusters' biases; the tiles are static
+    const size_t lds = (size_t)(((3 * Ck + 1 + 3) & ~3) + Ck + AT_BN) * sizeof(int);
     const int total = round_up(maxt * BH, AT_XCDS);
     if (kvars) {
       (void)hipFuncSetAttribute((const void*)attn_bf16_kernel<D, true>, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -1009,26 +1111,28 @@ static void launch_attn(const void* q, const void* k, const void* v, const int32
       hipLaunchKernelGGL((attn_bf16_kernel<D, true>), dim3(total), dim3(256), lds, st, (const bf16*)q,
                          (const bf16*)k, (const bf16*)v, qidx, qoff, ts, Cq, koff, Ck, km, vm, mask, N, sl2,
                          (bf16*)out, lse, maxt, BH, kvars, vcoef, (const int32_t*)nullptr,
-                         (const int32_t*)nullptr);
+                         (const int32_t*)nullptr, pk, pv);
     } else if (qexp) {
       (void)hipFuncSetAttribute((const void*)attn_bf16_kernel<D, false, true>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
       hipLaunchKernelGGL((attn_bf16_kernel<D, false, true>), dim3(total), dim3(256), lds, st, (const bf16*)q,
                          (const bf16*)k, (const bf16*)v, qidx, qoff, ts, Cq, koff, Ck, km, vm, mask, N, sl2,
-                         (bf16*)out, lse, maxt, BH, (const float*)nullptr, 0.f, qexp, kexp);
+                         (bf16*)out, lse, maxt, BH, (const float*)nullptr, 0.f, qexp, kexp, pk, pv);
     } else {
       (void)hipFuncSetAttribute((const void*)attn_bf16_kernel<D, false>, hipFuncAttributeMaxDynamicSharedMemorySize,
                                 (int)lds);
       hipLaunchKernelGGL((attn_bf16_kernel<D, false>), dim3(total), dim3(256), lds, st, (const bf16*)q,
                          (const bf16*)k, (const bf16*)v, qidx, qoff, ts, Cq, koff, Ck, km, vm, mask, N, sl2,
                          (bf16*)out, lse, maxt, BH, (const float*)nullptr, 0.f, (const int32_t*)nullptr,
-                         (const int32_t*)nullptr);
+                         (const int32_t*)nullptr, pk, pv);
     }
   } else {
     (void)kvars;
     (void)vcoef;
     (void)qexp;
     (void)kexp;
+    (void)pk;
+    (void)pv;
     using L = AttnLds<T, D>;
     const size_t lds = L::fixed + (size_t)(3 * Ck + 1) * sizeof(int);
     (void)hipFuncSetAttribute((const void*)attn_kernel<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -1042,10 +1146,8 @@ static void launch_attn(const void* q, const void* k, const void* v, const int32
 using namespace svg;
 
 extern "C" size_t svgear_sparse_attn_workspace(int B, int H, int N, int D, int Cq, int Ck) {
-  (void)D;
-  (void)Ck;
-  if (B < 1 || H < 1 || N < 1 || Cq < 1) return 0;
-  return at_plan(B, H, N, Cq).total;
+  if (B < 1 || H < 1 || N < 1 || Cq < 1 || Ck < 1 || (D != 64 && D != 128)) return 0;
+  return at_plan(B, H, N, D, Cq, Ck).total;
 }
 
 static svgear_status sparse_attn_impl(const void* q_perm, const void* k_perm, const void* v_perm, svgear_dtype dt,
@@ -1064,7 +1166,7 @@ static svgear_status sparse_attn_impl(const void* q_perm, const void* k_perm, co
   if (!q_perm || !k_perm || !v_perm || !q_perm_idx || !q_offsets || !k_offsets || !k_means || !v_means || !mask ||
       !out)
     return fail(SVGEAR_ERR_INVALID_ARG, "attn: null pointer");
-  AtPlan p = at_plan(B, H, N, Cq);
+  AtPlan p = at_plan(B, H, N, D, Cq, Ck);
   st = check_ws("attn", ws, ws_bytes, p.total);
   if (st != SVGEAR_OK) return st;
   int32_t* ts = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + p.off_ts);
@@ -1073,20 +1175,26 @@ static svgear_status sparse_attn_impl(const void* q_perm, const void* k_perm, co
   // variance term in log2 units: strength * sigma^2 / 2 * log2(e), sigma^2 = scale^2 sum q_i^2 Var(k_i)
   const float vcoef = 0.5f * strength * scale * scale * 1.4426950408889634f;
   hipLaunchKernelGGL(chunk_list_kernel, dim3(BH), dim3(1024), 0, stream, q_offsets, Cq, AT_BM, ts);
+  bf16* pk = reinterpret_cast<bf16*>(static_cast<char*>(ws) + p.off_pk);
+  bf16* pv = reinterpret_cast<bf16*>(static_cast<char*>(ws) + p.off_pv);
   if (dt == SVGEAR_BF16) {
-    if (D == 128)
+    const dim3 pg(cdiv(Ck * (D / 8), 256), BH);
+    if (D == 128) {
+      hipLaunchKernelGGL(at_pseudo_ops_kernel<128>, pg, dim3(256), 0, stream, k_means, v_means, Ck, pk, pv);
       launch_attn<bf16, 128>(q_perm, k_perm, v_perm, q_perm_idx, q_offsets, ts, Cq, k_offsets, Ck, k_means, v_means,
-                             mask, BH, N, sl2, out, lse, p.maxt, k_vars, vcoef, q_exp, k_exp, stream);
-    else
+                             mask, BH, N, sl2, out, lse, p.maxt, k_vars, vcoef, q_exp, k_exp, pk, pv, stream);
+    } else {
+      hipLaunchKernelGGL(at_pseudo_ops_kernel<64>, pg, dim3(256), 0, stream, k_means, v_means, Ck, pk, pv);
       launch_attn<bf16, 64>(q_perm, k_perm, v_perm, q_perm_idx, q_offsets, ts, Cq, k_offsets, Ck, k_means, v_means,
-                            mask, BH, N, sl2, out, lse, p.maxt, k_vars, vcoef, q_exp, k_exp, stream);
+                            mask, BH, N, sl2, out, lse, p.maxt, k_vars, vcoef, q_exp, k_exp, pk, pv, stream);
+    }
   } else {
     if (D == 128)
       launch_attn<float, 128>(q_perm, k_perm, v_perm, q_perm_idx, q_offsets, ts, Cq, k_offsets, Ck, k_means, v_means,
-                              mask, BH, N, sl2, out, lse, p.maxt, k_vars, vcoef, q_exp, k_exp, stream);
+                              mask, BH, N, sl2, out, lse, p.maxt, k_vars, vcoef, q_exp, k_exp, pk, pv, stream);
     else
       launch_attn<float, 64>(q_perm, k_perm, v_perm, q_perm_idx, q_offsets, ts, Cq, k_offsets, Ck, k_means, v_means,
-                             mask, BH, N, sl2, out, lse, p.maxt, k_vars, vcoef, q_exp, k_exp, stream);
+                             mask, BH, N, sl2, out, lse, p.maxt, k_vars, vcoef, q_exp, k_exp, pk, pv, stream);
   }
   return check_launch("svgear_sparse_attn");
 }

@@ -354,13 +354,23 @@ def test_sparse_attn_variance_corrected(sv, name, strength, ref_cache):
 
 
 def test_sparse_attn_variance_strength_zero_is_plain(sv, ref_cache):
+    # At strength 0 the variance kernel computes the plain method: its output
+    # meets the plain oracle at the attention tolerances.  (It is not the plain
+    # kernel's output bit for bit: the plain path rounds the pseudo-keys' means
+    # to bf16, the variance path carries them as bf16 hi + lo pairs.)
     w, x, outs, sc = oracle_layer("bf16-d128", ref_cache)
     BH = w.B * w.H
-    dev, _ = attn_inputs(w, x, outs)
+    dev, m = attn_inputs(w, x, outs)
     kvar = np.stack([orc.variances(x["k"][h], outs[h]["pk"], outs[h]["ok"]) for h in range(BH)])
-    plain, _ = sv.sparse_attn(*dev, sc)
     zero, _ = sv.sparse_attn(*dev, sc, k_vars=f32(reshape4(kvar, w)), strength=0.0)
-    assert torch.equal(plain, zero)
+    zero = host(zero).reshape(BH, w.N, w.D)
+    amax, amean = ATOL[w.dtype]
+    for h in range(BH):
+        o = outs[h]
+        O, _ = orc.attend(x["q"][h], x["k"][h], x["v"][h], o["pq"], o["oq"], o["pk"], o["ok"], o["kbar"], o["vbar"],
+                          m[h], sc)
+        err = np.abs(zero[h] - O)
+        assert err.max() <= amax and err.mean() <= amean, (err.max(), err.mean())
 
 
 # ------------------------------------------------------------------ top-p budget (SVG2) routing
