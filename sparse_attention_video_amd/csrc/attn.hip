@@ -568,7 +568,6 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
   }
   const int qrow = row0 + 32 * w + col;
   const bool qok = qrow < rowEnd;
-  const bool idle = row0 + 32 * w >= rowEnd;  // uniform: no row of this wave is real
   bf16x8 bq[KS];
   at_v8i bq8[F8 ? T8::KK : 1];
   if constexpr (!F8) {
@@ -880,17 +879,6 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
     // the Q fragments and tile 0 are in: later waits only cover the prefetch
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    // a wave whose 32 rows all lie past the cluster's end only loads its share
-    // of each tile and meets the barriers, leaving its SIMD to the other wave
-    if (idle) {
-      for (int kt = 0; kt < nreal; ++kt) {
-        sources(kt + 1, ro);
-        if constexpr (F8) sources8(kt + 1, ro8);
-        issue(ro, ro8, (kt & 1) ? sK0 : sK1, (kt & 1) ? sV0 : sV1);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-      }
-    } else {
     for (int kt = 0; kt < nreal; kt += 2) {
       // the next tile's loads go out while this tile's S^T products run; past
       // the last tile they fetch row 0 into the idle buffer, which is never read
@@ -906,7 +894,6 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
       }
-    }
     }
   }
 
@@ -947,14 +934,6 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
       pissue(ro, sK0, sV0);
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
-      if (idle) {
-        for (int pt = 0; pt < np64; ++pt) {
-          psources(pt + 1, ro);
-          pissue(ro, (pt & 1) ? sK0 : sK1, (pt & 1) ? sV0 : sV1);
-          __builtin_amdgcn_s_waitcnt(0);
-          __syncthreads();
-        }
-      } else {
       for (int pt = 0; pt < np64; pt += 2) {
         // past the last tile the loads fetch cluster 0's rows into the idle
         // buffer, which is never read
@@ -968,7 +947,6 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
           __builtin_amdgcn_s_waitcnt(0);
           __syncthreads();
         }
-      }
       }
     }
   }
