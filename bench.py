@@ -34,9 +34,9 @@ METRIC = "ms per attention layer (cluster+route+sparse attn), 75.6k tok, 25% den
 # FETCH_SIZE / WRITE_SIZE calibrated against a 1 GiB device copy (FETCH x 2.0,
 # WRITE x 1.0); valid only for the attention source it was measured on.
 ATTN_TRAFFIC = {
-    "source_sha256": "461a335524a50b7d12c4e1ed05ce0ab097aa3c6cb59bce8db5e1c44d8345efd6",
+    "source_sha256": "cde5c90a30fb4ef090eceb147f339eaefcaec56121caed1147303c3d783dd9d2",
     "workload": "wan",
-    "fetch_bytes": 35.23e9,
+    "fetch_bytes": 36.73e9,
     "write_bytes": 0.774e9,
 }
 PEAK_BF16_TFLOPS = 2500.0
