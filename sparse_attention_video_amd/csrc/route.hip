@@ -86,8 +86,8 @@ __global__ void __launch_bounds__(256) rt_main_kernel(const T* __restrict__ kp, 
                                                       float* __restrict__ part, float* __restrict__ t1part) {
   constexpr int KS = D / 16;
   constexpr int SQ = D + 8;  // LDS row stride for q_bar (bf16)
-  __shared__ __attribute__((aligned(16))) bf16 s_qh[RT_QB * SQ];
-  __shared__ __attribute__((aligned(16))) bf16 s_ql[RT_QB * SQ];
+  __shared__ __attribute__((aligned(1024))) bf16 s_qh[RT_QB * SQ];
+  __shared__ __attribute__((aligned(1024))) bf16 s_ql[RT_QB * SQ];
   __shared__ float s_kbar[D], s_vbar[D];
   __shared__ __attribute__((aligned(16))) float s_w[4][32];
   __shared__ __attribute__((aligned(16))) float s_vv[4][32];
@@ -95,7 +95,8 @@ __global__ void __launch_bounds__(256) rt_main_kernel(const T* __restrict__ kp, 
   __shared__ float s_t1[4];
   __shared__ int s_j;
 
-  const int bh = blockIdx.y, pc = blockIdx.x, tid = threadIdx.x, lane = lane_id(), w = wave_id();
+  const int bh = blockIdx.y, pc = blockIdx.x, tid = threadIdx.x, lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(wave_id());
   const int half = lane >> 5, col = lane & 31;
   const int32_t* ps = pstart + (size_t)bh * (Ck + 1);
   if (pc >= ps[Ck]) return;
@@ -118,12 +119,29 @@ __global__ void __launch_bounds__(256) rt_main_kernel(const T* __restrict__ kp, 
     const int nq = min(RT_QB, Cqp - qb);
     const int nqt = nq / 32;
     __syncthreads();
-    for (int v = tid; v < nq * (D / 8); v += 256) {
-      const int r = v / (D / 8), cu = v - r * (D / 8);
-      *reinterpret_cast<u32x4*>(&s_qh[r * SQ + cu * 8]) =
-          *reinterpret_cast<const u32x4*>(qhi + ((size_t)bh * Cqp + qb + r) * D + cu * 8);
-      *reinterpret_cast<u32x4*>(&s_ql[r * SQ + cu * 8]) =
-          *reinterpret_cast<const u32x4*>(qlo + ((size_t)bh * Cqp + qb + r) * D + cu * 8);
+    {
+      // q_bar hi/lo rows straight into LDS (no registers, one memory latency):
+      // load j fills bytes [1024 j, 1024 j + 1024) of the padded block, lane
+      // L the 16 bytes at o = 1024 j + 16 L, i.e. byte o % (2 SQ) of row
+      // o / (2 SQ); pad bytes and rows past nq take row 0's first bytes
+      constexpr int NJ = RT_QB * SQ * 2 / 1024;
+      static_assert(RT_QB * SQ * 2 % 1024 == 0, "q_bar block must be whole 1 KB loads");
+      const __amdgpu_buffer_rsrc_t rh = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(qhi + (size_t)bh * Cqp * D), (short)0, Cqp * D * 2, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rl = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(qlo + (size_t)bh * Cqp * D), (short)0, Cqp * D * 2, 0x00020000);
+      for (int j = w; j < NJ; j += 4) {
+        const int o = 1024 * j + 16 * lane;
+        const int r = o / (2 * SQ), cb = o - r * (2 * SQ);
+        const int off = (r < nq && cb < 2 * D) ? (qb + r) * D * 2 + cb : 0;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rh, (__attribute__((address_space(3))) void*)(reinterpret_cast<char*>(s_qh) + 1024 * j), 16, off, 0, 0,
+            0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rl, (__attribute__((address_space(3))) void*)(reinterpret_cast<char*>(s_ql) + 1024 * j), 16, off, 0, 0,
+            0);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vector-memory count 0 (this wave's loads landed)
     }
     __syncthreads();
     float dl[4], s2[4], s3[4];
