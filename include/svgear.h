@@ -267,9 +267,9 @@ svgear_status svgear_route_topp(const float* q_means, const int32_t* q_offsets, 
  * A query cluster with nothing selected and every key cluster empty cannot
  * occur (the key clusters partition N >= 1 keys).
  * bf16: the pseudo-keys enter with k_bar and v_bar rounded to bf16, like the
- * keys and values (the variance variant below keeps bf16 hi + lo pairs).
+ * keys and values (in the variance variant below the variances too).
  * Workspace (svgear_sparse_attn_workspace; 0 for invalid sizes): the tile
- * list and the bf16 copies of k_means and v_means, about 4 D Ck + 4 (Cq + 1)
+ * list and the bf16 copies of k_means, v_means (and k_vars), about 6 D Ck + 4 (Cq + 1)
  * bytes per (batch, head).
  * ---------------------------------------------------------------------- */
 size_t svgear_sparse_attn_workspace(int B, int H, int N, int D, int Cq, int Ck);

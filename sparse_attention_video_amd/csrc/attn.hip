@@ -17,9 +17,11 @@
 // lane owns one query column of both, making the softmax statistics and the
 // rescale of O lane-local.  bf16: QK^T and PV on v_mfma_f32_32x32x16_bf16,
 // P rounded to bf16; the pseudo-keys' k_bar and v_bar (fp32) enter rounded to
-// bf16 like the real keys and values (as bf16 hi + lo pairs in the variance
-// variant).  fp32: v_mfma_f32_32x32x2f32 throughout.
+// bf16 like the real keys and values.  fp32: v_mfma_f32_32x32x2f32
+// throughout.
 #include <float.h>
+
+#include <type_traits>
 
 #include "common.h"
 #include "host.h"
@@ -29,6 +31,7 @@ namespace svg {
 
 constexpr int AT_BM = 128;  // query rows per workgroup (4 waves x 32)
 constexpr int AT_BN = 64;   // keys per tile
+constexpr int AT_REAL = 0, AT_PS = 1, AT_PSV = 2;  // tile kinds of the bf16 kernel
 
 template <typename T, int D>
 struct AttnLds {
@@ -411,7 +414,8 @@ __global__ void __launch_bounds__(256) attn_kernel(const T* __restrict__ qp, con
 //    max, so the result is unchanged);
 //  * the row sum adds the bf16-rounded weights that multiply V (v_dot2), so
 //    numerator and denominator use the same weights;
-//  * skipped clusters (pseudo-keys, bf16 hi + lo) run in a second loop.
+//  * skipped clusters (pseudo-keys: bf16 rows of the means, prepared once
+//    per call) stream after the selected keys through the same loads.
 //
 // Tile layout: 64 rows of D bf16 (ROWB = 2 D bytes), chunk c (16 bytes) of
 // row r in slot c ^ swz(r).  For D = 128 (64 LDS banks, 256 bytes per clock):
@@ -471,8 +475,9 @@ struct AtTile {
   static __device__ __forceinline__ int swzV(int r) { return 4 * (r & (CH >= 16 ? 3 : 1)); }
 };
 
-// VAR: skipped clusters' scores also gain vcoef * sum_i q_i^2 kvars[j][i]
-// (variance-corrected compensation; vcoef in log2 units).
+// VAR: skipped clusters' scores also gain vcoef * sum_i q_i^2 Var_j[i]
+// (variance-corrected compensation; vcoef in log2 units); the variances come
+// in as bf16 rows of pkx (kvars itself is read by the operand preparation).
 template <int D, bool VAR = false, bool F8 = false>
 __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restrict__ qp, const bf16* __restrict__ kp,
                                                            const bf16* __restrict__ vp, const int32_t* __restrict__ qidx,
@@ -488,6 +493,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
                                                            const int32_t* __restrict__ kexp,
                                                            const bf16* __restrict__ pkx,
                                                            const bf16* __restrict__ pvx) {
+  (void)kvars;
   using TL = AtTile<D>;
   using T8 = AtTile8<D>;
   constexpr int KS = D / 16, DT = D / 32, ROWB = TL::ROWB, CH = TL::CH, RPI = TL::RPI, NI = TL::NI;
@@ -495,7 +501,6 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
   __shared__ __attribute__((aligned(1024))) char sK1[TL::BYTES];
   __shared__ __attribute__((aligned(1024))) char sV0[TL::BYTES];
   __shared__ __attribute__((aligned(1024))) char sV1[TL::BYTES];
-  __shared__ float sBias[AT_BN];
   __shared__ int sScan[16];
   __shared__ int sInfo[4];
   extern __shared__ __attribute__((aligned(16))) int sLists[];
@@ -551,7 +556,6 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
   }
   const int nsel = sInfo[1], ncomp = sInfo[2], nkeys = sInfo[3];
   const int nreal = (nkeys + AT_BN - 1) / AT_BN;
-  const int npseudo = (ncomp + AT_BN - 1) / AT_BN;
 
   // F8: qp and kp hold e4m3 bytes (D per row) with per-head power-of-two
   // scales 2^qexp, 2^kexp; real-tile scores use scale 2^(qexp+kexp) sl2 and
@@ -706,19 +710,24 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
     }
   };
 
-  // variance term sum_i q_i^2 Var_j(k_i) of the current pseudo tile (VAR only)
-  f32x16 svt[2] = {f32x16{}, f32x16{}};
+  // q^2 as bf16, the B operand of the variance products (variance variant)
+  bf16x8 q2[VAR ? KS : 1];
 
-  // one tile of keys in LDS: S^T, online softmax, O^T += V^T P^T.  Real tiles
-  // take the max on the raw scores (scale > 0) and fold the scale into one FMA
-  // per weight.  Pseudo tiles add the log2 n_j bias first; they come in two
-  // layouts: `pseudo` (the variance variant: hi parts of k_bar, v_bar in
-  // buffer 0, lo parts in buffer 1) and `pb` (bf16 k_bar, v_bar of skipped
-  // clusters 64 pt.. in the layout of a real tile, so these tiles stream
-  // through the same double-buffered loads).
-  auto compute = [&](const char* Kh, const char* Vh, int lim, bool pseudo, bool pbf, int pt, auto&& mid) {
+  // one tile of keys in LDS: S^T, online softmax, O^T += V^T P^T.  Modes:
+  //  AT_REAL  selected keys: the max is taken on the raw scores (scale > 0) and
+  //           the scale folds into one FMA per weight;
+  //  AT_PS    skipped clusters 64 pt .. 64 pt + 63 (rows of bf16 k_bar,
+  //           v_bar): score q.k_bar scale + log2 n_j;
+  //  AT_PSV   skipped clusters 32 pt .. 32 pt + 31, variance variant: K rows
+  //           0..31 hold k_bar, rows 32..63 Var (multiplied by q^2), V rows
+  //           0..31 v_bar: score q.k_bar scale + vcoef q^2.Var + log2 n_j.
+  // All scores are in log2 units.
+  auto compute = [&](const char* Kh, const char* Vh, int lim, auto mode_c, int pt, auto&& mid) {
+    constexpr int mode = decltype(mode_c)::value;
+    constexpr bool real = mode == AT_REAL, psv = mode == AT_PSV;
+    constexpr int NST = psv ? 2 : 4;  // 16-key steps of O^T += V^T P^T
     f32x16 s[2] = {f32x16{}, f32x16{}};
-    if (F8 && !pseudo && !pbf) {
+    if constexpr (F8 && real) {
 #pragma unroll
       for (int kk = 0; kk < T8::KK; ++kk)
 #pragma unroll
@@ -745,17 +754,15 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
           fr[(ks + 2) % 3][1] = *reinterpret_cast<const bf16x8*>(Kh + aK[ks + 2] + 32 * ROWB);
         }
         s[0] = mfma_bf16(fr[ks % 3][0], bq[ks], s[0]);
-        s[1] = mfma_bf16(fr[ks % 3][1], bq[ks], s[1]);
+        s[1] = mfma_bf16(fr[ks % 3][1], psv ? q2[ks % (VAR ? KS : 1)] : bq[ks], s[1]);
       }
     }
     // V^T fragments of the first 16 keys: read now, used after the softmax
     bf16x8 vf[2][DT];
-    if (!pseudo) {
 #pragma unroll
-      for (int t = 0; t < DT; ++t) vf[0][t] = vt_frag(Vh + aV[t], Vh + aV[t] + 8 * ROWB);
-    }
+    for (int t = 0; t < DT; ++t) vf[0][t] = vt_frag(Vh + aV[t], Vh + aV[t] + 8 * ROWB);
     mid();  // straight-line work that overlaps the products in flight
-    if ((!F8 || pbf) && !pseudo) {
+    if constexpr (!(F8 && real)) {
       // keep the read-ahead: the scheduler would otherwise sink each read to
       // just before its product (mask bits: 0x100 LDS read, 0x008 MFMA)
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -766,23 +773,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
       }
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * DT, 0);
     }
-    if (pseudo) {
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
-          s[sub] = mfma_bf16(*reinterpret_cast<const bf16x8*>(sK1 + aK[ks] + sub * 32 * ROWB), bq[ks], s[sub]);
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[sub][r] = fmaf(s[sub][r], sl2p, sBias[sub * 32 + c_row(r, half)]);
-      if constexpr (VAR) {
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) s[sub][r] = fmaf(svt[sub][r], vcoef, s[sub][r]);
-      }
-    } else if (pbf) {
+    if constexpr (mode == AT_PS) {
       // s[sub][r] = q.k_bar of skipped cluster 64 pt + sub*32 + c_row(r, half);
       // -inf past the last one
 #pragma unroll
@@ -797,6 +788,19 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
             s[sub][r] = c0 + e < ncomp ? fmaf(s[sub][r], sl2p, b[e]) : -INFINITY;
           }
         }
+    } else if constexpr (psv) {
+      // s[0][r] = q.k_bar and s[1][r] = q^2.Var of skipped cluster
+      // 32 pt + c_row(r, half); -inf past the last one
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c0 = 32 * pt + 8 * g + 4 * half;
+        const f32x4 b = *reinterpret_cast<const f32x4*>(sPBias + c0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          s[0][r] = c0 + e < ncomp ? fmaf(s[0][r], sl2p, fmaf(s[1][r], vcoef, b[e])) : -INFINITY;
+        }
+      }
     } else if (lim < AT_BN) {
       // key index sub*32 + c_row(r, half) >= lim, with the lane's part moved to the right
       const int lh = lim - 4 * half;
@@ -808,11 +812,11 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
+    for (int sub = 0; sub < (psv ? 1 : 2); ++sub)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
     mx = max_halves(mx);
-    if (!pseudo && !pbf) mx *= sl2r;
+    if constexpr (real) mx *= sl2r;
     const bool grow = mx > m_run + AT_LAZY;
     if (ballot(grow)) {
       const float m_new = grow ? mx : m_run;
@@ -824,11 +828,11 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[t][r] *= alpha;
     }
-    const float sc = (pseudo || pbf) ? 1.f : sl2r;
+    const float sc = real ? sl2r : 1.f;
     const float nm = -m_run;
     const at_bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
+    for (int st = 0; st < NST; ++st) {
       const int sub = st >> 1, tp = st & 1;
       bf16x8 pb;
 #pragma unroll
@@ -838,36 +842,25 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
         const at_bf16x2 pr = {pb[2 * e], pb[2 * e + 1]};
         l_run = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l_run, false);
       }
-      if (pseudo) {
+      // the next 16 keys' fragments are read before these products
+      if (st + 1 < NST) {
 #pragma unroll
         for (int t = 0; t < DT; ++t) {
-          const char* base = Vh + aV[t] + 16 * st * ROWB;
-          o[t] = mfma_bf16(vt_frag(base, base + 8 * ROWB), pb, o[t]);
-          const char* bl = sV1 + aV[t] + 16 * st * ROWB;
-          o[t] = mfma_bf16(vt_frag(bl, bl + 8 * ROWB), pb, o[t]);
+          const char* base = Vh + aV[t] + 16 * (st + 1) * ROWB;
+          vf[(st + 1) & 1][t] = vt_frag(base, base + 8 * ROWB);
         }
-      } else {
-        // the next 16 keys' fragments are read before these products
-        if (st + 1 < 4) {
-#pragma unroll
-          for (int t = 0; t < DT; ++t) {
-            const char* base = Vh + aV[t] + 16 * (st + 1) * ROWB;
-            vf[(st + 1) & 1][t] = vt_frag(base, base + 8 * ROWB);
-          }
-        }
-#pragma unroll
-        for (int t = 0; t < DT; ++t) o[t] = mfma_bf16(vf[st & 1][t], pb, o[t]);
       }
+#pragma unroll
+      for (int t = 0; t < DT; ++t) o[t] = mfma_bf16(vf[st & 1][t], pb, o[t]);
     }
-    if (!pseudo) {
-      // the next step's V^T reads go out before this step's products
+    // the next step's V^T reads go out before this step's products
 #pragma unroll
-      for (int st = 0; st < 4; ++st) {
-        if (st + 1 < 4) __builtin_amdgcn_sched_group_barrier(0x100, 2 * DT, 1);
-        __builtin_amdgcn_sched_group_barrier(0x008, DT, 1);
-      }
+    for (int st = 0; st < NST; ++st) {
+      if (st + 1 < NST) __builtin_amdgcn_sched_group_barrier(0x100, 2 * DT, 1);
+      __builtin_amdgcn_sched_group_barrier(0x008, DT, 1);
     }
   };
+  using RealT = std::integral_constant<int, AT_REAL>;
 
   // ---- selected keys: packed 64-key tiles, double buffered, loop unrolled by
   // two so each half reads one fixed buffer
@@ -884,13 +877,13 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
       // the last tile they fetch row 0 into the idle buffer, which is never read
       sources(kt + 1, ro);
       if constexpr (F8) sources8(kt + 1, ro8);
-      compute(sK0, sV0, nkeys - kt * AT_BN, false, false, 0, [&] { issue(ro, ro8, sK1, sV1); });
+      compute(sK0, sV0, nkeys - kt * AT_BN, RealT{}, 0, [&] { issue(ro, ro8, sK1, sV1); });
       __builtin_amdgcn_s_waitcnt(0);
       __syncthreads();
       if (kt + 1 < nreal) {
         sources(kt + 2, ro);
         if constexpr (F8) sources8(kt + 2, ro8);
-        compute(sK1, sV1, nkeys - (kt + 1) * AT_BN, false, false, 0, [&] { issue(ro, ro8, sK0, sV0); });
+        compute(sK1, sV1, nkeys - (kt + 1) * AT_BN, RealT{}, 0, [&] { issue(ro, ro8, sK0, sV0); });
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
       }
@@ -898,139 +891,68 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
   }
 
   // ---- skipped non-empty clusters: pseudo-keys k_bar_j, v_bar_j, bias
-  // log2 n_j.  Without the variance term: the means as bf16 rows (prepared
-  // once per call), 64 clusters a tile, loaded straight into LDS and double
-  // buffered like the real tiles.
-  if constexpr (!VAR) {
-    const int np64 = (ncomp + AT_BN - 1) / AT_BN;
-    if (np64 > 0) {
-      if constexpr (F8) load_bq_from_fp8();
-      for (int c = tid; c < ncomp; c += 256) {
-        const int j = sComp[c];
-        sPBias[c] = log2f((float)(ko[j + 1] - ko[j]));
-      }
-      const __amdgpu_buffer_rsrc_t rPK = lds_src(reinterpret_cast<const char*>(pkx + (size_t)bh * Ck * D),
-                                                 Ck * D * 2);
-      const __amdgpu_buffer_rsrc_t rPV = lds_src(reinterpret_cast<const char*>(pvx + (size_t)bh * Ck * D),
-                                                 Ck * D * 2);
-      // row of tile position p: skipped cluster 64 pt + p
-      auto psources = [&](int ptile, uint32_t* rowoff) {
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          const int c = AT_BN * ptile + (w * NI + i) * RPI + lq;
-          rowoff[i] = (uint32_t)(c < ncomp ? sComp[c] : 0) * (uint32_t)ROWB;
-        }
-      };
-      auto pissue = [&](const uint32_t* rowoff, char* dK, char* dV) {
-#pragma unroll
-        for (int i = 0; i < NI; ++i) {
-          const int g = w * NI + i;
-          load_lds16(rPK, rowoff[i] + (uint32_t)(chK[i] << 4), dK + g * 1024);
-          load_lds16(rPV, rowoff[i] + (uint32_t)(chV << 4), dV + g * 1024);
-        }
-      };
-      uint32_t ro[NI];
-      psources(0, ro);
-      pissue(ro, sK0, sV0);
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      for (int pt = 0; pt < np64; pt += 2) {
-        // past the last tile the loads fetch cluster 0's rows into the idle
-        // buffer, which is never read
-        psources(pt + 1, ro);
-        compute(sK0, sV0, AT_BN, false, true, pt, [&] { pissue(ro, sK1, sV1); });
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (pt + 1 < np64) {
-          psources(pt + 2, ro);
-          compute(sK1, sV1, AT_BN, false, true, pt + 1, [&] { pissue(ro, sK0, sV0); });
-          __builtin_amdgcn_s_waitcnt(0);
-          __syncthreads();
-        }
-      }
-    }
-  }
-  // Variance variant: tiles of 64 clusters staged through registers.
-  // Staging unit: keys 4 g4 .. 4 g4 + 3, dims d0 .. d0 + 7 (one 16-byte chunk per key).
-  constexpr int NUNIT = (AT_BN / 4) * (D / 8);
-  const bool has_unit = tid < NUNIT;
-  const int g4 = tid & 15, d0 = (tid >> 4) * 8;
-  bf16x8 q2[VAR ? KS : 1];
-  if constexpr (VAR) {
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) q2[ks][e] = (bf16)((float)bq[ks][e] * (float)bq[ks][e]);
-  }
-  for (int pt = 0; pt < (VAR ? npseudo : 0); ++pt) {
+  // log2 n_j, from bf16 rows prepared once per call, loaded straight into LDS
+  // and double buffered like the real tiles: 64 clusters a tile, 32 with the
+  // variance term (whose Var_j rows take the other half of the K tile)
+  constexpr int PCL = VAR ? 32 : 64;
+  const int npt = (ncomp + PCL - 1) / PCL;
+  if (npt > 0) {
+    if constexpr (F8) load_bq_from_fp8();
     if constexpr (VAR) {
-      // the tile's key variances (bf16) through sK1 in the K layout, then
-      // svt = Var_j . q^2 by the same products as S^T
-      if (has_unit) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int c = pt * AT_BN + 4 * g4 + r;
-          f32x4 a0 = {}, a1 = {};
-          if (c < ncomp) {
-            const float* vr = kvars + ((size_t)bh * Ck + sComp[c]) * D + d0;
-            a0 = *reinterpret_cast<const f32x4*>(vr);
-            a1 = *reinterpret_cast<const f32x4*>(vr + 4);
-          }
-          bf16x8 h;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) { h[e] = (bf16)a0[e]; h[e + 4] = (bf16)a1[e]; }
-          const int row = 4 * g4 + r;
-          *reinterpret_cast<bf16x8*>(sK1 + row * ROWB + (((d0 >> 3) ^ TL::swzK(row)) << 4)) = h;
-        }
-      }
-      __syncthreads();
-      svt[0] = f32x16{};
-      svt[1] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int sub = 0; sub < 2; ++sub)
-          svt[sub] = mfma_bf16(*reinterpret_cast<const bf16x8*>(sK1 + aK[ks] + sub * 32 * ROWB), q2[ks], svt[sub]);
-      __syncthreads();
+        for (int e = 0; e < 8; ++e) q2[ks % (VAR ? KS : 1)][e] = (bf16)((float)bq[ks][e] * (float)bq[ks][e]);
     }
-    if (has_unit) {
+    for (int c = tid; c < ncomp; c += 256) {
+      const int j = sComp[c];
+      sPBias[c] = log2f((float)(ko[j + 1] - ko[j]));
+    }
+    constexpr int KROWS = VAR ? 2 : 1;  // K operand rows per cluster
+    const __amdgpu_buffer_rsrc_t rPK = lds_src(
+        reinterpret_cast<const char*>(pkx + (size_t)bh * Ck * KROWS * D), Ck * KROWS * D * 2);
+    const __amdgpu_buffer_rsrc_t rPV =
+        lds_src(reinterpret_cast<const char*>(pvx + (size_t)bh * Ck * D), Ck * D * 2);
+    // rows of tile position p: K row KROWS j + part, V row j of skipped
+    // cluster PCL pt + p % PCL (part = p / 32 with the variance term)
+    auto psources = [&](int ptile, uint32_t* rk, uint32_t* rv) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int c = pt * AT_BN + 4 * g4 + r;
-        f32x4 k0 = {}, k1 = {}, v0 = {}, v1 = {};
-        float bias = -INFINITY;
-        if (c < ncomp) {
-          const int j = sComp[c];
-          const float* kr = kmeans + ((size_t)bh * Ck + j) * D + d0;
-          const float* vr = vmeans + ((size_t)bh * Ck + j) * D + d0;
-          k0 = *reinterpret_cast<const f32x4*>(kr);
-          k1 = *reinterpret_cast<const f32x4*>(kr + 4);
-          v0 = *reinterpret_cast<const f32x4*>(vr);
-          v1 = *reinterpret_cast<const f32x4*>(vr + 4);
-          bias = log2f((float)(ko[j + 1] - ko[j]));
-        }
-        const int row = 4 * g4 + r, chunk = d0 >> 3;
-        if (d0 == 0) sBias[row] = bias;
-        bf16x8 kh, kl, vh, vl;
+      for (int i = 0; i < NI; ++i) {
+        const int p = (w * NI + i) * RPI + lq;
+        const int c = PCL * ptile + (p % PCL);
+        const int j = c < ncomp ? sComp[c] : 0;
+        rk[i] = (uint32_t)(KROWS * j + (VAR ? p / 32 : 0)) * (uint32_t)ROWB;
+        rv[i] = (uint32_t)j * (uint32_t)ROWB;
+      }
+    };
+    auto pissue = [&](const uint32_t* rk, const uint32_t* rv, char* dK, char* dV) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          bf16 hh, ll;
-          split_bf16(k0[e], hh, ll); kh[e] = hh; kl[e] = ll;
-          split_bf16(k1[e], hh, ll); kh[e + 4] = hh; kl[e + 4] = ll;
-          split_bf16(v0[e], hh, ll); vh[e] = hh; vl[e] = ll;
-          split_bf16(v1[e], hh, ll); vh[e + 4] = hh; vl[e + 4] = ll;
-        }
-        const int ok_ = row * ROWB + ((chunk ^ TL::swzK(row)) << 4);
-        const int ov_ = row * ROWB + ((chunk ^ TL::swzV(row)) << 4);
-        *reinterpret_cast<bf16x8*>(sK0 + ok_) = kh;
-        *reinterpret_cast<bf16x8*>(sK1 + ok_) = kl;
-        *reinterpret_cast<bf16x8*>(sV0 + ov_) = vh;
-        *reinterpret_cast<bf16x8*>(sV1 + ov_) = vl;
+      for (int i = 0; i < NI; ++i) {
+        const int g = w * NI + i;
+        load_lds16(rPK, rk[i] + (uint32_t)(chK[i] << 4), dK + g * 1024);
+        load_lds16(rPV, rv[i] + (uint32_t)(chV << 4), dV + g * 1024);
+      }
+    };
+    using PsT = std::integral_constant<int, VAR ? AT_PSV : AT_PS>;
+    uint32_t rk[NI], rv[NI];
+    psources(0, rk, rv);
+    pissue(rk, rv, sK0, sV0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int pt = 0; pt < npt; pt += 2) {
+      // past the last tile the loads fetch cluster 0's rows into the idle
+      // buffer, which is never read
+      psources(pt + 1, rk, rv);
+      compute(sK0, sV0, AT_BN, PsT{}, pt, [&] { pissue(rk, rv, sK1, sV1); });
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (pt + 1 < npt) {
+        psources(pt + 2, rk, rv);
+        compute(sK1, sV1, AT_BN, PsT{}, pt + 1, [&] { pissue(rk, rv, sK0, sV0); });
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
       }
     }
-    __syncthreads();
-    compute(sK0, sV0, AT_BN, true, false, 0, [] {});
-    __syncthreads();
   }
 
   // ---- epilogue
@@ -1063,35 +985,45 @@ static AtPlan at_plan(int B, int H, int N, int D, int Cq, int Ck) {
   p.maxt = cdiv(N, AT_BM) + Cq;
   Carver cv(nullptr);
   p.off_ts = cv.used; cv.take<int32_t>((size_t)p.BH * (Cq + 1));
-  p.off_pk = cv.used; cv.take<bf16>((size_t)p.BH * Ck * D);
+  p.off_pk = cv.used; cv.take<bf16>((size_t)p.BH * Ck * 2 * D);  // 2 rows per cluster with variances
   p.off_pv = cv.used; cv.take<bf16>((size_t)p.BH * Ck * D);
   p.total = cv.used;
   return p;
 }
 
-// pseudo-key operands of the bf16 kernel: k_bar_j and v_bar_j rounded to
-// bf16 (nearest even), one row each like a row of K'/V'; thread u converts 8
-// elements of one mean
+// pseudo-key operands of the bf16 kernel, rounded to bf16 (nearest even)
+// like the rows of K'/V': pv row j = v_bar_j; pk row j = k_bar_j, or, with
+// the variances (kvars non-null), pk rows 2j = k_bar_j and 2j + 1 = Var_j.
+// Thread u converts 8 elements of one row.
+__device__ __forceinline__ bf16x8 at_round8(const float* m) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(m);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(m + 4);
+  bf16x8 h;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    h[e] = (bf16)a[e];
+    h[e + 4] = (bf16)b[e];
+  }
+  return h;
+}
+
 template <int D>
 __global__ void __launch_bounds__(256) at_pseudo_ops_kernel(const float* __restrict__ km,
-                                                            const float* __restrict__ vm, int Ck,
+                                                            const float* __restrict__ vm,
+                                                            const float* __restrict__ kvars, int Ck,
                                                             bf16* __restrict__ pk, bf16* __restrict__ pv) {
   const int bh = blockIdx.y;
   const int u = blockIdx.x * 256 + threadIdx.x;
   if (u >= Ck * (D / 8)) return;
-  const size_t at = (size_t)bh * Ck * D + (size_t)u * 8;
-#pragma unroll
-  for (int which = 0; which < 2; ++which) {
-    const float* m = which ? vm : km;
-    const f32x4 a = *reinterpret_cast<const f32x4*>(m + at);
-    const f32x4 b = *reinterpret_cast<const f32x4*>(m + at + 4);
-    bf16x8 h;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      h[e] = (bf16)a[e];
-      h[e + 4] = (bf16)b[e];
-    }
-    *reinterpret_cast<bf16x8*>((which ? pv : pk) + at) = h;
+  const int j = u / (D / 8), d0 = (u - j * (D / 8)) * 8;
+  const size_t src = ((size_t)bh * Ck + j) * D + d0;
+  *reinterpret_cast<bf16x8*>(pv + src) = at_round8(vm + src);
+  if (kvars) {
+    const size_t dst = ((size_t)bh * Ck + j) * 2 * D + d0;
+    *reinterpret_cast<bf16x8*>(pk + dst) = at_round8(km + src);
+    *reinterpret_cast<bf16x8*>(pk + dst + D) = at_round8(kvars + src);
+  } else {
+    *reinterpret_cast<bf16x8*>(pk + src) = at_round8(km + src);
   }
 }
 
@@ -1180,11 +1112,11 @@ static svgear_status sparse_attn_impl(const void* q_perm, const void* k_perm, co
   if (dt == SVGEAR_BF16) {
     const dim3 pg(cdiv(Ck * (D / 8), 256), BH);
     if (D == 128) {
-      hipLaunchKernelGGL(at_pseudo_ops_kernel<128>, pg, dim3(256), 0, stream, k_means, v_means, Ck, pk, pv);
+      hipLaunchKernelGGL(at_pseudo_ops_kernel<128>, pg, dim3(256), 0, stream, k_means, v_means, k_vars, Ck, pk, pv);
       launch_attn<bf16, 128>(q_perm, k_perm, v_perm, q_perm_idx, q_offsets, ts, Cq, k_offsets, Ck, k_means, v_means,
                              mask, BH, N, sl2, out, lse, p.maxt, k_vars, vcoef, q_exp, k_exp, pk, pv, stream);
     } else {
-      hipLaunchKernelGGL(at_pseudo_ops_kernel<64>, pg, dim3(256), 0, stream, k_means, v_means, Ck, pk, pv);
+      hipLaunchKernelGGL(at_pseudo_ops_kernel<64>, pg, dim3(256), 0, stream, k_means, v_means, k_vars, Ck, pk, pv);
       launch_attn<bf16, 64>(q_perm, k_perm, v_perm, q_perm_idx, q_offsets, ts, Cq, k_offsets, Ck, k_means, v_means,
                             mask, BH, N, sl2, out, lse, p.maxt, k_vars, vcoef, q_exp, k_exp, pk, pv, stream);
     }

@@ -356,8 +356,8 @@ def test_sparse_attn_variance_corrected(sv, name, strength, ref_cache):
 def test_sparse_attn_variance_strength_zero_is_plain(sv, ref_cache):
     # At strength 0 the variance kernel computes the plain method: its output
     # meets the plain oracle at the attention tolerances.  (It is not the plain
-    # kernel's output bit for bit: the plain path rounds the pseudo-keys' means
-    # to bf16, the variance path carries them as bf16 hi + lo pairs.)
+    # kernel's output bit for bit: its pseudo-key tiles hold 32 clusters instead
+    # of 64, so the online softmax rescales at other points.)
     w, x, outs, sc = oracle_layer("bf16-d128", ref_cache)
     BH = w.B * w.H
     dev, m = attn_inputs(w, x, outs)
