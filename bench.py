@@ -34,9 +34,9 @@ METRIC = "ms per attention layer (cluster+route+sparse attn), 75.6k tok, 25% den
 # FETCH_SIZE / WRITE_SIZE calibrated against a 1 GiB device copy (FETCH x 2.0,
 # WRITE x 1.0); valid only for the attention source it was measured on.
 ATTN_TRAFFIC = {
-    "source_sha256": "cde5c90a30fb4ef090eceb147f339eaefcaec56121caed1147303c3d783dd9d2",
+    "source_sha256": "ee0857b4319373b5b0e84584c00b72d70f02fff87fa9ffd95bdcba648e6b8e2b",
     "workload": "wan",
-    "fetch_bytes": 36.73e9,
+    "fetch_bytes": 38.01e9,
     "write_bytes": 0.774e9,
 }
 PEAK_BF16_TFLOPS = 2500.0
