@@ -474,31 +474,61 @@ __global__ void __launch_bounds__(256) km_hist_kernel(const int32_t* __restrict_
 // scan: offsets (cluster starts), per-tile bases (in place over counts) and
 // the segment-sum chunk list.  One block of 1024 threads per (batch, head).
 // --------------------------------------------------------------------------
+constexpr int KM_SCAN_LDS = 16384;  // tile histograms of a head held in LDS (64 KB)
+
 __global__ void __launch_bounds__(1024) km_scan_kernel(int32_t* __restrict__ counts, int N, int C, int ntiles,
                                                        int rows, int32_t* __restrict__ offsets,
                                                        int32_t* __restrict__ chunk_start, uint32_t* __restrict__ nmax) {
   __shared__ int sm[16];
-  const int bh = blockIdx.x;
-  if (threadIdx.x == 0) nmax[bh] = 0u;  // the assign kernel of this round has finished
+  __shared__ int s_cnt[KM_SCAN_LDS];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  if (tid == 0) nmax[bh] = 0u;  // the assign kernel of this round has finished
   int32_t* cnt = counts + (size_t)bh * ntiles * C;
+  const int M = ntiles * C;
+  const bool in_lds = M <= KM_SCAN_LDS;
+  if (in_lds) {
+    // the whole [ntiles][C] block with coalesced loads, all in flight together
+    constexpr int PER = KM_SCAN_LDS / 1024;
+    int v[PER];
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int i = tid + 1024 * k;
+      v[k] = i < M ? cnt[i] : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int i = tid + 1024 * k;
+      if (i < M) s_cnt[i] = v[k];
+    }
+    __syncthreads();
+  }
   // the tile loops load SB tiles of all 4 clusters before using any, so the
   // loads are in flight together rather than one latency each
   constexpr int SB = 8;
   int tot[4] = {0, 0, 0, 0}, nch[4];
   int sum = 0, csum = 0;
-  for (int t0 = 0; t0 < ntiles; t0 += SB) {
-    int v[4][SB];
+  if (in_lds) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+    for (int e = 0; e < 4; ++e) {
+      const int c = tid * 4 + e;
+      if (c < C)
+        for (int t = 0; t < ntiles; ++t) tot[e] += s_cnt[t * C + c];
+    }
+  } else {
+    for (int t0 = 0; t0 < ntiles; t0 += SB) {
+      int v[4][SB];
 #pragma unroll
-      for (int i = 0; i < SB; ++i) {
-        const int c = threadIdx.x * 4 + e;
-        v[e][i] = (c < C && t0 + i < ntiles) ? cnt[(size_t)(t0 + i) * C + c] : 0;
-      }
+      for (int e = 0; e < 4; ++e)
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+        for (int i = 0; i < SB; ++i) {
+          const int c = tid * 4 + e;
+          v[e][i] = (c < C && t0 + i < ntiles) ? cnt[(size_t)(t0 + i) * C + c] : 0;
+        }
 #pragma unroll
-      for (int i = 0; i < SB; ++i) tot[e] += v[e][i];
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int i = 0; i < SB; ++i) tot[e] += v[e][i];
+    }
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -514,7 +544,7 @@ __global__ void __launch_bounds__(1024) km_scan_kernel(int32_t* __restrict__ cou
   int b[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const int c = threadIdx.x * 4 + e;
+    const int c = tid * 4 + e;
     if (c < C) {
       off[c] = base;
       cs[c] = cbase;
@@ -523,25 +553,41 @@ __global__ void __launch_bounds__(1024) km_scan_kernel(int32_t* __restrict__ cou
     base += tot[e];
     cbase += nch[e];
   }
-  for (int t0 = 0; t0 < ntiles; t0 += SB) {
-    int v[4][SB];
+  if (in_lds) {
+    // per-tile bases in place, then one coalesced write of the block
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+    for (int e = 0; e < 4; ++e) {
+      const int c = tid * 4 + e;
+      if (c < C)
+        for (int t = 0; t < ntiles; ++t) {
+          const int v = s_cnt[t * C + c];
+          s_cnt[t * C + c] = b[e];
+          b[e] += v;
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < M; i += 1024) cnt[i] = s_cnt[i];
+  } else {
+    for (int t0 = 0; t0 < ntiles; t0 += SB) {
+      int v[4][SB];
 #pragma unroll
-      for (int i = 0; i < SB; ++i) {
-        const int c = threadIdx.x * 4 + e;
-        v[e][i] = (c < C && t0 + i < ntiles) ? cnt[(size_t)(t0 + i) * C + c] : 0;
-      }
+      for (int e = 0; e < 4; ++e)
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
+        for (int i = 0; i < SB; ++i) {
+          const int c = tid * 4 + e;
+          v[e][i] = (c < C && t0 + i < ntiles) ? cnt[(size_t)(t0 + i) * C + c] : 0;
+        }
 #pragma unroll
-      for (int i = 0; i < SB; ++i) {
-        const int c = threadIdx.x * 4 + e;
-        if (c < C && t0 + i < ntiles) cnt[(size_t)(t0 + i) * C + c] = b[e];
-        b[e] += v[e][i];
-      }
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int i = 0; i < SB; ++i) {
+          const int c = tid * 4 + e;
+          if (c < C && t0 + i < ntiles) cnt[(size_t)(t0 + i) * C + c] = b[e];
+          b[e] += v[e][i];
+        }
+    }
   }
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     off[C] = total;
     cs[C] = ctotal;
   }
@@ -551,16 +597,37 @@ __global__ void __launch_bounds__(1024) km_scan_kernel(int32_t* __restrict__ cou
 // stable scatter: perm[dest] = token, tokens of one cluster in original order.
 // Each wave owns a contiguous quarter of the tile; equal labels inside a
 // 64-token step are matched with ballots over the label bits, so ranks come
-// out in lane order with no atomics.
+// out in lane order with no atomics.  The tile is first ordered by cluster in
+// LDS and then written out in that order, so neighbouring lanes store to
+// neighbouring addresses of perm (one run per cluster) instead of scattering
+// every token on its own.
 // --------------------------------------------------------------------------
+constexpr int KM_SCATTER_CPT = SVGEAR_MAX_CLUSTERS / 256;  // clusters per thread in the tile scan
+
+inline size_t km_scatter_lds(int C) { return (size_t)(5 * C + 2 * SORT_TILE) * sizeof(int32_t); }
+
 __global__ void __launch_bounds__(256) km_scatter_kernel(const int32_t* __restrict__ labels,
                                                          const int32_t* __restrict__ tile_base, int N, int C,
                                                          int ntiles, int ib, int32_t* __restrict__ perm) {
-  extern __shared__ int32_t hw[];  // [4][C]
+  // [4][C] per-wave bases inside the tile | [C] tile position -> perm index
+  // shift per cluster | [SORT_TILE] tokens and [SORT_TILE] destinations in
+  // cluster order
+  extern __shared__ int32_t hw[];
+  __shared__ int s_scan[16];
+  int32_t* shift = hw + 4 * C;
+  int32_t* s_tok = shift + C;
+  int32_t* s_dst = s_tok + SORT_TILE;
   const int bh = blockIdx.y, tile = blockIdx.x, lane = lane_id(), w = wave_id();
   const int32_t* lb = labels + (size_t)bh * N;
   int32_t* pb = perm + (size_t)bh * N;
   for (int c = threadIdx.x; c < 4 * C; c += 256) hw[c] = 0;
+  // each thread scans a contiguous run of clusters; its tile bases are
+  // loaded now and used after the counting pass
+  const int per = (C + 255) / 256, cr = threadIdx.x * per;
+  const int32_t* tb = tile_base + ((size_t)bh * ntiles + tile) * C;
+  int tbv[KM_SCATTER_CPT];
+#pragma unroll
+  for (int j = 0; j < KM_SCATTER_CPT; ++j) tbv[j] = (j < per && cr + j < C) ? tb[cr + j] : 0;
   __syncthreads();
   const int q0 = tile * SORT_TILE + w * (SORT_TILE / 4);
   const int q1 = min(N, q0 + SORT_TILE / 4);
@@ -574,38 +641,74 @@ __global__ void __launch_bounds__(256) km_scatter_kernel(const int32_t* __restri
     const int n = q0 + i * SV_WAVE + lane;
     labv[i] = n < q1 ? lb[n] : 0;
   }
-  for (int pass = 0; pass < 2; ++pass) {
+  // counting pass: the rank of each token among the equal labels of its
+  // step (bits 0-7) and their count (bits 8-15) are kept for the placing
+  // pass; the lowest such lane (rank 0) adds the count
+  int rk[STEPS];
 #pragma unroll
-    for (int i = 0; i < STEPS; ++i) {
-      const int n0 = q0 + i * SV_WAVE;
-      if (n0 >= q1) break;
-      const int n = n0 + lane;
-      const bool ok = n < q1;
-      const int lab = labv[i];
-      uint64_t peers = ballot(ok);
-      for (int b = 0; b < ib; ++b) {
-        const bool bit = (lab >> b) & 1;
-        const uint64_t m = ballot(bit);
-        peers &= bit ? m : ~m;
-      }
-      const int leader = __builtin_ctzll(peers | (1ull << 63));
-      const int cnt = __popcll(peers);
-      if (pass == 1 && ok) pb[mine[lab] + __popcll(peers & lt)] = n;
-      if (ok && lane == leader) mine[lab] += cnt;
+  for (int i = 0; i < STEPS; ++i) {
+    const int n0 = q0 + i * SV_WAVE;
+    if (n0 >= q1) break;
+    const bool ok = n0 + lane < q1;
+    const int lab = labv[i];
+    uint64_t peers = ballot(ok);
+    for (int b = 0; b < ib; ++b) {
+      const bool bit = (lab >> b) & 1;
+      const uint64_t m = ballot(bit);
+      peers &= bit ? m : ~m;
     }
-    if (pass == 0) {
-      __syncthreads();
-      const int32_t* tb = tile_base + ((size_t)bh * ntiles + tile) * C;
-      for (int c = threadIdx.x; c < C; c += 256) {
-        int b = tb[c];
+    const int rank = __popcll(peers & lt), cnt = __popcll(peers);
+    rk[i] = rank | (cnt << 8);
+    if (ok && rank == 0) mine[lab] += cnt;
+  }
+  // tile position of each (wave, cluster) run: clusters in order, waves in
+  // order inside a cluster
+  __syncthreads();
+  {
+    int sum = 0;
+#pragma unroll
+    for (int j = 0; j < KM_SCATTER_CPT; ++j) {
+      const int c = cr + j;
+      if (j < per && c < C) sum += hw[c] + hw[C + c] + hw[2 * C + c] + hw[3 * C + c];
+    }
+    int total;
+    int base = block_exscan(sum, s_scan, &total);
+#pragma unroll
+    for (int j = 0; j < KM_SCATTER_CPT; ++j) {
+      const int c = cr + j;
+      if (j < per && c < C) {
+        shift[c] = tbv[j] - base;
+#pragma unroll
         for (int ww = 0; ww < 4; ++ww) {
           const int v = hw[ww * C + c];
-          hw[ww * C + c] = b;
-          b += v;
+          hw[ww * C + c] = base;
+          base += v;
         }
       }
-      __syncthreads();
     }
+  }
+  __syncthreads();
+  // placing pass: tokens and their perm indices in cluster order
+#pragma unroll
+  for (int i = 0; i < STEPS; ++i) {
+    const int n0 = q0 + i * SV_WAVE;
+    if (n0 >= q1) break;
+    const int n = n0 + lane;
+    if (n < q1) {
+      const int lab = labv[i], rank = rk[i] & 255;
+      const int pos = mine[lab] + rank;
+      s_tok[pos] = n;
+      s_dst[pos] = pos + shift[lab];
+      if (rank == 0) mine[lab] = pos + (rk[i] >> 8);
+    }
+  }
+  __syncthreads();
+  const int nt = min(N - tile * SORT_TILE, SORT_TILE);
+  constexpr int PER = SORT_TILE / 256;
+#pragma unroll
+  for (int r = 0; r < PER; ++r) {
+    const int i = threadIdx.x + 256 * r;
+    if (i < nt) pb[s_dst[i]] = s_tok[i];
   }
 }
 
@@ -689,13 +792,14 @@ __global__ void __launch_bounds__(256) km_partial_kernel(const T* __restrict__ x
 }
 
 // means[c] = (sum of c's chunks, in order) / |c|.  Empty clusters: keep the
-// old value (k-means update) or write 0 (svgear_centroids).
+// old value (k-means update) or write 0 (svgear_centroids).  Each thread
+// owns four consecutive columns of one cluster (D is a multiple of 4).
 __global__ void __launch_bounds__(256) km_finalize_kernel(const float* __restrict__ partial,
                                                           const int32_t* __restrict__ offsets,
                                                           const int32_t* __restrict__ chunk_start, int C, int D,
                                                           int maxch, float* __restrict__ means, int keep_empty) {
   const int bh = blockIdx.y;
-  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int i = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= C * D) return;
   const int c = i / D, d = i - c * D;
   const int32_t* off = offsets + (size_t)bh * (C + 1);
@@ -703,23 +807,47 @@ __global__ void __launch_bounds__(256) km_finalize_kernel(const float* __restric
   const int n = off[c + 1] - off[c];
   float* out = means + ((size_t)bh * C + c) * D + d;
   if (n == 0) {
-    if (!keep_empty) *out = 0.f;
+    if (!keep_empty)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[e] = 0.f;
     return;
   }
   // chunks added in order; eight loads are issued before their adds
-  float s = 0.f;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
   int k = cs[c];
   const int k1 = cs[c + 1];
-  const float* pp = partial + (size_t)bh * maxch * D + d;
+  const float4* pp = reinterpret_cast<const float4*>(partial + (size_t)bh * maxch * D + d);
+  const int stride = D / 4;
   for (; k + 8 <= k1; k += 8) {
-    float v[8];
+    float4 v[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = pp[(size_t)(k + j) * D];
+    for (int j = 0; j < 8; ++j) v[j] = pp[(size_t)(k + j) * stride];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) s += v[j];
+    for (int j = 0; j < 8; ++j) {
+      s.x += v[j].x;
+      s.y += v[j].y;
+      s.z += v[j].z;
+      s.w += v[j].w;
+    }
   }
-  for (; k < k1; ++k) s += pp[(size_t)k * D];
-  *out = s / (float)n;
+  for (; k < k1; ++k) {
+    const float4 v = pp[(size_t)k * stride];
+    s.x += v.x;
+    s.y += v.y;
+    s.z += v.z;
+    s.w += v.w;
+  }
+  const float fn = (float)n;
+  out[0] = s.x / fn;
+  out[1] = s.y / fn;
+  out[2] = s.z / fn;
+  out[3] = s.w / fn;
+}
+
+static void launch_finalize(const float* partial, const int32_t* offsets, const int32_t* cs, int BH, int C, int D,
+                            int maxch, float* means, int keep_empty, hipStream_t st) {
+  hipLaunchKernelGGL(km_finalize_kernel, dim3(cdiv(C * D / 4, 256), BH), dim3(256), 0, st, partial, offsets, cs, C,
+                     D, maxch, means, keep_empty);
 }
 
 // ---------------------------------------------------------------- host side
@@ -785,6 +913,8 @@ static svgear_status kmeans_impl(const void* x, int BH, int N, int C, int iters,
   float* partial = reinterpret_cast<float*>(ws + p.off_partial);
   uint32_t* nmax = reinterpret_cast<uint32_t*>(ws + p.off_nmax);
   hipLaunchKernelGGL(km_clear_kernel, dim3(cdiv(BH, 256)), dim3(256), 0, st, nmax, BH);
+  (void)hipFuncSetAttribute((const void*)km_scatter_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)km_scatter_lds(C));
   for (int it = 0; it < iters; ++it) {
     hipLaunchKernelGGL((km_prep_kernel<D>), dim3(cdiv(p.Cpad, KM_PREP_ROWS), BH), dim3(256), 0, st, cent, C, p.Cpad,
                        ops, nmax);
@@ -793,13 +923,10 @@ static svgear_status kmeans_impl(const void* x, int BH, int N, int C, int iters,
     hipLaunchKernelGGL(km_hist_kernel, dim3(p.ntiles, BH), dim3(256), 0, st, labels, N, C, p.ntiles, counts);
     hipLaunchKernelGGL(km_scan_kernel, dim3(BH), dim3(1024), 0, st, counts, N, C, p.ntiles, MEAN_ROWS, offsets, cs,
                        nmax);
-    (void)hipFuncSetAttribute((const void*)km_scatter_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)(4 * C * sizeof(int32_t)));
-    hipLaunchKernelGGL(km_scatter_kernel, dim3(p.ntiles, BH), dim3(256), 4 * C * sizeof(int32_t), st, labels, counts,
-                       N, C, p.ntiles, p.ib, perm);
+    hipLaunchKernelGGL(km_scatter_kernel, dim3(p.ntiles, BH), dim3(256), km_scatter_lds(C), st, labels, counts, N,
+                       C, p.ntiles, p.ib, perm);
     launch_partial<T, D>(x, perm, offsets, cs, BH, N, C, p.maxch, partial, nullptr, st);
-    hipLaunchKernelGGL(km_finalize_kernel, dim3(cdiv(C * D, 256), BH), dim3(256), 0, st, partial, offsets, cs, C, D,
-                       p.maxch, cent, 1);
+    launch_finalize(partial, offsets, cs, BH, C, D, p.maxch, cent, 1, st);
   }
   return check_launch("svgear_kmeans");
 }
@@ -864,8 +991,7 @@ extern "C" svgear_status svgear_centroids(const void* x, svgear_dtype dt, int B,
     else launch_partial<float, 64>(x, perm, offsets, cs, BH, N, C, p.maxch, partial, x_perm, stream);
   }
   if (means)
-    hipLaunchKernelGGL(km_finalize_kernel, dim3(cdiv(C * D, 256), BH), dim3(256), 0, stream, partial, offsets, cs, C,
-                       D, p.maxch, means, 0);
+    launch_finalize(partial, offsets, cs, BH, C, D, p.maxch, means, 0, stream);
   return check_launch("svgear_centroids");
 }
 
@@ -893,7 +1019,6 @@ extern "C" svgear_status svgear_centroid_variances(const void* x, svgear_dtype d
     if (D == 128) launch_partial_sq<float, 128>(x, perm, offsets, cs, BH, N, C, p.maxch, partial, means, stream);
     else launch_partial_sq<float, 64>(x, perm, offsets, cs, BH, N, C, p.maxch, partial, means, stream);
   }
-  hipLaunchKernelGGL(km_finalize_kernel, dim3(cdiv(C * D, 256), BH), dim3(256), 0, stream, partial, offsets, cs, C, D,
-                     p.maxch, vars, 0);
+  launch_finalize(partial, offsets, cs, BH, C, D, p.maxch, vars, 0, stream);
   return check_launch("svgear_centroid_variances");
 }
