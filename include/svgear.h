@@ -87,7 +87,12 @@ const char* svgear_last_error(void);
  *              lowest index (distances within 1e-5 relative of the minimum
  *              may resolve either way).  Update: each non-empty cluster's
  *              centroid becomes the mean of its members; an empty cluster
- *              keeps its centroid.
+ *              keeps its centroid.  The first three updates sum every
+ *              cluster from the sorted tokens; with more rounds, the third
+ *              keeps exact fixed-point sums (values rounded to a step of at
+ *              most 2^-30 of the largest row norm, per head) and every later
+ *              update adds or removes only the tokens whose label changed,
+ *              so results do not depend on the order of any addition.
  *   labels     [B,H,N] int32 OUT, the last assignment.
  *   perm       [B,H,N] int32 OUT, perm[p] = source token of permuted slot p:
  *              tokens grouped by label, original order inside a cluster.

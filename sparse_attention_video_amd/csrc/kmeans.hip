@@ -12,6 +12,8 @@
 // stable scatter (perm) -> chunked segment sums -> means.
 #include <float.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "host.h"
 #include "scan.h"
@@ -24,6 +26,8 @@ constexpr int SORT_TILE = 4096;     // tokens per histogram / scatter tile
 constexpr int MEAN_ROWS = 256;      // rows per segment-sum chunk
 constexpr float PAD_NORM = 1e30f;   // squared norm given to padding centroids
 constexpr int KM_PREP_ROWS = 32;    // centroid rows per prep workgroup
+constexpr int KM_FULL_ROUNDS = 3;  // rounds whose update re-sorts every token
+constexpr int KM_FX_BITS = 30;      // fixed-point values: |x| * 2^s < 2^30 (int32); sums of < 2^24 rows < 2^54
 
 // --------------------------------------------------------------------------
 // prep: per (batch, head), the bf16 operands of the distance GEMM, one row
@@ -33,19 +37,22 @@ constexpr int KM_PREP_ROWS = 32;    // centroid rows per prep workgroup
 //   [D + 16, 2D+16) lo part of -2 c
 // Padding rows (c >= C) get zeros and n = PAD_NORM, so they never win.
 // nmax[bh] collects the largest ||c||^2 (bit pattern) for the error window;
-// it is cleared by km_scan_kernel (and once before the first round).
+// it is cleared by km_scan_kernel or km_delta_kernel (and once before the
+// first round).
 // --------------------------------------------------------------------------
 template <int D>
 constexpr int km_row() { return 2 * D + KM_EXTRA; }
 
 template <int D>
 __global__ void __launch_bounds__(256) km_prep_kernel(const float* __restrict__ cent, int C, int Cpad,
-                                                      bf16* __restrict__ ops, uint32_t* __restrict__ nmax) {
+                                                      bf16* __restrict__ ops, uint32_t* __restrict__ nmax,
+                                                      int32_t* __restrict__ mtot) {
   constexpr int EPL = D / SV_WAVE;  // elements per lane
   constexpr int RW = km_row<D>();
   __shared__ double s_max[4];
   const int bh = blockIdx.y, lane = lane_id(), w = wave_id();
   const float* cb = cent + (size_t)bh * C * D;
+  if (mtot && blockIdx.x == 0 && threadIdx.x == 0) mtot[bh] = 0;  // the previous update has read it
   double wmax = 0.0;
   // the wave's rows are loaded before the first one is processed
   constexpr int RR = KM_PREP_ROWS / 4;
@@ -119,7 +126,8 @@ template <typename T, int D>
 __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) km_assign_kernel(const T* __restrict__ x, const bf16* __restrict__ ops,
                                                         const uint32_t* __restrict__ nmax,
                                                         const float* __restrict__ cent, int N, int C, int Cpad, int ib,
-                                                        int32_t* __restrict__ labels) {
+                                                        int32_t* __restrict__ labels, int2* __restrict__ moved,
+                                                        int32_t* __restrict__ mtot, uint32_t* __restrict__ r2max) {
   constexpr bool F32 = sizeof(T) == 4;
   constexpr int KS = D / 16;
   constexpr int RW = km_row<D>();          // operand row (bf16 elements)
@@ -181,6 +189,14 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) 
       }
     }
     xx[t] = part + shfl_xor(part, 32);
+  }
+  if (r2max) {
+    // an upper bound on max ||x||^2 (fp32 sum of D squares, relative error
+    // below D u < 1e-5), the basis of the fixed-point scale
+    float m = fmaxf(xx[0], xx[1]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, SV_WAVE));
+    if (lane == 0 && m > 0.f) atomicMax(&r2max[bh], __float_as_uint(m * (1.f + 1e-5f)));
   }
 
   const uint32_t imask = (1u << ib) - 1u;
@@ -362,6 +378,9 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) 
   constexpr int EPG = D / 16;
   const int grp = lane >> 4, gl = lane & 15;
   __shared__ float s_x[4][D];
+  // tokens whose label changes (tracking rounds only): (token, old | new << 16)
+  int2 mv[2];
+  uint64_t mvb[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int n_mine = tok0 + 32 * t + col;
@@ -434,7 +453,31 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) 
       }
       if (lane == src) lab[t] = bidx;
     }
-    if (half == 0 && n_mine < N) labels[(size_t)bh * N + n_mine] = min(lab[t], C - 1);
+    const bool mine = half == 0 && n_mine < N;
+    const int lnew = min(lab[t], C - 1);
+    if (moved) {
+      const int lold = mine ? labels[(size_t)bh * N + n_mine] : lnew;
+      mvb[t] = ballot(lold != lnew);
+      mv[t] = make_int2(n_mine, lold | (lnew << 16));
+    }
+    if (mine) labels[(size_t)bh * N + n_mine] = lnew;
+  }
+  if (moved) {
+    // one slot reservation per wave; the order of the list is immaterial
+    // (the update adds integers)
+    const int n0 = __popcll(mvb[0]), nt = n0 + __popcll(mvb[1]);
+    if (nt > 0) {
+      int base = 0;
+      if (lane == 0) base = atomicAdd(&mtot[bh], nt);
+      base = __shfl(base, 0, SV_WAVE);
+      int2* mb = moved + (size_t)bh * N;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        if ((mvb[t] >> lane) & 1) {
+          const int r = __builtin_amdgcn_mbcnt_hi((uint32_t)(mvb[t] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mvb[t], 0));
+          mb[base + (t ? n0 : 0) + r] = mv[t];
+        }
+    }
   }
 }
 
@@ -713,22 +756,41 @@ __global__ void __launch_bounds__(256) km_scatter_kernel(const int32_t* __restri
 }
 
 // --------------------------------------------------------------------------
+// Fixed-point values for the exact k-means sums (rounds after the first
+// three): v -> rint(v * 2^s), one power-of-two shift s per head.  With r2 a
+// bound on max ||x||^2 < 2^E2, every |x_d| < 2^e with e = ceil(E2 / 2), so
+// s = 30 - e keeps each value inside int32 and a sum of N < 2^24 of them
+// inside int64; integer sums are exact, so they do not depend on the order
+// of the additions.  The absolute error of a value is at most 2^(e - 31).
+// --------------------------------------------------------------------------
+__device__ __forceinline__ int km_fx_shift(uint32_t r2_bits) {
+  const int E = (int)((r2_bits >> 23) & 0xff);
+  const int E2 = (E ? E : 1) - 126;  // r2 < 2^E2
+  return KM_FX_BITS - ((E2 + 1) >> 1);
+}
+
+__device__ __forceinline__ int km_fx_q(float v, int s) { return (int)rintf(ldexpf(v, s)); }
+
+// --------------------------------------------------------------------------
 // segment sums over the permuted order: chunk k of cluster c sums rows
 // [offsets[c] + k' * rows, ...) of x[perm[.]] (k' = k - chunk_start[c]),
 // optionally writing the permuted copy.  Fixed row-to-lane mapping and a
 // fixed reduction order keep the sums deterministic.  SQ: sums of squared
 // deviations from the cluster means `center` instead (variances).
 // --------------------------------------------------------------------------
-template <typename T, int D, bool SQ = false>
+template <typename T, int D, bool SQ = false, bool FX = false>
 __global__ void __launch_bounds__(256) km_partial_kernel(const T* __restrict__ x, const int32_t* __restrict__ perm,
                                                          const int32_t* __restrict__ offsets,
                                                          const int32_t* __restrict__ chunk_start, int N, int C,
                                                          int rows, int maxch, float* __restrict__ partial,
-                                                         T* __restrict__ x_perm, const float* __restrict__ center = nullptr) {
+                                                         T* __restrict__ x_perm, const float* __restrict__ center = nullptr,
+                                                         long long* __restrict__ pfx = nullptr,
+                                                         const uint32_t* __restrict__ r2max = nullptr) {
   constexpr int EPL = 16 / sizeof(T);     // elements per lane (one 16-byte load)
   constexpr int LPR = D / EPL;            // lanes per row
   constexpr int RPI = 256 / LPR;          // rows per iteration
-  __shared__ float red[RPI * D];
+  using Acc = std::conditional_t<FX, long long, float>;
+  __shared__ Acc red[RPI * D];
   __shared__ int s_c;
   const int bh = blockIdx.y, k = blockIdx.x;
   const int32_t* cs = chunk_start + (size_t)bh * (C + 1);
@@ -743,14 +805,18 @@ __global__ void __launch_bounds__(256) km_partial_kernel(const T* __restrict__ x
   const T* xb = x + (size_t)bh * N * D;
   const int32_t* pb = perm + (size_t)bh * N;
   T* xpb = x_perm ? x_perm + (size_t)bh * N * D : nullptr;
-  float acc[EPL], mu[EPL];
+  Acc acc[EPL];
+  float mu[EPL];
+  const int fs = FX ? km_fx_shift(r2max[bh]) : 0;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
-    acc[e] = 0.f;
+    acc[e] = 0;
     mu[e] = SQ ? center[((size_t)bh * C + c) * D + e0 + e] : 0.f;
   }
   auto add = [&](float v, int e) {
-    if constexpr (SQ) {
+    if constexpr (FX) {
+      acc[e] += km_fx_q(v, fs);
+    } else if constexpr (SQ) {
       const float dv = v - mu[e];
       acc[e] = fmaf(dv, dv, acc[e]);
     } else {
@@ -785,19 +851,29 @@ __global__ void __launch_bounds__(256) km_partial_kernel(const T* __restrict__ x
   for (int e = 0; e < EPL; ++e) red[g * D + e0 + e] = acc[e];
   __syncthreads();
   for (int d = threadIdx.x; d < D; d += 256) {
-    float s = 0.f;
+    Acc s = 0;
     for (int gg = 0; gg < RPI; ++gg) s += red[gg * D + d];
-    partial[((size_t)bh * maxch + k) * D + d] = s;
+    if constexpr (FX) pfx[((size_t)bh * maxch + k) * D + d] = s;
+    else partial[((size_t)bh * maxch + k) * D + d] = s;
   }
 }
 
 // means[c] = (sum of c's chunks, in order) / |c|.  Empty clusters: keep the
 // old value (k-means update) or write 0 (svgear_centroids).  Each thread
 // owns four consecutive columns of one cluster (D is a multiple of 4).
+// With fx set (the last full round of a k-means call that continues with
+// incremental rounds), the chunk sums are the fixed-point integers of
+// km_partial_kernel<..., FX>: their total goes to fx, the cluster size to
+// fxcnt, and the mean is taken from fx the way the incremental update takes
+// it.
 __global__ void __launch_bounds__(256) km_finalize_kernel(const float* __restrict__ partial,
                                                           const int32_t* __restrict__ offsets,
                                                           const int32_t* __restrict__ chunk_start, int C, int D,
-                                                          int maxch, float* __restrict__ means, int keep_empty) {
+                                                          int maxch, float* __restrict__ means, int keep_empty,
+                                                          long long* __restrict__ fx = nullptr,
+                                                          int32_t* __restrict__ fxcnt = nullptr,
+                                                          const long long* __restrict__ pfx = nullptr,
+                                                          const uint32_t* __restrict__ r2max = nullptr) {
   const int bh = blockIdx.y;
   const int i = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= C * D) return;
@@ -806,37 +882,51 @@ __global__ void __launch_bounds__(256) km_finalize_kernel(const float* __restric
   const int32_t* cs = chunk_start + (size_t)bh * (C + 1);
   const int n = off[c + 1] - off[c];
   float* out = means + ((size_t)bh * C + c) * D + d;
+  long long* fo = fx ? fx + ((size_t)bh * C + c) * D + d : nullptr;
+  if (fx && d == 0) fxcnt[(size_t)bh * C + c] = n;
   if (n == 0) {
     if (!keep_empty)
 #pragma unroll
       for (int e = 0; e < 4; ++e) out[e] = 0.f;
+    if (fo)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) fo[e] = 0;
     return;
   }
   // chunks added in order; eight loads are issued before their adds
   float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
   int k = cs[c];
   const int k1 = cs[c + 1];
+  if (fo) {
+    long long q[4] = {0, 0, 0, 0};
+    const long long* pq = pfx + (size_t)bh * maxch * D + d;
+    for (; k < k1; ++k)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) q[e] += pq[(size_t)k * D + e];
+    const int fs = km_fx_shift(r2max[bh]);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      fo[e] = q[e];
+      out[e] = (float)(ldexp((double)q[e], -fs) / (double)n);
+    }
+    return;
+  }
   const float4* pp = reinterpret_cast<const float4*>(partial + (size_t)bh * maxch * D + d);
   const int stride = D / 4;
+  auto add4 = [&](const float4& v) {
+    s.x += v.x;
+    s.y += v.y;
+    s.z += v.z;
+    s.w += v.w;
+  };
   for (; k + 8 <= k1; k += 8) {
     float4 v[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) v[j] = pp[(size_t)(k + j) * stride];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      s.x += v[j].x;
-      s.y += v[j].y;
-      s.z += v[j].z;
-      s.w += v[j].w;
-    }
+    for (int j = 0; j < 8; ++j) add4(v[j]);
   }
-  for (; k < k1; ++k) {
-    const float4 v = pp[(size_t)k * stride];
-    s.x += v.x;
-    s.y += v.y;
-    s.z += v.z;
-    s.w += v.w;
-  }
+  for (; k < k1; ++k) add4(pp[(size_t)k * stride]);
   const float fn = (float)n;
   out[0] = s.x / fn;
   out[1] = s.y / fn;
@@ -850,10 +940,133 @@ static void launch_finalize(const float* partial, const int32_t* offsets, const 
                      D, maxch, means, keep_empty);
 }
 
+// --------------------------------------------------------------------------
+// incremental update (rounds after the first three): only tokens whose label
+// changed touch the sums.  Each workgroup owns kcl <= KD_CL clusters, picks
+// from the moved list the entries that enter or leave them, adds the
+// fixed-point values +-rint(x * 2^s) into LDS integer accumulators (exact, so
+// the order of the list and of the atomics does not matter), then updates
+// the owned clusters' fixed-point sums, sizes and means.  Clusters no entry
+// touched keep everything.
+// --------------------------------------------------------------------------
+constexpr int KD_CL = 8;      // most clusters per workgroup
+constexpr int KD_WIN = 1024;  // moved entries examined per window (4 per thread)
+
+template <typename T, int D>
+__global__ void __launch_bounds__(256) km_delta_kernel(const T* __restrict__ x, const int2* __restrict__ moved,
+                                                       const int32_t* __restrict__ mtot,
+                                                       const uint32_t* __restrict__ r2max, int N, int C, int kcl,
+                                                       long long* __restrict__ fx, int32_t* __restrict__ fxcnt,
+                                                       float* __restrict__ cent, uint32_t* __restrict__ nmax) {
+  constexpr int EPL = 16 / sizeof(T);  // elements per 16-byte load
+  constexpr int LPR = D / EPL;         // lanes per row
+  constexpr int RPI = 256 / LPR;       // rows per iteration
+  constexpr int UR = 4;                // rows per thread loaded together
+  __shared__ unsigned long long acc[KD_CL * D];
+  __shared__ int s_m[2 * KD_WIN];  // token | local cluster << 24 | leaving << 27
+  __shared__ int s_dc[KD_CL], s_cnt[KD_CL], s_nm;
+  const int bh = blockIdx.y, c0 = blockIdx.x * kcl, tid = threadIdx.x;
+  if (blockIdx.x == 0 && tid == 0) nmax[bh] = 0u;  // the assign kernel of this round has finished
+  const int2* mb = moved + (size_t)bh * N;
+  // loads that do not depend on the list length go out with it: the owned
+  // clusters' sums and sizes and the first window of the list (the list
+  // buffer holds N entries, so reading past the length stays inside it)
+  constexpr int FPT = KD_CL * D / 256;  // owned sum entries per thread
+  long long fxv[FPT];
+#pragma unroll
+  for (int j = 0; j < FPT; ++j) {
+    const int i = tid + 256 * j, c = c0 + i / D;
+    fxv[j] = (i < kcl * D && c < C) ? fx[((size_t)bh * C + c0) * D + i] : 0;
+  }
+  const int cnt0 = (tid < kcl && c0 + tid < C) ? fxcnt[(size_t)bh * C + c0 + tid] : 0;
+  int2 ev[KD_WIN / 256];
+#pragma unroll
+  for (int j = 0; j < KD_WIN / 256; ++j) {
+    const int idx = tid + 256 * j;
+    ev[j] = idx < N ? mb[idx] : make_int2(0, -1);
+  }
+  const int M = mtot[bh];
+  if (M == 0) return;
+  for (int i = tid; i < KD_CL * D; i += 256) acc[i] = 0ull;
+  if (tid < KD_CL) s_dc[tid] = 0;
+  const int fs = km_fx_shift(r2max[bh]);
+  const T* xb = x + (size_t)bh * N * D;
+  const int g = tid / LPR, e0 = (tid % LPR) * EPL;
+  int touched = 0;  // per-thread bit mask of owned clusters seen
+  for (int w0 = 0; w0 < M; w0 += KD_WIN) {
+    if (tid == 0) s_nm = 0;
+    __syncthreads();
+    if (w0 > 0)
+#pragma unroll
+      for (int j = 0; j < KD_WIN / 256; ++j) {
+        const int idx = w0 + tid + 256 * j;
+        ev[j] = idx < M ? mb[idx] : make_int2(0, -1);
+      }
+#pragma unroll
+    for (int j = 0; j < KD_WIN / 256; ++j) {
+      if (w0 + tid + 256 * j >= M || ev[j].y < 0) continue;
+      const int lo = (ev[j].y & 0xffff) - c0, ln = (ev[j].y >> 16) - c0;
+      if ((unsigned)ln < (unsigned)kcl) s_m[atomicAdd(&s_nm, 1)] = ev[j].x | (ln << 24);
+      if ((unsigned)lo < (unsigned)kcl) s_m[atomicAdd(&s_nm, 1)] = ev[j].x | (lo << 24) | (1 << 27);
+    }
+    __syncthreads();
+    const int nm = s_nm;
+    for (int r0 = 0; r0 < nm; r0 += UR * RPI) {
+      int code[UR];
+      u32x4 v[UR];
+#pragma unroll
+      for (int u = 0; u < UR; ++u) {
+        const int r = r0 + u * RPI + g;
+        code[u] = r < nm ? s_m[r] : -1;
+        if (code[u] >= 0) v[u] = ld16(xb + (size_t)(code[u] & 0xffffff) * D + e0);
+      }
+#pragma unroll
+      for (int u = 0; u < UR; ++u) {
+        if (code[u] < 0) continue;
+        const int lc = (code[u] >> 24) & 7;
+        const bool leave = (code[u] >> 27) & 1;
+        const T* tv = reinterpret_cast<const T*>(&v[u]);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          const long long q = km_fx_q(to_f32(tv[e]), fs);
+          atomicAdd(&acc[lc * D + e0 + e], (unsigned long long)(leave ? -q : q));
+        }
+        if (e0 == 0) atomicAdd(&s_dc[lc], leave ? -1 : 1);
+        touched |= 1 << lc;
+      }
+    }
+    __syncthreads();
+  }
+  // which owned clusters any entry touched (each thread saw a subset)
+  __shared__ int s_touch;
+  if (tid == 0) s_touch = 0;
+  __syncthreads();
+  if (touched) atomicOr(&s_touch, touched);
+  __syncthreads();
+  const int tmask = s_touch;
+  if (tid < kcl && ((tmask >> tid) & 1) && c0 + tid < C) {
+    const int n = cnt0 + s_dc[tid];
+    fxcnt[(size_t)bh * C + c0 + tid] = n;
+    s_cnt[tid] = n;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < FPT; ++j) {
+    const int i = tid + 256 * j;
+    const int lc = i / D, c = c0 + lc;
+    if (i >= kcl * D || c >= C || !((tmask >> lc) & 1)) continue;
+    const size_t o = ((size_t)bh * C + c0) * D + i;
+    const long long q = fxv[j] + (long long)acc[i];
+    fx[o] = q;
+    const int n = s_cnt[lc];
+    if (n > 0) cent[o] = (float)(ldexp((double)q, -fs) / (double)n);  // an emptied cluster keeps its centroid
+  }
+}
+
 // ---------------------------------------------------------------- host side
 struct KmPlan {
   int BH, Cpad, ib, ntiles, maxch;
-  size_t off_ops, off_nmax, off_counts, off_cs, off_partial, total;
+  size_t off_ops, off_nmax, off_counts, off_cs, off_partial, off_pfx, off_fx, off_fxcnt, off_moved, off_mtot, off_r2max, total;
 };
 
 static KmPlan km_plan(int B, int H, int N, int D, int C) {
@@ -870,6 +1083,12 @@ static KmPlan km_plan(int B, int H, int N, int D, int C) {
   p.off_counts = cv.used; cv.take<int32_t>((size_t)p.BH * p.ntiles * C);
   p.off_cs = cv.used; cv.take<int32_t>((size_t)p.BH * (C + 1));
   p.off_partial = cv.used; cv.take<float>((size_t)p.BH * p.maxch * D);
+  p.off_pfx = cv.used; cv.take<long long>((size_t)p.BH * p.maxch * D);
+  p.off_fx = cv.used; cv.take<long long>((size_t)p.BH * C * D);
+  p.off_fxcnt = cv.used; cv.take<int32_t>((size_t)p.BH * C);
+  p.off_moved = cv.used; cv.take<int2>((size_t)p.BH * N);
+  p.off_mtot = cv.used; cv.take<int32_t>(p.BH);
+  p.off_r2max = cv.used; cv.take<uint32_t>(p.BH);
   p.total = cv.used;
   return p;
 }
@@ -912,22 +1131,55 @@ static svgear_status kmeans_impl(const void* x, int BH, int N, int C, int iters,
   int32_t* cs = reinterpret_cast<int32_t*>(ws + p.off_cs);
   float* partial = reinterpret_cast<float*>(ws + p.off_partial);
   uint32_t* nmax = reinterpret_cast<uint32_t*>(ws + p.off_nmax);
+  long long* pfx = reinterpret_cast<long long*>(ws + p.off_pfx);
+  long long* fx = reinterpret_cast<long long*>(ws + p.off_fx);
+  int32_t* fxcnt = reinterpret_cast<int32_t*>(ws + p.off_fxcnt);
+  int2* moved = reinterpret_cast<int2*>(ws + p.off_moved);
+  int32_t* mtot = reinterpret_cast<int32_t*>(ws + p.off_mtot);
+  uint32_t* r2max = reinterpret_cast<uint32_t*>(ws + p.off_r2max);
+  // The first KM_FULL_ROUNDS updates recompute every sum from the sorted
+  // tokens (the first rounds move many tokens); the last of them leaves
+  // exact fixed-point sums, and every later round updates those from the
+  // tokens whose label changed.
+  const int nfull = iters > KM_FULL_ROUNDS ? KM_FULL_ROUNDS : iters;
+  const bool incr = iters > nfull;
+  // clusters per delta workgroup: enough workgroups to fill the chip
+  const int kcl = std::max(1, std::min(KD_CL, cdiv(C * BH, 2048)));
   hipLaunchKernelGGL(km_clear_kernel, dim3(cdiv(BH, 256)), dim3(256), 0, st, nmax, BH);
+  if (incr) hipLaunchKernelGGL(km_clear_kernel, dim3(cdiv(BH, 256)), dim3(256), 0, st, r2max, BH);
   (void)hipFuncSetAttribute((const void*)km_scatter_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)km_scatter_lds(C));
-  for (int it = 0; it < iters; ++it) {
-    hipLaunchKernelGGL((km_prep_kernel<D>), dim3(cdiv(p.Cpad, KM_PREP_ROWS), BH), dim3(256), 0, st, cent, C, p.Cpad,
-                       ops, nmax);
-    hipLaunchKernelGGL((km_assign_kernel<T, D>), dim3(cdiv(N, KM_TOK_WG), BH), dim3(256), 0, st, (const T*)x, ops,
-                       nmax, cent, N, C, p.Cpad, p.ib, labels);
+  auto sort_labels = [&]() {  // tile histograms -> offsets -> stable perm
     hipLaunchKernelGGL(km_hist_kernel, dim3(p.ntiles, BH), dim3(256), 0, st, labels, N, C, p.ntiles, counts);
     hipLaunchKernelGGL(km_scan_kernel, dim3(BH), dim3(1024), 0, st, counts, N, C, p.ntiles, MEAN_ROWS, offsets, cs,
                        nmax);
     hipLaunchKernelGGL(km_scatter_kernel, dim3(p.ntiles, BH), dim3(256), km_scatter_lds(C), st, labels, counts, N,
                        C, p.ntiles, p.ib, perm);
-    launch_partial<T, D>(x, perm, offsets, cs, BH, N, C, p.maxch, partial, nullptr, st);
-    launch_finalize(partial, offsets, cs, BH, C, D, p.maxch, cent, 1, st);
+  };
+  for (int it = 0; it < iters; ++it) {
+    const bool track = it >= nfull;             // incremental round
+    const bool setup = incr && it == nfull - 1;  // full round that sets up the fixed-point sums
+    hipLaunchKernelGGL((km_prep_kernel<D>), dim3(cdiv(p.Cpad, KM_PREP_ROWS), BH), dim3(256), 0, st, cent, C, p.Cpad,
+                       ops, nmax, track ? mtot : nullptr);
+    hipLaunchKernelGGL((km_assign_kernel<T, D>), dim3(cdiv(N, KM_TOK_WG), BH), dim3(256), 0, st, (const T*)x, ops,
+                       nmax, cent, N, C, p.Cpad, p.ib, labels, track ? moved : nullptr, mtot,
+                       setup ? r2max : nullptr);
+    if (track) {
+      hipLaunchKernelGGL((km_delta_kernel<T, D>), dim3(cdiv(C, kcl), BH), dim3(256), 0, st, (const T*)x, moved, mtot,
+                         r2max, N, C, kcl, fx, fxcnt, cent, nmax);
+    } else if (setup) {
+      sort_labels();
+      hipLaunchKernelGGL((km_partial_kernel<T, D, false, true>), dim3(p.maxch, BH), dim3(256), 0, st, (const T*)x,
+                         perm, offsets, cs, N, C, MEAN_ROWS, p.maxch, partial, (T*)nullptr, nullptr, pfx, r2max);
+      hipLaunchKernelGGL(km_finalize_kernel, dim3(cdiv(C * D / 4, 256), BH), dim3(256), 0, st, partial, offsets, cs,
+                         C, D, p.maxch, cent, 1, fx, fxcnt, pfx, r2max);
+    } else {
+      sort_labels();
+      launch_partial<T, D>(x, perm, offsets, cs, BH, N, C, p.maxch, partial, nullptr, st);
+      launch_finalize(partial, offsets, cs, BH, C, D, p.maxch, cent, 1, st);
+    }
   }
+  if (incr) sort_labels();  // perm and offsets of the last labels
   return check_launch("svgear_kmeans");
 }
 

@@ -150,6 +150,37 @@ def test_kmeans_singletons_and_single_cluster(sv):
         np.testing.assert_allclose(host(cent)[0, 0], Co, rtol=0, atol=1e-5)
 
 
+@pytest.mark.parametrize("dtype,D", [("f32", 64), ("bf16", 128)])
+def test_kmeans_cluster_emptied_in_later_round(sv, dtype, D):
+    """A cluster that loses every member after the first round keeps its
+    centroid, and the clusters its members join get the right means.  Along
+    the first axis: 40 points near 0, 40 near 4, and two points at 0.9 and
+    3.1.  Centroids start at -1.5, 5.5 and 2.0: the two lone points first go
+    to the middle centroid; once the outer centroids have moved onto their
+    groups each lone point is nearer to an outer one (0.9 against 1.1), so
+    the middle cluster empties in the second round and stays empty."""
+    from synth.gen import bf16_bits
+    rng = np.random.default_rng(7)
+    N = 82
+    X = rng.normal(0.0, 0.01, (1, N, D))
+    X[0, 40:80, 0] += 4.0
+    X[0, 80, 0], X[0, 81, 0] = 0.9, 3.1
+    X = X.astype(np.float32)
+    if dtype == "bf16":
+        X = (bf16_bits(X).astype(np.uint32) << 16).view(np.float32)
+    C0 = np.zeros((1, 3, D), np.float32)
+    C0[0, :, 0] = (-1.5, 5.5, 2.0)
+    cent = f32(C0[:, None])
+    lab, perm, off = sv.kmeans(to_dev(X[:, None], dtype), cent, 4)
+    Co, lo = orc.lloyd(X[0].astype(np.float64), C0[0].astype(np.float64), 4)
+    assert (lo[80], lo[81]) == (0, 1) and not (lo == 2).any()
+    np.testing.assert_array_equal(host(lab)[0, 0], lo)
+    po, oo = orc.permute(lo, 3)
+    np.testing.assert_array_equal(host(perm)[0, 0], po)
+    np.testing.assert_array_equal(host(off)[0, 0], oo)
+    np.testing.assert_allclose(host(cent)[0, 0], Co, rtol=0, atol=1e-5)
+
+
 # ------------------------------------------------------------------ centroids
 @pytest.mark.parametrize("name", list(CASES))
 def test_centroids_gather_and_means(sv, name, ref_cache):
