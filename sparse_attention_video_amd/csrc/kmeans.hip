@@ -27,6 +27,7 @@ constexpr int MEAN_ROWS = 256;      // rows per segment-sum chunk
 constexpr float PAD_NORM = 1e30f;   // squared norm given to padding centroids
 constexpr int KM_PREP_ROWS = 32;    // centroid rows per prep workgroup
 constexpr int KM_FULL_ROUNDS = 3;  // rounds whose update re-sorts every token
+constexpr int KM_MSLOTS = 16;      // per-head counters (and sub-lists) the assign waves spread their atomics over
 constexpr int KM_FX_BITS = 30;      // fixed-point values: |x| * 2^s < 2^30 (int32); sums of < 2^24 rows < 2^54
 
 // --------------------------------------------------------------------------
@@ -43,6 +44,12 @@ constexpr int KM_FX_BITS = 30;      // fixed-point values: |x| * 2^s < 2^30 (int
 template <int D>
 constexpr int km_row() { return 2 * D + KM_EXTRA; }
 
+// Moved-token sub-list capacity: assign wave i of a head (64 tokens) appends
+// to sub-list i mod KM_MSLOTS, so a sub-list never holds more than this.
+inline __host__ __device__ int km_mcap(int N) {
+  return ((N + KM_TOK_WG - 1) / KM_TOK_WG * 4 + KM_MSLOTS - 1) / KM_MSLOTS * 64;
+}
+
 template <int D>
 __global__ void __launch_bounds__(256) km_prep_kernel(const float* __restrict__ cent, int C, int Cpad,
                                                       bf16* __restrict__ ops, uint32_t* __restrict__ nmax,
@@ -52,7 +59,7 @@ __global__ void __launch_bounds__(256) km_prep_kernel(const float* __restrict__ 
   __shared__ double s_max[4];
   const int bh = blockIdx.y, lane = lane_id(), w = wave_id();
   const float* cb = cent + (size_t)bh * C * D;
-  if (mtot && blockIdx.x == 0 && threadIdx.x == 0) mtot[bh] = 0;  // the previous update has read it
+  if (mtot && blockIdx.x == 0 && threadIdx.x < KM_MSLOTS) mtot[bh * KM_MSLOTS + threadIdx.x] = 0;  // read by the previous update
   double wmax = 0.0;
   // the wave's rows are loaded before the first one is processed
   constexpr int RR = KM_PREP_ROWS / 4;
@@ -196,7 +203,8 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) 
     float m = fmaxf(xx[0], xx[1]);
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, SV_WAVE));
-    if (lane == 0 && m > 0.f) atomicMax(&r2max[bh], __float_as_uint(m * (1.f + 1e-5f)));
+    if (lane == 0 && m > 0.f)
+      atomicMax(&r2max[bh * KM_MSLOTS + ((blockIdx.x * 4 + w) & (KM_MSLOTS - 1))], __float_as_uint(m * (1.f + 1e-5f)));
   }
 
   const uint32_t imask = (1u << ib) - 1u;
@@ -463,14 +471,15 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) 
     if (mine) labels[(size_t)bh * N + n_mine] = lnew;
   }
   if (moved) {
-    // one slot reservation per wave; the order of the list is immaterial
-    // (the update adds integers)
+    // one reservation per wave in its sub-list; the order of the list is
+    // immaterial (the update adds integers)
     const int n0 = __popcll(mvb[0]), nt = n0 + __popcll(mvb[1]);
     if (nt > 0) {
+      const int sl = (blockIdx.x * 4 + w) & (KM_MSLOTS - 1), cap = km_mcap(N);
       int base = 0;
-      if (lane == 0) base = atomicAdd(&mtot[bh], nt);
+      if (lane == 0) base = atomicAdd(&mtot[bh * KM_MSLOTS + sl], nt);
       base = __shfl(base, 0, SV_WAVE);
-      int2* mb = moved + (size_t)bh * N;
+      int2* mb = moved + ((size_t)bh * KM_MSLOTS + sl) * cap;
 #pragma unroll
       for (int t = 0; t < 2; ++t)
         if ((mvb[t] >> lane) & 1) {
@@ -763,6 +772,13 @@ __global__ void __launch_bounds__(256) km_scatter_kernel(const int32_t* __restri
 // inside int64; integer sums are exact, so they do not depend on the order
 // of the additions.  The absolute error of a value is at most 2^(e - 31).
 // --------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t km_r2_bits(const uint32_t* __restrict__ r2max, int bh) {
+  uint32_t b = 0;
+#pragma unroll
+  for (int i = 0; i < KM_MSLOTS; ++i) b = max(b, r2max[bh * KM_MSLOTS + i]);
+  return b;
+}
+
 __device__ __forceinline__ int km_fx_shift(uint32_t r2_bits) {
   const int E = (int)((r2_bits >> 23) & 0xff);
   const int E2 = (E ? E : 1) - 126;  // r2 < 2^E2
@@ -807,7 +823,7 @@ __global__ void __launch_bounds__(256) km_partial_kernel(const T* __restrict__ x
   T* xpb = x_perm ? x_perm + (size_t)bh * N * D : nullptr;
   Acc acc[EPL];
   float mu[EPL];
-  const int fs = FX ? km_fx_shift(r2max[bh]) : 0;
+  const int fs = FX ? km_fx_shift(km_r2_bits(r2max, bh)) : 0;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) {
     acc[e] = 0;
@@ -903,7 +919,7 @@ __global__ void __launch_bounds__(256) km_finalize_kernel(const float* __restric
     for (; k < k1; ++k)
 #pragma unroll
       for (int e = 0; e < 4; ++e) q[e] += pq[(size_t)k * D + e];
-    const int fs = km_fx_shift(r2max[bh]);
+    const int fs = km_fx_shift(km_r2_bits(r2max, bh));
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       fo[e] = q[e];
@@ -967,10 +983,9 @@ __global__ void __launch_bounds__(256) km_delta_kernel(const T* __restrict__ x, 
   __shared__ int s_dc[KD_CL], s_cnt[KD_CL], s_nm;
   const int bh = blockIdx.y, c0 = blockIdx.x * kcl, tid = threadIdx.x;
   if (blockIdx.x == 0 && tid == 0) nmax[bh] = 0u;  // the assign kernel of this round has finished
-  const int2* mb = moved + (size_t)bh * N;
-  // loads that do not depend on the list length go out with it: the owned
-  // clusters' sums and sizes and the first window of the list (the list
-  // buffer holds N entries, so reading past the length stays inside it)
+  const int cap = km_mcap(N);
+  const int2* mb = moved + (size_t)bh * KM_MSLOTS * cap;
+  // the owned clusters' sums and sizes are loaded with the list lengths
   constexpr int FPT = KD_CL * D / 256;  // owned sum entries per thread
   long long fxv[FPT];
 #pragma unroll
@@ -979,32 +994,42 @@ __global__ void __launch_bounds__(256) km_delta_kernel(const T* __restrict__ x, 
     fxv[j] = (i < kcl * D && c < C) ? fx[((size_t)bh * C + c0) * D + i] : 0;
   }
   const int cnt0 = (tid < kcl && c0 + tid < C) ? fxcnt[(size_t)bh * C + c0 + tid] : 0;
-  int2 ev[KD_WIN / 256];
+  // the list is the concatenation of the sub-lists: pre[i] = start of i
+  int pre[KM_MSLOTS];
+  int M = 0;
 #pragma unroll
-  for (int j = 0; j < KD_WIN / 256; ++j) {
-    const int idx = tid + 256 * j;
-    ev[j] = idx < N ? mb[idx] : make_int2(0, -1);
+  for (int i = 0; i < KM_MSLOTS; ++i) {
+    pre[i] = M;
+    M += mtot[bh * KM_MSLOTS + i];
   }
-  const int M = mtot[bh];
   if (M == 0) return;
+  auto entry = [&](int idx) {
+    int sl = 0;
+#pragma unroll
+    for (int i = 1; i < KM_MSLOTS; ++i) sl += idx >= pre[i] ? 1 : 0;
+    int st = pre[0];
+#pragma unroll
+    for (int i = 1; i < KM_MSLOTS; ++i) st = sl == i ? pre[i] : st;
+    return mb[(size_t)sl * cap + (idx - st)];
+  };
   for (int i = tid; i < KD_CL * D; i += 256) acc[i] = 0ull;
   if (tid < KD_CL) s_dc[tid] = 0;
-  const int fs = km_fx_shift(r2max[bh]);
+  const int fs = km_fx_shift(km_r2_bits(r2max, bh));
   const T* xb = x + (size_t)bh * N * D;
   const int g = tid / LPR, e0 = (tid % LPR) * EPL;
   int touched = 0;  // per-thread bit mask of owned clusters seen
   for (int w0 = 0; w0 < M; w0 += KD_WIN) {
     if (tid == 0) s_nm = 0;
     __syncthreads();
-    if (w0 > 0)
-#pragma unroll
-      for (int j = 0; j < KD_WIN / 256; ++j) {
-        const int idx = w0 + tid + 256 * j;
-        ev[j] = idx < M ? mb[idx] : make_int2(0, -1);
-      }
+    int2 ev[KD_WIN / 256];
 #pragma unroll
     for (int j = 0; j < KD_WIN / 256; ++j) {
-      if (w0 + tid + 256 * j >= M || ev[j].y < 0) continue;
+      const int idx = w0 + tid + 256 * j;
+      ev[j] = idx < M ? entry(idx) : make_int2(0, -1);
+    }
+#pragma unroll
+    for (int j = 0; j < KD_WIN / 256; ++j) {
+      if (ev[j].y < 0) continue;
       const int lo = (ev[j].y & 0xffff) - c0, ln = (ev[j].y >> 16) - c0;
       if ((unsigned)ln < (unsigned)kcl) s_m[atomicAdd(&s_nm, 1)] = ev[j].x | (ln << 24);
       if ((unsigned)lo < (unsigned)kcl) s_m[atomicAdd(&s_nm, 1)] = ev[j].x | (lo << 24) | (1 << 27);
@@ -1086,9 +1111,9 @@ static KmPlan km_plan(int B, int H, int N, int D, int C) {
   p.off_pfx = cv.used; cv.take<long long>((size_t)p.BH * p.maxch * D);
   p.off_fx = cv.used; cv.take<long long>((size_t)p.BH * C * D);
   p.off_fxcnt = cv.used; cv.take<int32_t>((size_t)p.BH * C);
-  p.off_moved = cv.used; cv.take<int2>((size_t)p.BH * N);
-  p.off_mtot = cv.used; cv.take<int32_t>(p.BH);
-  p.off_r2max = cv.used; cv.take<uint32_t>(p.BH);
+  p.off_moved = cv.used; cv.take<int2>((size_t)p.BH * KM_MSLOTS * km_mcap(N));
+  p.off_mtot = cv.used; cv.take<int32_t>((size_t)p.BH * KM_MSLOTS);
+  p.off_r2max = cv.used; cv.take<uint32_t>((size_t)p.BH * KM_MSLOTS);
   p.total = cv.used;
   return p;
 }
@@ -1146,7 +1171,8 @@ static svgear_status kmeans_impl(const void* x, int BH, int N, int C, int iters,
   // clusters per delta workgroup: enough workgroups to fill the chip
   const int kcl = std::max(1, std::min(KD_CL, cdiv(C * BH, 2048)));
   hipLaunchKernelGGL(km_clear_kernel, dim3(cdiv(BH, 256)), dim3(256), 0, st, nmax, BH);
-  if (incr) hipLaunchKernelGGL(km_clear_kernel, dim3(cdiv(BH, 256)), dim3(256), 0, st, r2max, BH);
+  if (incr)
+    hipLaunchKernelGGL(km_clear_kernel, dim3(cdiv(BH * KM_MSLOTS, 256)), dim3(256), 0, st, r2max, BH * KM_MSLOTS);
   (void)hipFuncSetAttribute((const void*)km_scatter_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
                             (int)km_scatter_lds(C));
   auto sort_labels = [&]() {  // tile histograms -> offsets -> stable perm
