@@ -27,7 +27,7 @@ constexpr int MEAN_ROWS = 256;      // rows per segment-sum chunk
 constexpr float PAD_NORM = 1e30f;   // squared norm given to padding centroids
 constexpr int KM_PREP_ROWS = 32;    // centroid rows per prep workgroup
 constexpr int KM_FULL_ROUNDS = 3;  // rounds whose update re-sorts every token
-constexpr int KM_MSLOTS = 16;      // per-head counters (and sub-lists) the assign waves spread their atomics over
+constexpr int KM_MSLOTS = 64;      // per-head counters (and sub-lists) the assign waves spread their atomics over
 constexpr int KM_FX_BITS = 30;      // fixed-point values: |x| * 2^s < 2^30 (int32); sums of < 2^24 rows < 2^54
 
 // --------------------------------------------------------------------------
@@ -774,7 +774,6 @@ __global__ void __launch_bounds__(256) km_scatter_kernel(const int32_t* __restri
 // --------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t km_r2_bits(const uint32_t* __restrict__ r2max, int bh) {
   uint32_t b = 0;
-#pragma unroll
   for (int i = 0; i < KM_MSLOTS; ++i) b = max(b, r2max[bh * KM_MSLOTS + i]);
   return b;
 }
@@ -994,23 +993,32 @@ __global__ void __launch_bounds__(256) km_delta_kernel(const T* __restrict__ x, 
     fxv[j] = (i < kcl * D && c < C) ? fx[((size_t)bh * C + c0) * D + i] : 0;
   }
   const int cnt0 = (tid < kcl && c0 + tid < C) ? fxcnt[(size_t)bh * C + c0 + tid] : 0;
-  // the list is the concatenation of the sub-lists: pre[i] = start of i
-  int pre[KM_MSLOTS];
-  int M = 0;
+  // the list is the concatenation of the sub-lists: s_pre[i] = start of
+  // sub-list i, s_pre[KM_MSLOTS] = length (one wave scans the counts)
+  __shared__ int s_pre[KM_MSLOTS + 1];
+  static_assert(KM_MSLOTS == SV_WAVE, "one sub-list count per lane of the first wave");
+  if (tid < SV_WAVE) {
+    const int v = mtot[bh * KM_MSLOTS + tid];
+    int x = v;
 #pragma unroll
-  for (int i = 0; i < KM_MSLOTS; ++i) {
-    pre[i] = M;
-    M += mtot[bh * KM_MSLOTS + i];
+    for (int o = 1; o < SV_WAVE; o <<= 1) {
+      const int y = __shfl_up(x, o, SV_WAVE);
+      if (tid >= o) x += y;
+    }
+    s_pre[tid] = x - v;
+    if (tid == SV_WAVE - 1) s_pre[KM_MSLOTS] = x;
   }
+  __syncthreads();
+  const int M = s_pre[KM_MSLOTS];
   if (M == 0) return;
-  auto entry = [&](int idx) {
-    int sl = 0;
+  auto entry = [&](int idx) {  // last sub-list starting at or before idx
+    int lo = 0, hi = KM_MSLOTS - 1;
 #pragma unroll
-    for (int i = 1; i < KM_MSLOTS; ++i) sl += idx >= pre[i] ? 1 : 0;
-    int st = pre[0];
-#pragma unroll
-    for (int i = 1; i < KM_MSLOTS; ++i) st = sl == i ? pre[i] : st;
-    return mb[(size_t)sl * cap + (idx - st)];
+    for (int k = 0; k < 6; ++k) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (s_pre[mid] <= idx) lo = mid; else hi = mid - 1;
+    }
+    return mb[(size_t)lo * cap + (idx - s_pre[lo])];
   };
   for (int i = tid; i < KD_CL * D; i += 256) acc[i] = 0ull;
   if (tid < KD_CL) s_dc[tid] = 0;
