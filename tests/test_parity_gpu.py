@@ -103,7 +103,7 @@ def test_kmeans_rounds_teacher_forced(sv, name, which):
         Cs = np.stack(nxt)
 
 
-@pytest.mark.parametrize("name", ["bf16-d128", "f32-d64"])
+@pytest.mark.parametrize("name", list(CASES))
 def test_kmeans_multi_round_matches_lloyd(sv, name):
     w, x = make(name)
     X, C0 = x["k"], x["ck0"]
@@ -179,6 +179,35 @@ def test_kmeans_cluster_emptied_in_later_round(sv, dtype, D):
     np.testing.assert_array_equal(host(perm)[0, 0], po)
     np.testing.assert_array_equal(host(off)[0, 0], oo)
     np.testing.assert_allclose(host(cent)[0, 0], Co, rtol=0, atol=1e-5)
+
+
+def test_kmeans_incremental_bookkeeping_max_clusters(sv):
+    """Six rounds at C = 4096 on 8,192 bf16 tokens (clusters of one or two
+    tokens, so many change every round): whatever the tie decisions, after
+    the last round each non-empty cluster's centroid is the mean of the
+    tokens the last assignment gave it, and perm and offsets sort those
+    labels stably.  Means and the sort are recomputed here in fp64 / numpy
+    from the returned labels (a property of the result, not the oracle)."""
+    w = scaled(WORKLOADS["tiny"], B=1, H=1, N=8192, D=64, dtype="bf16", comps=64, zipf=1.1, Cq=4096, Ck=4096,
+               seed=29, density=0.3)
+    x = layer_inputs(w)
+    X, C0 = x["k"][0].astype(np.float64), x["ck0"][0]
+    cent = f32(C0[None, None])
+    lab, perm, off = sv.kmeans(to_dev(x["k"][0][None, None], "bf16"), cent, 6)
+    lab, cent = host(lab)[0, 0], host(cent)[0, 0]
+    assert lab.min() >= 0 and lab.max() < 4096
+    po = np.argsort(lab, kind="stable")
+    oo = np.concatenate([[0], np.cumsum(np.bincount(lab, minlength=4096))])
+    np.testing.assert_array_equal(host(perm)[0, 0], po)
+    np.testing.assert_array_equal(host(off)[0, 0], oo)
+    sums = np.zeros((4096, X.shape[1]))
+    np.add.at(sums, lab, X)
+    n = np.diff(oo)
+    full = n > 0
+    means = sums[full] / n[full, None]
+    err = np.abs(cent[full] - means).max(axis=1)
+    bound = mean_bound(X, po, oo)[full] + 1e-6
+    assert (err <= bound).all(), (err.max(), int((err > bound).sum()))
 
 
 # ------------------------------------------------------------------ centroids
