@@ -158,10 +158,12 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) 
   bf16x8 bxl[2][F32 ? KS : 1];
   bf16x8 bext[2];
   float xx[2];
+  int lold[2];  // previous labels (tracking rounds), loaded with the rows
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int n = tok0 + 32 * t + col;
     const bool ok = n < N;
+    lold[t] = (moved && ok && half == 0) ? labels[(size_t)bh * N + n] : -1;
     float part = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -464,9 +466,9 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) 
     const bool mine = half == 0 && n_mine < N;
     const int lnew = min(lab[t], C - 1);
     if (moved) {
-      const int lold = mine ? labels[(size_t)bh * N + n_mine] : lnew;
-      mvb[t] = ballot(lold != lnew);
-      mv[t] = make_int2(n_mine, lold | (lnew << 16));
+      const int lo = mine ? lold[t] : lnew;
+      mvb[t] = ballot(lo != lnew);
+      mv[t] = make_int2(n_mine, lo | (lnew << 16));
     }
     if (mine) labels[(size_t)bh * N + n_mine] = lnew;
   }
