@@ -138,16 +138,40 @@ def test_kmeans_empty_cluster_keeps_centroid(sv):
         np.testing.assert_array_equal(cent[h][5], C0[h][5])
 
 
-def test_kmeans_singletons_and_single_cluster(sv):
+@pytest.mark.parametrize("iters", [2, 5])
+def test_kmeans_singletons_and_single_cluster(sv, iters):
+    """C = N (every token its own cluster) and C = 1; with 5 rounds the last
+    two run the incremental update with no token moving."""
     w, x = make("f32-d64")
     X = x["k"][:1, :300]
     for C0 in (X.copy(), X[:, :1].copy()):
         C = C0.shape[1]
         cent = f32(C0[:, None])
-        lab, perm, off = sv.kmeans(f32(X[:, None]), cent, 2)
-        Co, lo = orc.lloyd(X[0], C0[0], 2)
+        lab, perm, off = sv.kmeans(f32(X[:, None]), cent, iters)
+        Co, lo = orc.lloyd(X[0], C0[0], iters)
         np.testing.assert_array_equal(host(lab)[0, 0], lo)
         np.testing.assert_allclose(host(cent)[0, 0], Co, rtol=0, atol=1e-5)
+
+
+@pytest.mark.parametrize("N,C", [(70, 3), (129, 5), (5, 2)])
+def test_kmeans_tiny_ragged_many_rounds(sv, N, C):
+    """Token counts that leave partial waves and workgroups, 8 rounds (five
+    incremental), two heads: labels, perm and offsets as the oracle's Lloyd
+    iterates, centroids within the fp32 mean bound."""
+    rng = np.random.default_rng(N * 31 + C)
+    X = np.concatenate([rng.normal(3.0 * k, 1.0, (2, N // C + 1, 64)) for k in range(C)], axis=1)[:, :N]
+    X = X.astype(np.float32)
+    C0 = X[:, :C].copy()
+    cent = f32(C0[None])
+    lab, perm, off = sv.kmeans(f32(X[None]), cent, 8)
+    lab, perm, off, cent = host(lab)[0], host(perm)[0], host(off)[0], host(cent)[0]
+    for h in range(2):
+        Co, lo = orc.lloyd(X[h].astype(np.float64), C0[h].astype(np.float64), 8)
+        np.testing.assert_array_equal(lab[h], lo)
+        po, oo = orc.permute(lo, C)
+        np.testing.assert_array_equal(perm[h], po)
+        np.testing.assert_array_equal(off[h], oo)
+        assert (np.abs(cent[h] - Co).max(axis=1) <= mean_bound(X[h], po, oo) + 1e-6).all()
 
 
 @pytest.mark.parametrize("dtype,D", [("f32", 64), ("bf16", 128)])
