@@ -428,6 +428,9 @@ __global__ void __launch_bounds__(256) attn_kernel(const T* __restrict__ qp, con
 // ---------------------------------------------------------------------------
 constexpr float AT_LAZY = 8.f;
 constexpr int AT_XCDS = 8;  // MI355X: 8 XCDs, each with its own L2
+// Largest one-dimensional grid of the bf16 kernel: 256-thread workgroups, at
+// most 2^32 - 1 threads per launch, a multiple of AT_XCDS.
+constexpr long long AT_MAX_GRID = ((4294967295LL / 256) / AT_XCDS) * AT_XCDS;
 
 typedef __bf16 at_bf16x2 __attribute__((ext_vector_type(2)));
 #define AT_LDS(p) ((__attribute__((address_space(3))) void*)(p))
@@ -438,8 +441,8 @@ typedef __bf16 at_bf16x2 __attribute__((ext_vector_type(2)));
 // counted on the vector-memory counter alone; the global (flat) form would
 // also make every later LDS-read wait a full drain, which defeats reading
 // fragments ahead.  Word 3 = 0x00020000: 32-bit data format, raw access.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t lds_src(const char* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, bytes, 0x00020000);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t lds_src(const char* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
 }
 __device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t src, uint32_t off, char* dst) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(src, AT_LDS(dst), 16, (int)off, 0, 0, 0);
@@ -694,8 +697,9 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
     }
   };
   // a 32-bit per-lane offset from the head's base (4 address bytes per lane)
-  const __amdgpu_buffer_rsrc_t rK = lds_src(kb, N * D * (F8 ? 1 : 2));
-  const __amdgpu_buffer_rsrc_t rV = lds_src(vb, N * D * 2);
+  // byte sizes of one head's rows: below 2^32 for N < 2^24 (checked on the host)
+  const __amdgpu_buffer_rsrc_t rK = lds_src(kb, (uint32_t)N * (uint32_t)D * (F8 ? 1u : 2u));
+  const __amdgpu_buffer_rsrc_t rV = lds_src(vb, (uint32_t)N * (uint32_t)D * 2u);
   auto issue = [&](const uint32_t* rowoff, const uint32_t* rowoff8, char* dK, char* dV) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -910,9 +914,9 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
     }
     constexpr int KROWS = VAR ? 2 : 1;  // K operand rows per cluster
     const __amdgpu_buffer_rsrc_t rPK = lds_src(
-        reinterpret_cast<const char*>(pkx + (size_t)bh * Ck * KROWS * D), Ck * KROWS * D * 2);
+        reinterpret_cast<const char*>(pkx + (size_t)bh * Ck * KROWS * D), (uint32_t)(Ck * KROWS * D * 2));
     const __amdgpu_buffer_rsrc_t rPV =
-        lds_src(reinterpret_cast<const char*>(pvx + (size_t)bh * Ck * D), Ck * D * 2);
+        lds_src(reinterpret_cast<const char*>(pvx + (size_t)bh * Ck * D), (uint32_t)(Ck * D * 2));
     // rows of tile position p: K row KROWS j + part, V row j of skipped
     // cluster PCL pt + p % PCL (part = p / 32 with the variance term)
     auto psources = [&](int ptile, uint32_t* rk, uint32_t* rv) {
@@ -1077,9 +1081,14 @@ static void launch_attn(const void* q, const void* k, const void* v, const int32
 
 using namespace svg;
 
+// Whether one launch of the bf16 kernel can cover every (head, query tile).
+static bool at_grid_fits(const AtPlan& p) { return (long long)p.maxt * p.BH + AT_XCDS <= AT_MAX_GRID; }
+
 extern "C" size_t svgear_sparse_attn_workspace(int B, int H, int N, int D, int Cq, int Ck) {
   if (B < 1 || H < 1 || N < 1 || Cq < 1 || Ck < 1 || (D != 64 && D != 128)) return 0;
-  return at_plan(B, H, N, D, Cq, Ck).total;
+  if ((long long)B * H > 65535 || N >= (1 << 24)) return 0;
+  const AtPlan p = at_plan(B, H, N, D, Cq, Ck);
+  return at_grid_fits(p) ? p.total : 0;
 }
 
 static svgear_status sparse_attn_impl(const void* q_perm, const void* k_perm, const void* v_perm, svgear_dtype dt,
@@ -1099,6 +1108,9 @@ static svgear_status sparse_attn_impl(const void* q_perm, const void* k_perm, co
       !out)
     return fail(SVGEAR_ERR_INVALID_ARG, "attn: null pointer");
   AtPlan p = at_plan(B, H, N, D, Cq, Ck);
+  if (!at_grid_fits(p))
+    return fail(SVGEAR_ERR_INVALID_ARG, "attn: %lld query tiles exceed one launch's grid (B*H=%d, N=%d, Cq=%d)",
+                (long long)p.maxt * p.BH, p.BH, N, Cq);
   st = check_ws("attn", ws, ws_bytes, p.total);
   if (st != SVGEAR_OK) return st;
   int32_t* ts = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + p.off_ts);

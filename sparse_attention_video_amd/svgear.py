@@ -127,10 +127,78 @@ def _stream(dev: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
+_FLOAT = (torch.bfloat16, torch.float32)
+
+
+def _want(name: str, t: Optional[torch.Tensor], dtype, shape=None, optional: bool = True) -> None:
+    """Checks one tensor argument before anything is launched: its dtype (one
+    dtype or a tuple of allowed ones) and its shape (a tuple whose None
+    entries match any size).  Raises ValueError on a mismatch, so that a
+    wrong table can never make a kernel index outside its buffers."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    allowed = dtype if isinstance(dtype, tuple) else (dtype,)
+    if t.dtype not in allowed:
+        raise ValueError(f"{name} must have dtype {' or '.join(str(d) for d in allowed)}, not {t.dtype}")
+    if shape is not None:
+        ok = t.dim() == len(shape) and all(s is None or int(a) == int(s) for a, s in zip(t.shape, shape))
+        if not ok:
+            want = "[" + ", ".join("*" if s is None else str(s) for s in shape) + "]"
+            raise ValueError(f"{name} must have shape {want}, not {list(t.shape)}")
+
+
+def _want_ws(ws: Optional[torch.Tensor]) -> None:
+    _want("ws", ws, torch.uint8, (None,))
+
+
+def _dims4(name: str, t: torch.Tensor, dtype=_FLOAT):
+    _want(name, t, dtype, (None, None, None, None), optional=False)
+    return tuple(int(a) for a in t.shape)
+
+
+def _offsets(name: str, t: torch.Tensor, B: Optional[int] = None, H: Optional[int] = None) -> int:
+    """int32 [B, H, C + 1] offsets; returns C."""
+    _want(name, t, torch.int32, (B, H, None), optional=False)
+    if t.shape[2] < 2:
+        raise ValueError(f"{name} must hold at least one cluster")
+    return int(t.shape[2]) - 1
+
+
 def _workspace(nbytes: int, dev: torch.device) -> torch.Tensor:
     ws = torch.empty(max(int(nbytes), 1) + 256, dtype=torch.uint8, device=dev)
     off = (-ws.data_ptr()) % 256
     return ws[off:off + max(int(nbytes), 1)]
+
+
+def _route_tables(B, H, Cq, Ck, q_means, k_perm, v_perm, k_means, v_means, needs_probe: bool, D=None) -> None:
+    """Shapes and dtypes of the routing inputs that are given (all of them
+    when the probe runs)."""
+    if k_perm is not None:
+        _, _, N, D = _dims4("k_perm", k_perm)
+        _want("k_perm", k_perm, _FLOAT, (B, H, N, D))
+        _want("v_perm", v_perm, k_perm.dtype, (B, H, N, D), optional=not needs_probe)
+    elif needs_probe:
+        raise ValueError("k_perm is required")
+    _want("q_means", q_means, torch.float32, (B, H, Cq, D), optional=not needs_probe)
+    _want("k_means", k_means, torch.float32, (B, H, Ck, D), optional=not needs_probe)
+    _want("v_means", v_means, torch.float32, (B, H, Ck, D), optional=not needs_probe)
+
+
+def _attn_tables(B, H, N, D, q_perm_idx, q_offsets, k_offsets, k_means, v_means, mask, out, out_dtype, lse):
+    """Shapes and dtypes of the attention inputs besides Q', K', V'; returns (Cq, Ck)."""
+    _want("q_perm_idx", q_perm_idx, torch.int32, (B, H, N), optional=False)
+    Cq = _offsets("q_offsets", q_offsets, B, H)
+    Ck = _offsets("k_offsets", k_offsets, B, H)
+    _want("k_means", k_means, torch.float32, (B, H, Ck, D), optional=False)
+    _want("v_means", v_means, torch.float32, (B, H, Ck, D), optional=False)
+    _want("mask", mask, torch.uint8, (B, H, Cq, Ck), optional=False)
+    _want("out", out, out_dtype, (B, H, N, D))
+    _want("lse", lse, torch.float32, (B, H, N))
+    return Cq, Ck
 
 
 # ----------------------------------------------------------------------------
@@ -138,11 +206,14 @@ def kmeans(x: torch.Tensor, centroids: torch.Tensor, iters: int, labels=None, pe
     """Lloyd k-means; ``centroids`` [B,H,C,D] fp32 is updated in place.
 
     Returns (labels [B,H,N] int32, perm [B,H,N] int32, offsets [B,H,C+1] int32)."""
-    dev = _dev(x, centroids)
-    B, H, N, D = x.shape
-    C = centroids.shape[2]
-    if centroids.dtype != torch.float32 or tuple(centroids.shape) != (B, H, C, D):
-        raise ValueError("centroids must be float32 [B,H,C,D]")
+    B, H, N, D = _dims4("x", x)
+    _want("centroids", centroids, torch.float32, (B, H, None, D), optional=False)
+    C = int(centroids.shape[2])
+    _want("labels", labels, torch.int32, (B, H, N))
+    _want("perm", perm, torch.int32, (B, H, N))
+    _want("offsets", offsets, torch.int32, (B, H, C + 1))
+    _want_ws(ws)
+    dev = _dev(x, centroids, labels, perm, offsets, ws)
     labels = labels if labels is not None else torch.empty((B, H, N), dtype=torch.int32, device=dev)
     perm = perm if perm is not None else torch.empty((B, H, N), dtype=torch.int32, device=dev)
     offsets = offsets if offsets is not None else torch.empty((B, H, C + 1), dtype=torch.int32, device=dev)
@@ -158,9 +229,13 @@ def kmeans(x: torch.Tensor, centroids: torch.Tensor, iters: int, labels=None, pe
 def centroids(x: torch.Tensor, perm: torch.Tensor, offsets: torch.Tensor, want_perm: bool = True,
               want_means: bool = True, x_perm=None, means=None, ws=None):
     """Returns (x_perm [B,H,N,D] or None, means [B,H,C,D] fp32 or None)."""
-    dev = _dev(x, perm, offsets)
-    B, H, N, D = x.shape
-    C = offsets.shape[2] - 1
+    B, H, N, D = _dims4("x", x)
+    _want("perm", perm, torch.int32, (B, H, N), optional=False)
+    C = _offsets("offsets", offsets, B, H)
+    _want("x_perm", x_perm, x.dtype, (B, H, N, D))
+    _want("means", means, torch.float32, (B, H, C, D))
+    _want_ws(ws)
+    dev = _dev(x, perm, offsets, x_perm, means, ws)
     if want_perm and x_perm is None:
         x_perm = torch.empty_like(x)
     if want_means and means is None:
@@ -178,9 +253,15 @@ def centroids(x: torch.Tensor, perm: torch.Tensor, offsets: torch.Tensor, want_p
 def route(q_means, q_offsets, k_perm, v_perm, k_means, v_means, k_offsets, scale: float, density: float,
           scores_in: Optional[torch.Tensor] = None, want_scores: bool = True, mask=None, scores=None, ws=None):
     """Returns (scores [B,H,Cq,Ck] fp32 or None, mask [B,H,Cq,Ck] uint8)."""
-    dev = _dev(q_offsets, k_offsets)
-    B, H, Cq1 = q_offsets.shape
-    Cq, Ck = Cq1 - 1, k_offsets.shape[2] - 1
+    Cq = _offsets("q_offsets", q_offsets)
+    B, H = int(q_offsets.shape[0]), int(q_offsets.shape[1])
+    Ck = _offsets("k_offsets", k_offsets, B, H)
+    _route_tables(B, H, Cq, Ck, q_means, k_perm, v_perm, k_means, v_means, needs_probe=scores_in is None)
+    for name, t in (("scores_in", scores_in), ("scores", scores)):
+        _want(name, t, torch.float32, (B, H, Cq, Ck))
+    _want("mask", mask, torch.uint8, (B, H, Cq, Ck))
+    _want_ws(ws)
+    dev = _dev(q_offsets, k_offsets, mask, scores, ws)
     if scores_in is None:
         _dev(q_means, k_perm, v_perm, k_means, v_means)
         N, D = k_perm.shape[2], k_perm.shape[3]
@@ -210,10 +291,12 @@ def kmeanspp(x: torch.Tensor, words: torch.Tensor, C: int, centroids=None, chose
     """k-means++ seeds from one uniform 64-bit word per seed (words: [B,H,C]
     int64 or uint64 tensor, bits taken as unsigned).  Returns (centroids
     [B,H,C,D] fp32, chosen [B,H,C] int32)."""
-    dev = _dev(x, words)
-    B, H, N, D = x.shape
-    if tuple(words.shape) != (B, H, C) or words.element_size() != 8 or not words.is_contiguous():
-        raise ValueError("words must be a contiguous [B, H, C] tensor of 64-bit integers")
+    B, H, N, D = _dims4("x", x)
+    _want("words", words, (torch.int64, torch.uint64), (B, H, C), optional=False)
+    _want("centroids", centroids, torch.float32, (B, H, C, D))
+    _want("chosen", chosen, torch.int32, (B, H, C))
+    _want_ws(ws)
+    dev = _dev(x, words, centroids, chosen, ws)
     centroids = centroids if centroids is not None else torch.empty((B, H, C, D), dtype=torch.float32, device=dev)
     chosen = chosen if chosen is not None else torch.empty((B, H, C), dtype=torch.int32, device=dev)
     lib = load()
@@ -226,8 +309,11 @@ def kmeanspp(x: torch.Tensor, words: torch.Tensor, C: int, centroids=None, chose
 
 def quantize_fp8(x: torch.Tensor, x8=None, exps=None, ws=None):
     """e4m3fn codes [B,H,N,D] uint8 and per-(batch, head) exponents [B,H] int32."""
-    dev = _dev(x)
-    B, H, N, D = x.shape
+    B, H, N, D = _dims4("x", x)
+    _want("x8", x8, torch.uint8, (B, H, N, D))
+    _want("exps", exps, torch.int32, (B, H))
+    _want_ws(ws)
+    dev = _dev(x, x8, exps, ws)
     x8 = x8 if x8 is not None else torch.empty((B, H, N, D), dtype=torch.uint8, device=dev)
     exps = exps if exps is not None else torch.empty((B, H), dtype=torch.int32, device=dev)
     lib = load()
@@ -241,13 +327,15 @@ def quantize_fp8(x: torch.Tensor, x8=None, exps=None, ws=None):
 def sparse_attn_fp8(q8, q_exp, k8, k_exp, v_perm, q_perm_idx, q_offsets, k_offsets, k_means, v_means, mask,
                     scale: float, want_lse: bool = False, out=None, lse=None, ws=None):
     """FP8 variant: e4m3 Q'/K' (from quantize_fp8), bf16 V'.  Returns (out, lse or None)."""
-    dev = _dev(q8, q_exp, k8, k_exp, v_perm, q_perm_idx, q_offsets, k_offsets, k_means, v_means, mask)
-    B, H, N, D = v_perm.shape
-    Cq, Ck = q_offsets.shape[2] - 1, k_offsets.shape[2] - 1
-    if q8.dtype != torch.uint8 or k8.dtype != torch.uint8 or tuple(q8.shape) != (B, H, N, D):
-        raise ValueError("q8 and k8 must be uint8 [B, H, N, D] e4m3 codes")
-    if v_perm.dtype != torch.bfloat16:
-        raise ValueError("the FP8 variant takes bf16 values")
+    B, H, N, D = _dims4("v_perm", v_perm, torch.bfloat16)
+    _want("q8", q8, torch.uint8, (B, H, N, D), optional=False)
+    _want("k8", k8, torch.uint8, (B, H, N, D), optional=False)
+    _want("q_exp", q_exp, torch.int32, (B, H), optional=False)
+    _want("k_exp", k_exp, torch.int32, (B, H), optional=False)
+    Cq, Ck = _attn_tables(B, H, N, D, q_perm_idx, q_offsets, k_offsets, k_means, v_means, mask, out,
+                          torch.bfloat16, lse)
+    _want_ws(ws)
+    dev = _dev(q8, q_exp, k8, k_exp, v_perm, q_perm_idx, q_offsets, k_offsets, k_means, v_means, mask, out, lse, ws)
     out = out if out is not None else torch.empty_like(v_perm)
     if want_lse and lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
@@ -269,9 +357,15 @@ def route_topp(q_means, q_offsets, k_perm, v_perm, k_means, v_means, k_offsets, 
     """Routing under the SVG2 top-p budget.  Returns (probs [B,H,Cq,Ck] fp32 or
     None, scores [B,H,Cq,Ck] fp32 or None, budget [B,H,Cq] int32 or None,
     mask [B,H,Cq,Ck] uint8).  N and D default to k_perm's shape."""
-    dev = _dev(q_offsets, k_offsets)
-    B, H, Cq1 = q_offsets.shape
-    Cq, Ck = Cq1 - 1, k_offsets.shape[2] - 1
+    Cq = _offsets("q_offsets", q_offsets)
+    B, H = int(q_offsets.shape[0]), int(q_offsets.shape[1])
+    Ck = _offsets("k_offsets", k_offsets, B, H)
+    _route_tables(B, H, Cq, Ck, q_means, k_perm, v_perm, k_means, v_means,
+                  needs_probe=bool(error_ranked) and scores_in is None, D=D)
+    for name, t in (("probs_in", probs_in), ("scores_in", scores_in)):
+        _want(name, t, torch.float32, (B, H, Cq, Ck))
+    _want_ws(ws)
+    dev = _dev(q_offsets, k_offsets, ws)
     if k_perm is not None:
         _dev(k_perm)
         N, D, dt = int(k_perm.shape[2]), int(k_perm.shape[3]), _dtype(k_perm)
@@ -301,9 +395,13 @@ def route_topp(q_means, q_offsets, k_perm, v_perm, k_means, v_means, k_offsets, 
 def centroid_variances(x: torch.Tensor, perm: torch.Tensor, offsets: torch.Tensor, means: torch.Tensor, vars=None,
                        ws=None):
     """Per-cluster, per-coordinate population variances [B,H,C,D] fp32."""
-    dev = _dev(x, perm, offsets, means)
-    B, H, N, D = x.shape
-    C = offsets.shape[2] - 1
+    B, H, N, D = _dims4("x", x)
+    _want("perm", perm, torch.int32, (B, H, N), optional=False)
+    C = _offsets("offsets", offsets, B, H)
+    _want("means", means, torch.float32, (B, H, C, D), optional=False)
+    _want("vars", vars, torch.float32, (B, H, C, D))
+    _want_ws(ws)
+    dev = _dev(x, perm, offsets, means, vars, ws)
     vars = vars if vars is not None else torch.empty((B, H, C, D), dtype=torch.float32, device=dev)
     lib = load()
     need = lib.svgear_centroids_workspace(B, H, N, D, C)
@@ -319,9 +417,14 @@ def sparse_attn(q_perm, k_perm, v_perm, q_perm_idx, q_offsets, k_offsets, k_mean
     """Returns (out [B,H,N,D] in original token order, lse [B,H,N] fp32 or None).
     With ``k_vars`` the skipped clusters' scores gain strength * sigma^2 / 2
     (variance-corrected compensation, bf16 only)."""
-    dev = _dev(q_perm, k_perm, v_perm, q_perm_idx, q_offsets, k_offsets, k_means, v_means, mask)
-    B, H, N, D = q_perm.shape
-    Cq, Ck = q_offsets.shape[2] - 1, k_offsets.shape[2] - 1
+    B, H, N, D = _dims4("q_perm", q_perm)
+    _want("k_perm", k_perm, q_perm.dtype, (B, H, N, D), optional=False)
+    _want("v_perm", v_perm, q_perm.dtype, (B, H, N, D), optional=False)
+    Cq, Ck = _attn_tables(B, H, N, D, q_perm_idx, q_offsets, k_offsets, k_means, v_means, mask, out, q_perm.dtype,
+                          lse)
+    _want("k_vars", k_vars, torch.float32, (B, H, Ck, D))
+    _want_ws(ws)
+    dev = _dev(q_perm, k_perm, v_perm, q_perm_idx, q_offsets, k_offsets, k_means, v_means, mask, out, lse, k_vars, ws)
     out = out if out is not None else torch.empty_like(q_perm)
     if want_lse and lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)

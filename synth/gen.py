@@ -125,25 +125,42 @@ class HeadDraw:
         self.init_k = r.choice(N, size=w.Ck, replace=False)
         self.bh = bh
 
+    def drift_increments(self, s: int):
+        """The float32 increments of the Q, K, V component means at step s >= 1
+        (drift times a standard normal draw from default_rng([seed, h, s]))."""
+        rs = np.random.default_rng([self.w.seed, self.bh, s])
+        shp = self.mq.shape
+        dq = self.w.drift * rs.standard_normal(shp, dtype=np.float32)
+        dk = self.w.drift * rs.standard_normal(shp, dtype=np.float32)
+        dv = self.w.drift * rs.standard_normal(shp, dtype=np.float32)
+        return dq, dk, dv
+
     def means_at(self, step: int):
         mq, mk, mv = self.mq, self.mk, self.mv
         if step > 0 and self.w.drift > 0:
             mq, mk, mv = mq.copy(), mk.copy(), mv.copy()
             for s in range(1, step + 1):
-                rs = np.random.default_rng([self.w.seed, self.bh, s])
-                mq += self.w.drift * rs.standard_normal(mq.shape, dtype=np.float32)
-                mk += self.w.drift * rs.standard_normal(mk.shape, dtype=np.float32)
-                mv += self.w.drift * rs.standard_normal(mv.shape, dtype=np.float32)
+                dq, dk, dv = self.drift_increments(s)
+                mq += dq
+                mk += dk
+                mv += dv
         return mq, mk, mv
+
+    def noise(self):
+        """The per-token float32 offsets from the component means, sigma * eps
+        for Q, K and V: a token is (its component's mean) + (its offset),
+        added in float32 and then cast to the workload dtype."""
+        sa = self.sig[self.a][:, None]
+        sb = self.sig[self.b][:, None]
+        return sa * self.eq, sb * self.ek, sb * self.ev
 
     def tensors(self, step: int = 0):
         """q, k, v (float32 arrays holding the values of the workload dtype)."""
         mq, mk, mv = self.means_at(step)
-        sa = self.sig[self.a][:, None]
-        sb = self.sig[self.b][:, None]
-        q = _cast(self.w, mq[self.a] + sa * self.eq)
-        k = _cast(self.w, mk[self.b] + sb * self.ek)
-        v = _cast(self.w, mv[self.b] + sb * self.ev)
+        nq, nk, nv = self.noise()
+        q = _cast(self.w, mq[self.a] + nq)
+        k = _cast(self.w, mk[self.b] + nk)
+        v = _cast(self.w, mv[self.b] + nv)
         return q, k, v
 
 

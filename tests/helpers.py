@@ -109,3 +109,42 @@ def check_ratio_masks(mask_gpu, r_o, mask_o, rows=None, rel=4e-3):
         n += diff.size
         assert np.all(np.abs(r_o[i][diff] - thr) <= rel * thr + 1e-7 * rowmax[i]), (i, diff)
     return n
+
+
+def first_divergence(gpu_labels_after, X, C0, iters, rel=1e-5):
+    """Lloyd iterations amplify a near tie (a token whose two nearest
+    centroids agree to float32 rounding) into later label changes, so several
+    final label sets are correct.  This finds the first round r whose GPU
+    labels (``gpu_labels_after(r)``: the head's labels after r rounds from C0)
+    differ from the oracle's Lloyd iterate and asserts that there they differ
+    only at near ties for the oracle's centroids of round r - 1.  Returns
+    (r, number of differing labels), or (None, 0) if no round differs."""
+    X = np.asarray(X, np.float64)
+    C = np.asarray(C0, np.float64)
+    for r in range(1, iters + 1):
+        lab_o = orc.assign(X, C)
+        lab_g = np.asarray(gpu_labels_after(r))
+        if (lab_g != lab_o).any():
+            return r, check_labels_near_ties(X, C, lab_g, lab_o, rel)
+        C = orc.update(X, lab_o, C)
+    return None, 0
+
+
+def oracle_from_labels(q, k, v, lq, lk, Cq, Ck, scale, density):
+    """The oracle's permutation, means, routing ratios and mask for given final
+    k-means labels (the GPU's own, once they have been shown valid): every
+    stage after the clustering, so that a layer whose labels legitimately
+    differ from the oracle's Lloyd iterates is still checked end to end."""
+    N = q.shape[0]
+    out = {}
+    out["pq"], out["oq"] = orc.permute(np.asarray(lq, np.int64), Cq)
+    out["pk"], out["ok"] = orc.permute(np.asarray(lk, np.int64), Ck)
+    out["qbar"] = orc.means(q, out["pq"], out["oq"])
+    out["kbar"] = orc.means(k, out["pk"], out["ok"])
+    out["vbar"] = orc.means(v, out["pk"], out["ok"])
+    qs, ks = np.diff(out["oq"]), np.diff(out["ok"])
+    Kp, Vp = np.asarray(k)[out["pk"]], np.asarray(v)[out["pk"]]
+    e, _ = orc.probe_errors(out["qbar"], Kp, Vp, out["kbar"], out["vbar"], out["ok"], scale, q_nonempty=qs > 0)
+    out["ratio"] = orc.ratios(e, qs, ks)
+    out["mask"] = orc.select(out["ratio"], qs, ks, density, N)
+    return out

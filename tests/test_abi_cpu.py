@@ -143,3 +143,101 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros((1, 1, 64, 64))
     with pytest.raises(ValueError):
         svgear.kmeans(x, torch.zeros((1, 1, 4, 64)), 1)
+
+
+def test_attn_grid_limit_at_the_size_boundary(lib):
+    """The largest token count the library takes (N = 2^24 - 1) still passes
+    validation for one head (its row bytes fit the 32-bit buffer range); a
+    grid of query tiles larger than one launch is refused before any launch,
+    and its workspace query reports 0."""
+    F = FAKE
+    N = (1 << 24) - 1
+    A = lambda B, H, Cq: lib.svgear_sparse_attn(F, F, F, 0, F, F, Cq, F, 8, F, F, F, B, H, N, 128,
+                                                ctypes.c_float(0.125), F, None, None, 0, None)
+    assert A(1, 1, 4) == 3                   # valid sizes; only the workspace is missing
+    assert lib.svgear_sparse_attn_workspace(1, 1, N, 128, 4, 8) > 0
+    assert A(1, 65535, 4096) == 1            # 135,168 tiles per head x 65,535 heads
+    assert "grid" in lib.svgear_last_error().decode()
+    assert lib.svgear_sparse_attn_workspace(1, 65535, N, 128, 4096, 8) == 0
+    assert A(1, 1, 4) == 3
+
+
+def _cpu_case(B=1, H=2, N=64, D=64, Cq=4, Ck=8):
+    import torch
+    z = lambda *s, dt=torch.float32: torch.zeros(s, dtype=dt)
+    i = torch.int32
+    return dict(q=z(B, H, N, D), k=z(B, H, N, D), v=z(B, H, N, D), idx=z(B, H, N, dt=i), oq=z(B, H, Cq + 1, dt=i),
+                ok=z(B, H, Ck + 1, dt=i), km=z(B, H, Ck, D), vm=z(B, H, Ck, D), qm=z(B, H, Cq, D),
+                mask=z(B, H, Cq, Ck, dt=torch.uint8))
+
+
+@pytest.mark.parametrize("bad", [
+    dict(oq="int64"), dict(ok="int64"), dict(idx="int64"), dict(mask="bool"), dict(km="float64"),
+    dict(k="bfloat16"), dict(mask_shape=(1, 2, 3, 8)), dict(ok_shape=(1, 1, 9)), dict(vm_shape=(1, 2, 7, 64)),
+    dict(out="float64"), dict(lse_shape=(1, 2, 63)),
+])
+def test_binding_validates_attention_tables(bad):
+    """Every table's dtype and shape is checked before anything reaches the
+    library (int64 offsets, a wrongly shaped mask, ...), so a wrong table can
+    never make a kernel index outside its buffers.  CPU tensors: the checks
+    run before the device check."""
+    import torch
+    from sparse_attention_video_amd import svgear
+    a = _cpu_case()
+    kw = {}
+    for key, val in bad.items():
+        if key.endswith("_shape"):
+            name = key[:-6]
+            src = a.get(name)
+            shape = val
+            dt = src.dtype if src is not None else torch.float32
+            a[name] = torch.zeros(shape, dtype=dt)
+        elif key in ("out", "lse"):
+            kw[key] = torch.zeros(a["q"].shape, dtype=getattr(torch, val))
+        else:
+            a[key] = a[key].to(getattr(torch, val))
+    if "lse" in a:
+        kw["lse"] = a.pop("lse")
+        kw["want_lse"] = True
+    with pytest.raises(ValueError):
+        svgear.sparse_attn(a["q"], a["k"], a["v"], a["idx"], a["oq"], a["ok"], a["km"], a["vm"], a["mask"], 0.125,
+                           **kw)
+
+
+def test_binding_validates_other_calls():
+    import torch
+    from sparse_attention_video_amd import svgear
+    a = _cpu_case()
+    i32, f32 = torch.int32, torch.float32
+    with pytest.raises(ValueError, match="centroids"):
+        svgear.kmeans(a["k"], torch.zeros((1, 2, 8, 32)), 1)                 # D mismatch
+    with pytest.raises(ValueError, match="offsets"):
+        svgear.kmeans(a["k"], a["km"], 1, offsets=torch.zeros((1, 2, 8), dtype=i32))
+    with pytest.raises(ValueError, match="perm"):
+        svgear.centroids(a["k"], a["idx"].long(), a["ok"])
+    with pytest.raises(ValueError, match="means"):
+        svgear.centroids(a["k"], a["idx"], a["ok"], means=torch.zeros((1, 2, 9, 64)))
+    with pytest.raises(ValueError, match="mask"):
+        svgear.route(a["qm"], a["oq"], a["k"], a["v"], a["km"], a["vm"], a["ok"], 0.125, 0.25,
+                     mask=torch.zeros((1, 2, 4, 8), dtype=torch.int32))
+    with pytest.raises(ValueError, match="v_perm"):
+        svgear.route(a["qm"], a["oq"], a["k"], a["v"].bfloat16(), a["km"], a["vm"], a["ok"], 0.125, 0.25)
+    with pytest.raises(ValueError, match="scores_in"):
+        svgear.route(None, a["oq"], a["k"], None, None, None, a["ok"], 0.125, 0.25,
+                     scores_in=torch.zeros((1, 2, 8, 4)))
+    with pytest.raises(ValueError, match="probs_in"):
+        svgear.route_topp(a["qm"], a["oq"], a["k"], a["v"], a["km"], a["vm"], a["ok"], 0.125, 0.9,
+                          probs_in=torch.zeros((1, 2, 4, 8), dtype=torch.float64))
+    with pytest.raises(ValueError, match="words"):
+        svgear.kmeanspp(a["k"], torch.zeros((1, 2, 4), dtype=i32), 4)
+    with pytest.raises(ValueError, match="exps"):
+        svgear.quantize_fp8(a["k"], exps=torch.zeros((1, 2), dtype=torch.int64))
+    with pytest.raises(ValueError, match="k8"):
+        svgear.sparse_attn_fp8(torch.zeros((1, 2, 64, 64), dtype=torch.uint8), torch.zeros((1, 2), dtype=i32),
+                               torch.zeros((1, 2, 64, 64)), torch.zeros((1, 2), dtype=i32), a["v"].bfloat16(),
+                               a["idx"], a["oq"], a["ok"], a["km"], a["vm"], a["mask"], 0.125)
+    with pytest.raises(ValueError, match="vars"):
+        svgear.centroid_variances(a["k"], a["idx"], a["ok"], a["km"], vars=torch.zeros((1, 2, 8, 64), dtype=f32)[..., :32])
+    with pytest.raises(ValueError, match="ws"):
+        svgear.sparse_attn(a["q"], a["k"], a["v"], a["idx"], a["oq"], a["ok"], a["km"], a["vm"], a["mask"], 0.125,
+                           ws=torch.zeros(16, dtype=f32))
