@@ -21,7 +21,9 @@
  *     the caller, and must stay valid until the work queued on `stream`
  *     finishes.  The library never allocates, frees or retains memory; the
  *     scratch it needs is the caller's `ws` buffer of at least the size the
- *     matching *_workspace() query returns (256-byte aligned).
+ *     matching *_workspace() query returns (256-byte aligned).  The one
+ *     exception is svgear_sparse_attn_noalloc, whose scratch is a static
+ *     device array of the library (below).
  *   - Every call is asynchronous on `stream` and never synchronises.  Calls
  *     that share a workspace or outputs must be ordered on one stream.
  *   - Arguments are validated before anything is queued.  On any non-OK
@@ -285,6 +287,28 @@ svgear_status svgear_sparse_attn(const void* q_perm, const void* k_perm, const v
                                  const uint8_t* mask, int B, int H, int N, int D, float scale,
                                  void* out, float* lse, void* ws, size_t ws_bytes,
                                  hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * svgear_sparse_attn_noalloc -- svgear_sparse_attn for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): same arguments, results and errors,
+ * minus the workspace.  Its scratch (the tile list and the bf16 pseudo-key
+ * rows, svgear_sparse_attn_workspace(...) bytes) is a static device array of
+ * SVGEAR_NOALLOC_SCRATCH_BYTES that each GPU holds until the process ends;
+ * the call allocates and frees nothing.  Sizes whose workspace exceeds that
+ * limit return SVGEAR_ERR_INVALID_ARG before anything is queued.  Every call
+ * on one GPU shares that GPU's array (the GPU is the stream's device, or the
+ * current device for the null stream), so calls that overlap on one GPU race:
+ * order them on one stream.  The first call on a device looks up the array's
+ * device address (hipGetSymbolAddress) with that device current.
+ * ---------------------------------------------------------------------- */
+#define SVGEAR_NOALLOC_SCRATCH_BYTES (32u << 20)
+svgear_status svgear_sparse_attn_noalloc(const void* q_perm, const void* k_perm, const void* v_perm,
+                                         svgear_dtype dt, const int32_t* q_perm_idx,
+                                         const int32_t* q_offsets, int Cq, const int32_t* k_offsets,
+                                         int Ck, const float* k_means, const float* v_means,
+                                         const uint8_t* mask, int B, int H, int N, int D, float scale,
+                                         void* out, float* lse, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Variance-corrected compensation (a variant; FrontierCS blog on SVG-EAR,

@@ -21,6 +21,7 @@
 // throughout.
 #include <float.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "common.h"
@@ -1091,13 +1092,13 @@ extern "C" size_t svgear_sparse_attn_workspace(int B, int H, int N, int D, int C
   return at_grid_fits(p) ? p.total : 0;
 }
 
-static svgear_status sparse_attn_impl(const void* q_perm, const void* k_perm, const void* v_perm, svgear_dtype dt,
-                                      const int32_t* q_perm_idx, const int32_t* q_offsets, int Cq,
-                                      const int32_t* k_offsets, int Ck, const float* k_means, const float* v_means,
-                                      const float* k_vars, float strength, const uint8_t* mask, int B, int H, int N,
-                                      int D, float scale, void* out, float* lse, void* ws, size_t ws_bytes,
-                                      hipStream_t stream, const int32_t* q_exp = nullptr,
-                                      const int32_t* k_exp = nullptr) {
+// Every argument check of the attention calls (before anything is queued);
+// fills the launch plan.
+static svgear_status attn_check_args(const void* q_perm, const void* k_perm, const void* v_perm, svgear_dtype dt,
+                                     const int32_t* q_perm_idx, const int32_t* q_offsets, int Cq,
+                                     const int32_t* k_offsets, int Ck, const float* k_means, const float* v_means,
+                                     const uint8_t* mask, int B, int H, int N, int D, float scale, void* out,
+                                     AtPlan* plan) {
   svgear_status st = check_common("attn", dt, B, H, N, D);
   if (st != SVGEAR_OK) return st;
   if (Cq < 1 || Cq > N || Cq > SVGEAR_MAX_CLUSTERS || Ck < 1 || Ck > N || Ck > SVGEAR_MAX_CLUSTERS)
@@ -1107,10 +1108,24 @@ static svgear_status sparse_attn_impl(const void* q_perm, const void* k_perm, co
   if (!q_perm || !k_perm || !v_perm || !q_perm_idx || !q_offsets || !k_offsets || !k_means || !v_means || !mask ||
       !out)
     return fail(SVGEAR_ERR_INVALID_ARG, "attn: null pointer");
-  AtPlan p = at_plan(B, H, N, D, Cq, Ck);
-  if (!at_grid_fits(p))
+  *plan = at_plan(B, H, N, D, Cq, Ck);
+  if (!at_grid_fits(*plan))
     return fail(SVGEAR_ERR_INVALID_ARG, "attn: %lld query tiles exceed one launch's grid (B*H=%d, N=%d, Cq=%d)",
-                (long long)p.maxt * p.BH, p.BH, N, Cq);
+                (long long)plan->maxt * plan->BH, plan->BH, N, Cq);
+  return SVGEAR_OK;
+}
+
+static svgear_status sparse_attn_impl(const void* q_perm, const void* k_perm, const void* v_perm, svgear_dtype dt,
+                                      const int32_t* q_perm_idx, const int32_t* q_offsets, int Cq,
+                                      const int32_t* k_offsets, int Ck, const float* k_means, const float* v_means,
+                                      const float* k_vars, float strength, const uint8_t* mask, int B, int H, int N,
+                                      int D, float scale, void* out, float* lse, void* ws, size_t ws_bytes,
+                                      hipStream_t stream, const int32_t* q_exp = nullptr,
+                                      const int32_t* k_exp = nullptr) {
+  AtPlan p;
+  svgear_status st = attn_check_args(q_perm, k_perm, v_perm, dt, q_perm_idx, q_offsets, Cq, k_offsets, Ck, k_means,
+                                     v_means, mask, B, H, N, D, scale, out, &p);
+  if (st != SVGEAR_OK) return st;
   st = check_ws("attn", ws, ws_bytes, p.total);
   if (st != SVGEAR_OK) return st;
   int32_t* ts = reinterpret_cast<int32_t*>(static_cast<char*>(ws) + p.off_ts);
@@ -1178,4 +1193,71 @@ extern "C" svgear_status svgear_sparse_attn_fp8(const uint8_t* q8, const int32_t
   if (!q_exp || !k_exp) return fail(SVGEAR_ERR_INVALID_ARG, "attn_fp8: null pointer");
   return sparse_attn_impl(q8, k8, v_perm, SVGEAR_BF16, q_perm_idx, q_offsets, Cq, k_offsets, Ck, k_means, v_means,
                           nullptr, 0.f, mask, B, H, N, D, scale, out, lse, ws, ws_bytes, stream, q_exp, k_exp);
+}
+
+// ---------------------------------------------------------------- allocation-free variant
+// Scratch of svgear_sparse_attn_noalloc: the tile list and the bf16
+// pseudo-key rows of one call, in a static device array instead of a caller
+// workspace.  Each GPU the library runs on holds its own copy until the
+// process ends; every call on that GPU reuses it (nothing in it needs to
+// start at zero: each call writes all it reads), so calls that overlap on one
+// GPU race.
+static __device__ __attribute__((aligned(256))) unsigned char scratch[SVGEAR_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int AT_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[AT_MAX_DEVICES] = {};
+}  // namespace
+
+// The device address of this GPU's copy of the scratch array.  In host code
+// the array's name is only a stand-in, so the address is looked up once per
+// device, with that device current, and kept.
+static svgear_status noalloc_scratch(hipStream_t stream, void** out) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return fail(SVGEAR_ERR_HIP, "attn_noalloc: hipGetDevice: %s", hipGetErrorString(e));
+  int dev = cur;
+  if (stream != nullptr) {
+    e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return fail(SVGEAR_ERR_HIP, "attn_noalloc: hipStreamGetDevice: %s", hipGetErrorString(e));
+  }
+  if (dev < 0 || dev >= AT_MAX_DEVICES)
+    return fail(SVGEAR_ERR_UNSUPPORTED, "attn_noalloc: device %d beyond the %d this build tracks", dev, AT_MAX_DEVICES);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess)
+      return fail(SVGEAR_ERR_HIP, "attn_noalloc: hipSetDevice(%d): %s", dev, hipGetErrorString(e));
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess || p == nullptr)
+      return fail(SVGEAR_ERR_HIP, "attn_noalloc: hipGetSymbolAddress: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SVGEAR_OK;
+}
+
+extern "C" svgear_status svgear_sparse_attn_noalloc(const void* q_perm, const void* k_perm, const void* v_perm,
+                                                    svgear_dtype dt, const int32_t* q_perm_idx,
+                                                    const int32_t* q_offsets, int Cq, const int32_t* k_offsets,
+                                                    int Ck, const float* k_means, const float* v_means,
+                                                    const uint8_t* mask, int B, int H, int N, int D, float scale,
+                                                    void* out, float* lse, hipStream_t stream) {
+  AtPlan p;
+  svgear_status st = attn_check_args(q_perm, k_perm, v_perm, dt, q_perm_idx, q_offsets, Cq, k_offsets, Ck, k_means,
+                                     v_means, mask, B, H, N, D, scale, out, &p);
+  if (st != SVGEAR_OK) return st;
+  if (p.total > (size_t)SVGEAR_NOALLOC_SCRATCH_BYTES)
+    return fail(SVGEAR_ERR_INVALID_ARG,
+                "attn_noalloc: these sizes need %zu bytes of scratch, more than the library's %zu (use "
+                "svgear_sparse_attn with a workspace)",
+                p.total, (size_t)SVGEAR_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  st = noalloc_scratch(stream, &ws);
+  if (st != SVGEAR_OK) return st;
+  return sparse_attn_impl(q_perm, k_perm, v_perm, dt, q_perm_idx, q_offsets, Cq, k_offsets, Ck, k_means, v_means,
+                          nullptr, 0.f, mask, B, H, N, D, scale, out, lse, ws, (size_t)SVGEAR_NOALLOC_SCRATCH_BYTES,
+                          stream);
 }

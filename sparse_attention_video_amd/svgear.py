@@ -30,6 +30,7 @@ EXPORTS = (
     "svgear_route_topp",
     "svgear_kmeanspp_workspace", "svgear_kmeanspp",
     "svgear_quantize_fp8_workspace", "svgear_quantize_fp8", "svgear_sparse_attn_fp8",
+    "svgear_sparse_attn_noalloc",
 )
 
 _lib = None
@@ -84,6 +85,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.svgear_quantize_fp8.restype = I
     lib.svgear_sparse_attn_fp8.argtypes = [P, P, P, P, P, P, P, I, P, I, P, P, P, I, I, I, I, F, P, P, P, Z, P]
     lib.svgear_sparse_attn_fp8.restype = I
+    lib.svgear_sparse_attn_noalloc.argtypes = [P, P, P, I, P, P, I, P, I, P, P, P, I, I, I, I, F, P, P, P]
+    lib.svgear_sparse_attn_noalloc.restype = I
     _lib = lib
     return lib
 
@@ -446,6 +449,26 @@ def sparse_attn(q_perm, k_perm, v_perm, q_perm_idx, q_offsets, k_offsets, k_mean
                                           B, H, N, D, float(scale), _ptr(out), _ptr(lse if want_lse else None),
                                           _ptr(ws), ws.numel(), _stream(dev)))
     return out, (lse if want_lse else None)
+
+
+def sparse_attn_noalloc(q_perm, k_perm, v_perm, q_perm_idx, q_offsets, k_offsets, k_means, v_means, mask,
+                        scale: float, out: torch.Tensor, lse: Optional[torch.Tensor] = None):
+    """sparse_attn through the entry point that allocates nothing: its scratch
+    is the library's static device array (calls that overlap on one GPU
+    race).  ``out`` (and ``lse`` if wanted) are the caller's."""
+    B, H, N, D = _dims4("q_perm", q_perm)
+    _want("k_perm", k_perm, q_perm.dtype, (B, H, N, D), optional=False)
+    _want("v_perm", v_perm, q_perm.dtype, (B, H, N, D), optional=False)
+    _want("out", out, q_perm.dtype, (B, H, N, D), optional=False)
+    Cq, Ck = _attn_tables(B, H, N, D, q_perm_idx, q_offsets, k_offsets, k_means, v_means, mask, out, q_perm.dtype,
+                          lse)
+    dev = _dev(q_perm, k_perm, v_perm, q_perm_idx, q_offsets, k_offsets, k_means, v_means, mask, out, lse)
+    _check("svgear_sparse_attn_noalloc",
+           load().svgear_sparse_attn_noalloc(_ptr(q_perm), _ptr(k_perm), _ptr(v_perm), _dtype(q_perm),
+                                             _ptr(q_perm_idx), _ptr(q_offsets), Cq, _ptr(k_offsets), Ck,
+                                             _ptr(k_means), _ptr(v_means), _ptr(mask), B, H, N, D, float(scale),
+                                             _ptr(out), _ptr(lse), _stream(dev)))
+    return out, lse
 
 
 # ----------------------------------------------------------------------------

@@ -28,7 +28,7 @@ def lib():
 
 def test_every_declared_symbol_is_exported(lib):
     names = declared()
-    assert len(names) == 18
+    assert len(names) == 19
     for n in names:
         assert hasattr(lib, n), n
     from sparse_attention_video_amd import svgear
@@ -241,3 +241,16 @@ def test_binding_validates_other_calls():
     with pytest.raises(ValueError, match="ws"):
         svgear.sparse_attn(a["q"], a["k"], a["v"], a["idx"], a["oq"], a["ok"], a["km"], a["vm"], a["mask"], 0.125,
                            ws=torch.zeros(16, dtype=f32))
+
+
+def test_noalloc_attention_validates_before_touching_the_gpu(lib):
+    """The allocation-free attention entry point refuses sizes whose scratch
+    exceeds its static array, and bad arguments, before any HIP call."""
+    F = FAKE
+    A = lambda H, N, Cq, Ck, out=F: lib.svgear_sparse_attn_noalloc(F, F, F, 0, F, F, Cq, F, Ck, F, F, F, 1, H, N, 128,
+                                                                   ctypes.c_float(0.088), out, None, None)
+    assert lib.svgear_sparse_attn_workspace(1, 200, 75600, 128, 100, 500) > (32 << 20)
+    assert A(200, 75600, 100, 500) == 1
+    assert "scratch" in lib.svgear_last_error().decode()
+    assert A(40, 75600, 0, 500) == 1         # invalid sizes: workspace query 0, validation refuses
+    assert A(40, 100, 200, 500) == 1         # Cq > N
