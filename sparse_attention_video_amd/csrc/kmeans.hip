@@ -793,9 +793,11 @@ __device__ __forceinline__ int km_fx_q(float v, int s) { return (int)rintf(ldexp
 // [offsets[c] + k' * rows, ...) of x[perm[.]] (k' = k - chunk_start[c]),
 // optionally writing the permuted copy.  Fixed row-to-lane mapping and a
 // fixed reduction order keep the sums deterministic.  SQ: sums of squared
-// deviations from the cluster means `center` instead (variances).
+// deviations from the cluster means `center` instead (variances).  PERM:
+// the permuted copy x_perm is written (svgear_centroids); without it the
+// kernel only reads (the k-means update).
 // --------------------------------------------------------------------------
-template <typename T, int D, bool SQ = false, bool FX = false>
+template <typename T, int D, bool SQ = false, bool FX = false, bool PERM = false>
 __global__ void __launch_bounds__(256) km_partial_kernel(const T* __restrict__ x, const int32_t* __restrict__ perm,
                                                          const int32_t* __restrict__ offsets,
                                                          const int32_t* __restrict__ chunk_start, int N, int C,
@@ -821,7 +823,7 @@ __global__ void __launch_bounds__(256) km_partial_kernel(const T* __restrict__ x
   const int g = threadIdx.x / LPR, e0 = (threadIdx.x % LPR) * EPL;
   const T* xb = x + (size_t)bh * N * D;
   const int32_t* pb = perm + (size_t)bh * N;
-  T* xpb = x_perm ? x_perm + (size_t)bh * N * D : nullptr;
+  T* xpb = PERM ? x_perm + (size_t)bh * N * D : nullptr;
   Acc acc[EPL];
   float mu[EPL];
   const int fs = FX ? km_fx_shift(km_r2_bits(r2max, bh)) : 0;
@@ -850,7 +852,7 @@ __global__ void __launch_bounds__(256) km_partial_kernel(const T* __restrict__ x
     for (int k = 0; k < 4; ++k) v[k] = ld16(xb + (size_t)src[k] * D + e0);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      if (xpb) st16(xpb + (size_t)(p + k * RPI) * D + e0, v[k]);
+      if constexpr (PERM) st16(xpb + (size_t)(p + k * RPI) * D + e0, v[k]);
       const T* tv = reinterpret_cast<const T*>(&v[k]);
 #pragma unroll
       for (int e = 0; e < EPL; ++e) add(to_f32(tv[e]), e);
@@ -859,7 +861,7 @@ __global__ void __launch_bounds__(256) km_partial_kernel(const T* __restrict__ x
   for (; p < r1; p += RPI) {
     const int src = pb[p];
     const u32x4 v = ld16(xb + (size_t)src * D + e0);
-    if (xpb) st16(xpb + (size_t)p * D + e0, v);
+    if constexpr (PERM) st16(xpb + (size_t)p * D + e0, v);
     const T* tv = reinterpret_cast<const T*>(&v);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) add(to_f32(tv[e]), e);
@@ -1147,8 +1149,12 @@ static MeanPlan mean_plan(int B, int H, int N, int D, int C) {
 template <typename T, int D>
 static void launch_partial(const void* x, const int32_t* perm, const int32_t* offsets, const int32_t* cs, int BH,
                            int N, int C, int maxch, float* partial, void* x_perm, hipStream_t st) {
-  hipLaunchKernelGGL((km_partial_kernel<T, D>), dim3(maxch, BH), dim3(256), 0, st, (const T*)x, perm, offsets, cs, N,
-                     C, MEAN_ROWS, maxch, partial, (T*)x_perm, nullptr);
+  if (x_perm)
+    hipLaunchKernelGGL((km_partial_kernel<T, D, false, false, true>), dim3(maxch, BH), dim3(256), 0, st, (const T*)x,
+                       perm, offsets, cs, N, C, MEAN_ROWS, maxch, partial, (T*)x_perm, nullptr);
+  else
+    hipLaunchKernelGGL((km_partial_kernel<T, D>), dim3(maxch, BH), dim3(256), 0, st, (const T*)x, perm, offsets, cs,
+                       N, C, MEAN_ROWS, maxch, partial, (T*)nullptr, nullptr);
 }
 
 template <typename T, int D>
