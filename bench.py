@@ -34,10 +34,10 @@ METRIC = "ms per attention layer (cluster+route+sparse attn), 75.6k tok, 25% den
 # FETCH_SIZE / WRITE_SIZE calibrated against a 1 GiB device copy (FETCH x 2.0,
 # WRITE x 1.0); valid only for the attention source it was measured on.
 ATTN_TRAFFIC = {
-    "source_sha256": "ee0857b4319373b5b0e84584c00b72d70f02fff87fa9ffd95bdcba648e6b8e2b",
+    "source_sha256": "ef6e19ac9aa3bf14b3ab0d713d7f9ac53585bde8241deac3aec93ce4e17c8eb7",
     "workload": "wan",
-    "fetch_bytes": 38.01e9,
-    "write_bytes": 0.774e9,
+    "fetch_bytes": 40.12e9,
+    "write_bytes": 0.775e9,
 }
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP8_TFLOPS = 5000.0
