@@ -661,17 +661,33 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
   // scores are masked
   int tc = 0, tc_base = nsel > 0 ? sSelStart[0] : 0, tc_pre = 0;
   int tc_nxt = nsel > 1 ? sSelPre[1] : 0x7fffffff;
+  auto advance = [&](int p) {
+    while (p >= tc_nxt) {
+      ++tc;
+      tc_base = sSelStart[tc];
+      tc_pre = tc_nxt;
+      tc_nxt = tc + 1 < nsel ? sSelPre[tc + 1] : 0x7fffffff;
+    }
+  };
+  // the lane's rows are p0 + RPI i (i < NI); when every lane's rows lie in
+  // one selected cluster before the end (a cluster boundary falls in the
+  // wave's 16-row band of a tile about one time in ten) one cursor step and
+  // one offset serve them all
   auto sources = [&](int kt, uint32_t* rowoff) {
+    const int p0 = kt * AT_BN + w * NI * RPI + lq;
+    const int pl = p0 + (NI - 1) * RPI;
+    advance(p0);
+    if (ballot(pl >= tc_nxt || pl >= nkeys) == 0) {
+      const uint32_t r0 = (uint32_t)(tc_base + (p0 - tc_pre)) * (uint32_t)ROWB;
 #pragma unroll
-    for (int i = 0; i < NI; ++i) {
-      const int p = kt * AT_BN + (w * NI + i) * RPI + lq;
-      while (p >= tc_nxt) {
-        ++tc;
-        tc_base = sSelStart[tc];
-        tc_pre = tc_nxt;
-        tc_nxt = tc + 1 < nsel ? sSelPre[tc + 1] : 0x7fffffff;
+      for (int i = 0; i < NI; ++i) rowoff[i] = r0 + (uint32_t)(i * RPI * ROWB);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int p = p0 + i * RPI;
+        advance(p);
+        rowoff[i] = (uint32_t)(p < nkeys ? tc_base + (p - tc_pre) : 0) * (uint32_t)ROWB;
       }
-      rowoff[i] = (uint32_t)(p < nkeys ? tc_base + (p - tc_pre) : 0) * (uint32_t)ROWB;
     }
   };
   // e4m3 K rows: instruction j of wave w fills rows (w NI8 + j) RPI8 + L / CH8
