@@ -34,10 +34,10 @@ METRIC = "ms per attention layer (cluster+route+sparse attn), 75.6k tok, 25% den
 # FETCH_SIZE / WRITE_SIZE calibrated against a 1 GiB device copy (FETCH x 2.0,
 # WRITE x 1.0); valid only for the attention source it was measured on.
 ATTN_TRAFFIC = {
-    "source_sha256": "fda47aaa020fd0d933bbdf3f13f5c2e79da8293d70dc08ce1efdab61b403f3fa",
+    "source_sha256": "121308afdd1ba5d3ba538f17214b64b3b30c4d719577a20c3ce6b0ada693ce0d",
     "workload": "wan",
-    "fetch_bytes": 41.16e9,
-    "write_bytes": 0.774e9,
+    "fetch_bytes": 41.72e9,
+    "write_bytes": 0.775e9,
 }
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_FP8_TFLOPS = 5000.0
