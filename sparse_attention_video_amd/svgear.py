@@ -520,8 +520,9 @@ class Layer:
         with torch.cuda.stream(self.side):
             kmeans(k, ck, iters, self.lk, self.pk, self.ok, ws=self.ws_k)
         kmeans(q, cq, iters, self.lq, self.pq, self.oq, ws=self.ws)
-        main.wait_stream(self.side)
+        # Q's permuted copy and means overlap the tail of K's clustering
         centroids(q, self.pq, self.oq, x_perm=self.qp, means=self.qm, ws=self.ws)
+        main.wait_stream(self.side)
         centroids(k, self.pk, self.ok, x_perm=self.kp, means=self.km, ws=self.ws)
         centroids(v, self.pk, self.ok, x_perm=self.vp, means=self.vm, ws=self.ws)
         if top_p is None:
