@@ -360,6 +360,59 @@ def test_sparse_attn_teacher_forced(sv, name, maskkind, ref_cache):
         assert np.abs(lse[h] - L).max() <= (1e-2 if w.dtype == "bf16" else 1e-4)
 
 
+def _subset_with_sum(sizes, target, rng):
+    """Indices of clusters whose sizes add up to exactly `target`."""
+    for _ in range(2000):
+        pick, tot = [], 0
+        for j in rng.permutation(len(sizes)):
+            if tot + sizes[j] <= target:
+                pick.append(j)
+                tot += sizes[j]
+            if tot == target:
+                return sorted(pick)
+    raise AssertionError(f"no subset sums to {target}")
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_sparse_attn_cluster_boundaries_and_ragged_tiles(sv, D):
+    """Key clusters of 1..200 keys, so that cluster boundaries fall at every
+    offset of a tile's wave bands and long runs have none; selected lists of
+    0, 1, 63, 64, 65 keys and more (partial, exact and one-past tiles); query
+    clusters of 1, 31-33, 127-129 rows (partly filled waves and tiles)."""
+    from synth.gen import bf16_round
+    rng = np.random.default_rng(17 + D)
+    N = 1536
+    ks = [1, 2, 3, 4, 5, 6, 7, 8, 9, 11, 12, 13, 15, 16, 17, 19, 23, 31, 32, 33, 47, 63, 64, 65, 100, 130, 200]
+    ks.append(N - sum(ks))
+    qs = [1, 31, 32, 33, 127, 128, 129, 64, 200]
+    qs.append(N - sum(qs))
+    Ck, Cq = len(ks), len(qs)
+    lk = rng.permutation(np.repeat(np.arange(Ck), ks))
+    lq = rng.permutation(np.repeat(np.arange(Cq), qs))
+    q, k, v = (bf16_round(rng.normal(0.0, 1.0, (N, D)).astype(np.float32)) for _ in range(3))
+    pq, oq = orc.permute(lq.astype(np.int64), Cq)
+    pk, ok = orc.permute(lk.astype(np.int64), Ck)
+    kbar, vbar = orc.means(k, pk, ok), orc.means(v, pk, ok)
+    sizes = np.diff(ok)
+    mask = (rng.random((Cq, Ck)) < 0.5).astype(np.uint8)
+    mask[0] = 1                                      # every cluster
+    mask[1] = 0                                      # compensation only
+    mask[2] = 0
+    mask[2, int(np.argmin(sizes))] = 1               # one key
+    for row, target in ((3, 63), (4, 64), (5, 65), (6, 129)):
+        mask[row] = 0
+        mask[row, _subset_with_sum(list(sizes), target, rng)] = 1
+    sc = 1.0 / np.sqrt(D)
+    dev4 = lambda a: to_dev(a[None, None], "bf16")
+    out, _ = sv.sparse_attn(dev4(q[pq]), dev4(k[pk]), dev4(v[pk]), i32(pq[None, None]), i32(oq[None, None]),
+                            i32(ok[None, None]), f32(kbar[None, None]), f32(vbar[None, None]),
+                            torch.from_numpy(mask[None, None]).cuda(), sc)
+    out = host(out)[0, 0]
+    O, _ = orc.attend(q, k, v, pq, oq, pk, ok, kbar, vbar, mask, sc)
+    err = np.abs(out - O)
+    assert err.max() <= ATOL["bf16"][0] and err.mean() <= ATOL["bf16"][1], (err.max(), err.mean())
+
+
 def test_sparse_attn_density_one_is_full_attention(sv, ref_cache):
     w, x, outs, sc = oracle_layer("bf16-d128", ref_cache)
     m = np.stack([(np.diff(o["ok"]) > 0)[None, :].repeat(w.Cq, 0) for o in outs]).astype(np.uint8)
