@@ -411,6 +411,308 @@ __global__ void __launch_bounds__(RT_WAVES * 64) __attribute__((amdgpu_waves_per
   }
 }
 
+// The probe for bfloat16 keys, without centring.  A bf16 key is exact, so the
+// two 16x16x32 products of a key against the hi and lo planes of scale *
+// log2(e) * q_bar give s_k = q2 . k (q2 = hi + lo, within 2^-17 of q_bar per
+// coordinate) exact up to the fp32 accumulation.  A piece's reference score
+// s'_j = q2 . k_bar_j is taken by the same product sequence on rows holding
+// k_bar_j's exact three-piece bf16 split, summed, so that ds = s_k - s'_j =
+// q2 . (k - k_bar_j) up to rounding (the centring kernel's ds carries the same
+// 2^-17 truncation of q_bar), and a key equal to its cluster mean (a
+// singleton, a cluster of identical members) gets ds = 0 exactly; the
+// statistics are then those of rt_probe_kernel.  K sub-tiles go straight from
+// global memory into two LDS tiles (each thread one 16-byte chunk, loads
+// issued one sub-tile ahead; two separate arrays, so that the compiler's
+// waits for an operand read cover only the tile it reads), rows past a
+// piece's end repeat its last key, whose statistics are zeroed; the chunks of a row are XOR-swizzled so
+// that the 16 rows of an operand read fall on distinct banks.  V rows come
+// into registers for the per-key statistics as in rt_probe_kernel.
+template <int D>
+struct RtTile {
+  static constexpr int ROWB = 2 * D, CH = D / 8, SLOTS = 32 * CH;  // 16-byte chunks per row, per sub-tile
+  static __device__ __forceinline__ int swz(int r) { return CH == 16 ? (r & 15) : ((r >> 1) & 7); }
+};
+
+template <int D>
+__global__ void __launch_bounds__(RT_WAVES * 64) __attribute__((amdgpu_waves_per_eu(4))) rt_probe_bf16_kernel(
+    const bf16* __restrict__ kp, const bf16* __restrict__ vp, const float* __restrict__ kmeans,
+    const float* __restrict__ vmeans, const int4* __restrict__ pinfo, const int32_t* __restrict__ pstart,
+    const bf16* __restrict__ qhi, const bf16* __restrict__ qlo, int N, int Cq, int Cqp, int Ck, int maxp,
+    float* __restrict__ part, float* __restrict__ t1part) {
+  using TL = RtTile<D>;
+  constexpr int NT = RT_WAVES * 64;
+  constexpr int KS = D / 32;   // 16x16x32 K-steps over the head dim
+  constexpr int DPT = D / 16;  // V coordinates per thread (16 threads per key)
+  constexpr int QW = 16 * RT_WAVES;
+  constexpr int MSLOTS = RT_PPW * (D / 4) / NT;  // 16-byte v_bar loads per thread in the prologue
+  static_assert(TL::SLOTS <= NT && MSLOTS >= 1, "one K chunk per thread");
+  __shared__ __attribute__((aligned(1024))) char sK0[32 * TL::ROWB];
+  __shared__ __attribute__((aligned(1024))) char sK1[32 * TL::ROWB];
+  // chunks of the waves beyond a sub-tile's (D = 64) land here, unused, so
+  // that every thread issues the same loads and the load counts stay exact
+  __shared__ __attribute__((aligned(1024))) char sKx[TL::SLOTS < NT ? 16 * (NT - TL::SLOTS) : 16];
+  __shared__ __attribute__((aligned(16))) float sW[2][32];
+  __shared__ __attribute__((aligned(16))) float sVV[2][32];
+  __shared__ __attribute__((aligned(16))) float sVm[RT_PPW][D];  // v_bar of each piece's cluster
+  __shared__ float sVbsq[RT_PPW][16];                            // ||v_bar||^2 over each thread segment
+  __shared__ float sSb[RT_WAVES][RT_PPW][16];                    // s'_j of each piece, per wave query column
+  __shared__ int4 sInfo[RT_PPW];
+  __shared__ int2 sStream[RT_PPW * (RT_PIECE / 32)];
+  __shared__ int sNsub;
+
+  const int bh = blockIdx.y, tid = threadIdx.x, lane = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(wave_id());
+  const int grp = lane >> 4, col = lane & 15;
+  const int kr = tid >> 4, seg = tid & 15, d0 = seg * DPT;
+  const int P = pstart[(size_t)bh * (Ck + 1) + Ck];
+  const int bx = blockIdx.x, G = gridDim.x;
+  if (bx >= P) return;
+  const int nall = (P - 1 - bx) / G + 1;
+  const bf16* kb = kp + (size_t)bh * N * D;
+  const bf16* vb = vp + (size_t)bh * N * D;
+  const __amdgpu_buffer_rsrc_t rK = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)kb, (short)0, (int)((uint32_t)N * (uint32_t)TL::ROWB), 0x00020000);
+  // this thread's K chunk in a sub-tile: row kq, chunk kc (stored at slot tid)
+  const int kslot = tid % TL::SLOTS;
+  const int kq = kslot / TL::CH, kc = (kslot % TL::CH) ^ TL::swz(kslot / TL::CH);
+
+  for (int kb0 = 0; kb0 < nall; kb0 += RT_PPW) {
+  const int npc = min(RT_PPW, nall - kb0);
+  if (tid < npc) sInfo[tid] = pinfo[(size_t)bh * maxp + bx + (kb0 + tid) * G];
+  __syncthreads();
+  {
+    f32x4 mv[MSLOTS];
+#pragma unroll
+    for (int u = 0; u < MSLOTS; ++u) {
+      const int v = tid + NT * u, k = v / (D / 4), o = (v % (D / 4)) * 4;
+      mv[u] = f32x4{};
+      if (k < npc) mv[u] = *reinterpret_cast<const f32x4*>(vmeans + ((size_t)bh * Ck + sInfo[k].x) * D + o);
+    }
+#pragma unroll
+    for (int u = 0; u < MSLOTS; ++u) {
+      const int v = tid + NT * u, k = v / (D / 4), o = (v % (D / 4)) * 4;
+      if (k < npc) *reinterpret_cast<f32x4*>(&sVm[k][o]) = mv[u];
+    }
+  }
+  if (w == 0) {
+    const int4 in = lane < npc ? sInfo[lane] : make_int4(0, 0, 0, 0);
+    const int ns = lane < npc ? (in.z - in.y + 31) / 32 : 0;
+    int x = ns;
+#pragma unroll
+    for (int o = 1; o < SV_WAVE; o <<= 1) {
+      const int y = __shfl_up(x, o, SV_WAVE);
+      if (lane >= o) x += y;
+    }
+    const int base = x - ns;
+    for (int u = 0; u < ns; ++u) sStream[base + u] = make_int2(lane, in.y + 32 * u);
+    if (lane == SV_WAVE - 1) sNsub = x;
+  }
+  __syncthreads();
+  for (int u = tid; u < npc * 16; u += NT) {
+    const int k = u >> 4, sg = u & 15;
+    float t = 0.f;
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) t = fmaf(sVm[k][sg * DPT + e], sVm[k][sg * DPT + e], t);
+    sVbsq[k][sg] = t;
+  }
+  __syncthreads();
+  const int nsub = sNsub;
+
+  // K chunks of sub-tile s into tile kt, and this thread's V row segment of
+  // sub-tile s.  Every thread always issues both loads (past the last
+  // sub-tile, or past a piece's end, the rows are clamped to real ones whose
+  // statistics are not used), so that the loads in flight are the same on
+  // every path and the waits for them stay partial.
+  auto kload = [&](int s, char* kt) {
+    const int2 st = sStream[min(s, nsub - 1)];
+    const int g = min(st.y + kq, sInfo[st.x].z - 1);
+    char* dst = tid < TL::SLOTS ? kt + 1024 * w : sKx + 1024 * (w - TL::SLOTS / 64);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (__attribute__((address_space(3))) void*)dst, 16,
+                                             (int)((uint32_t)g * TL::ROWB + kc * 16), 0, 0, 0);
+  };
+  auto fetch = [&](int s, RtSeg<bf16, DPT>& rv) {
+    const int2 st = sStream[min(s, nsub - 1)];
+    rv.load(vb + (size_t)min(st.y + kr, sInfo[st.x].z - 1) * D + d0);
+  };
+
+  for (int qb = 0; qb < Cqp; qb += QW) {
+    const int qt = qb / 16 + w;
+    const bool has_q = qt * 16 < Cq;
+    bf16x8 qh[KS], ql[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 h = {}, l = {};
+      if (has_q) {
+        const size_t o = ((size_t)bh * Cqp + qt * 16 + col) * D + 32 * ks + 8 * grp;
+        h = *reinterpret_cast<const bf16x8*>(qhi + o);
+        l = *reinterpret_cast<const bf16x8*>(qlo + o);
+      }
+      qh[ks] = h;
+      ql[ks] = l;
+    }
+    // s_k for 16 rows whose K-step ks operand frag(ks) returns: the same
+    // product sequence for keys and for the k_bar rows
+    auto scores16 = [&](auto frag) {
+      f32x4 acc = f32x4{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 a = frag(ks);
+        acc = mfma16_bf16(a, qh[ks], acc);
+        acc = mfma16_bf16(a, ql[ks], acc);
+      }
+      return acc;
+    };
+    if (has_q) {
+      // s'_j: block bl holds pieces 4 bl + m in rows 4 m + t, t = 0, 1, 2 the
+      // hi, mid, lo parts of k_bar (row 4 m + 3 zero); lane (col, grp) then
+      // holds the three parts of piece 4 bl + grp for its query column
+      for (int bl = 0; 4 * bl < npc; ++bl) {
+        const int k = 4 * bl + (col >> 2), t = col & 3;
+        const bool live = k < npc && t < 3;
+        const float* src = kmeans + ((size_t)bh * Ck + (live ? sInfo[k].x : 0)) * D + 8 * grp;
+        const f32x4 acc = scores16([&](int ks) {
+          bf16x8 a = {};
+          if (live) {
+            const f32x4 x0 = *reinterpret_cast<const f32x4*>(src + 32 * ks);
+            const f32x4 x1 = *reinterpret_cast<const f32x4*>(src + 32 * ks + 4);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float v = e < 4 ? x0[e] : x1[e - 4];
+              const bf16 h = (bf16)v;
+              const float r1 = v - (float)h;
+              const bf16 m = (bf16)r1;
+              const bf16 l = (bf16)(r1 - (float)m);
+              a[e] = t == 0 ? h : (t == 1 ? m : l);
+            }
+          }
+          return a;
+        });
+        if (4 * bl + grp < npc) sSb[w][4 * bl + grp][col] = (acc[0] + acc[1]) + acc[2];
+      }
+    }
+    RtSeg<bf16, DPT> rv[2];
+    kload(0, sK0);
+    fetch(0, rv[0]);
+    __builtin_amdgcn_sched_barrier(0);  // keep sub-tile 0's load ahead of sub-tile 1's (the loop's waits count on it)
+    fetch(1, rv[1]);
+    __syncthreads();  // s'_j table written
+    float dl = 0.f, s2 = 0.f, s3 = 0.f, t1acc = 0.f;
+
+    auto step = [&](int s, auto bc) {
+      constexpr int b = decltype(bc)::value;
+      const int2 st = sStream[s];
+      const int k = st.x;
+      {
+        const bool ok = st.y + kr < sInfo[k].z;
+        float bvp = 0.f, vvp = 0.f;
+        if (ok) {
+#pragma unroll
+          for (int e0 = 0; e0 < DPT; e0 += 4) {
+            const f32x4 vb4 = *reinterpret_cast<const f32x4*>(&sVm[k][d0 + e0]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float vf = rv[b].at(e0 + e);
+              bvp = fmaf(vb4[e], vf, bvp);
+              vvp = fmaf(vf, vf, vvp);
+            }
+          }
+          t1acc += sVbsq[k][seg] - 2.f * bvp + vvp;
+        }
+        bvp = row16_sum(bvp);
+        vvp = row16_sum(vvp);
+        if (seg == 0) {
+          sW[b][kr] = ok ? bvp - vvp : 0.f;
+          sVV[b][kr] = ok ? vvp : 0.f;
+        }
+      }
+      // this wave's K chunks of sub-tile s have landed (only the V load of
+      // sub-tile s + 1 may still be in flight); after the barrier every
+      // wave's have, and every wave is done with sub-tile s - 1's tile
+      __builtin_amdgcn_s_waitcnt(0x0F71);
+      __syncthreads();
+      kload(s + 1, b ? sK0 : sK1);
+      fetch(s + 2, rv[b]);
+      if (has_q) {
+        const char* kt = b ? sK1 : sK0;
+        f32x4 acc[2];
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          const int r = 16 * hb + col;
+          acc[hb] = scores16([&](int ks) {
+            return *reinterpret_cast<const bf16x8*>(kt + r * TL::ROWB + (((4 * ks + grp) ^ TL::swz(r)) << 4));
+          });
+        }
+        const float sbp = sSb[w][k][col];
+        float mx = acc[0][0];
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) mx = fmaxf(mx, acc[hb][j]);
+        const float dn = fmaxf(dl, mx - sbp);
+        if (dn > dl) {
+          const float f = __builtin_amdgcn_exp2f(dl - dn);
+          s2 *= f;
+          s3 *= f * f;
+          dl = dn;
+        }
+        const float a = __builtin_amdgcn_exp2f(-dn);
+        const float c = sbp + dn;
+        float t2 = 0.f, t3 = 0.f;
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          const f32x4 wv = *reinterpret_cast<const f32x4*>(&sW[b][16 * hb + 4 * grp]);
+          const f32x4 vq = *reinterpret_cast<const f32x4*>(&sVV[b][16 * hb + 4 * grp]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float eps = __builtin_amdgcn_exp2f(acc[hb][j] - c) - a;
+            t2 = fmaf(eps, wv[j], t2);
+            t3 = fmaf(eps * eps, vq[j], t3);
+          }
+        }
+        s2 += t2;
+        s3 += t3;
+      }
+      if (s + 1 == nsub || sStream[s + 1].x != k) {
+        const int pc = bx + (kb0 + k) * G;
+        if (has_q) {
+#pragma unroll
+          for (int m = 16; m <= 32; m <<= 1) {
+            const float od = shfl_xor(dl, m), o2 = shfl_xor(s2, m), o3 = shfl_xor(s3, m);
+            const float dm = fmaxf(dl, od);
+            const float fa = __builtin_amdgcn_exp2f(dl - dm), fb = __builtin_amdgcn_exp2f(od - dm);
+            s2 = s2 * fa + o2 * fb;
+            s3 = s3 * fa * fa + o3 * fb * fb;
+            dl = dm;
+          }
+          const int q = qt * 16 + col;
+          if (grp == 0 && q < Cq) {
+            float* o = part + (((size_t)bh * maxp + pc) * Cq + q) * 3;
+            o[0] = dl * 0.69314718055994531f;
+            o[1] = s2;
+            o[2] = s3;
+          }
+        }
+        dl = 0.f;
+        s2 = 0.f;
+        s3 = 0.f;
+        const float t1w = wave_sum_f(t1acc);
+        if (qb == 0 && lane == 0) t1part[((size_t)bh * maxp + pc) * RT_WAVES + w] = t1w;
+        t1acc = 0.f;
+      }
+    };
+    // pairs of sub-tiles, then an odd last one (a loop that could also skip
+    // its second step would merge load counts and make every wait a drain)
+    int s = 0;
+    for (; s + 1 < nsub; s += 2) {
+      step(s, std::integral_constant<int, 0>{});
+      step(s + 1, std::integral_constant<int, 1>{});
+    }
+    if (s < nsub) step(s, std::integral_constant<int, 0>{});
+    __syncthreads();
+  }
+  }
+}
+
 // T1_j = sum over cluster j's keys of ||v_bar_j - v_k||^2, from the probe
 // waves' shares, added in a fixed order (pieces ascending, waves ascending).
 __global__ void __launch_bounds__(256) rt_t1_kernel(const float* __restrict__ t1part,
@@ -566,6 +868,49 @@ __global__ void __launch_bounds__(256) rt_topp_kernel(const float* __restrict__ 
   if (tid == 0 && budget) budget[row] = s_take[1];
 }
 
+// Error of key cluster j for query cluster i from the probe's per-piece
+// statistics: the pieces are merged in piece order (up to 8 pieces' loads in
+// flight at a time), each rescaled to the running stabiliser; E is the error
+// relative to e^{2 mu} with mu = s_bar_ij + delta_ij (the cluster's largest
+// probe score), i.e. e_ij = E e^{2 mu}.
+__device__ __forceinline__ void cluster_error(const float* __restrict__ part, const float* __restrict__ t1c,
+                                              const int32_t* __restrict__ ps, const float* __restrict__ sbar, int bh,
+                                              int i, int j, int Cq, int Ck, int maxp, float& E, float& mu) {
+  float dm = 0.f, S2 = 0.f, S3 = 0.f;
+  const int pe = ps[j + 1];
+  for (int pc0 = ps[j]; pc0 < pe; pc0 += 8) {
+    float o0[8], o1[8], o2[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const bool in = pc0 + u < pe;
+      const float* o = part + (((size_t)bh * maxp + (in ? pc0 + u : pc0)) * Cq + i) * 3;
+      o0[u] = in ? o[0] : 0.f;
+      o1[u] = in ? o[1] : 0.f;
+      o2[u] = in ? o[2] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (pc0 + u >= pe) break;  // (an absent piece would leave the sums unchanged)
+      const float dn = fmaxf(dm, o0[u]);
+      const float fa = __expf(dm - dn), fb = __expf(o0[u] - dn);
+      S2 = S2 * fa + o1[u] * fb;
+      S3 = S3 * fa * fa + o2[u] * fb * fb;
+      dm = dn;
+    }
+  }
+  const float T1 = t1c[(size_t)bh * Ck + j];
+  const float a = __expf(-dm);
+  E = fmaxf(0.f, a * a * T1 - 2.f * a * S2 + S3);
+  mu = sbar[((size_t)bh * Cq + i) * Ck + j] + dm;
+}
+
+// The ratio r_ij = e_ij e^{-2 M} / (|Q_i| |K_j|) from E and mu (M the row's
+// largest mu), in fp64 and rounded once.
+__device__ __forceinline__ float cluster_ratio(float E, float mu, float M, int mi, int nj) {
+  const double e = (double)E * exp(2.0 * ((double)mu - (double)M));
+  return (float)(e / ((double)mi * (double)nj));
+}
+
 __global__ void __launch_bounds__(256) rt_select_kernel(const float* __restrict__ part, const float* __restrict__ t1c,
                                                         const int32_t* __restrict__ pstart, const float* __restrict__ sbar,
                                                         const int32_t* __restrict__ qoff, const int32_t* __restrict__ koff,
@@ -603,33 +948,7 @@ __global__ void __launch_bounds__(256) rt_select_kernel(const float* __restrict_
     for (int j = tid; j < Ck; j += 256) {
       float mu = -INFINITY, E = 0.f;
       if (ko[j + 1] > ko[j]) {
-        // merge the cluster's pieces: up to 8 pieces' statistics are loaded
-        // at once, then folded in piece order with rescaling to the running
-        // stabiliser
-        float dm = 0.f, S2 = 0.f, S3 = 0.f;
-        for (int pc0 = ps[j]; pc0 < ps[j + 1]; pc0 += 8) {
-          float o0[8], o1[8], o2[8];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const bool in = pc0 + u < ps[j + 1];
-            const float* o = part + (((size_t)bh * maxp + (in ? pc0 + u : pc0)) * Cq + i) * 3;
-            o0[u] = in ? o[0] : 0.f;
-            o1[u] = in ? o[1] : 0.f;
-            o2[u] = in ? o[2] : 0.f;
-          }
-#pragma unroll
-          for (int u = 0; u < 8; ++u) {
-            const float dn = fmaxf(dm, o0[u]);
-            const float fa = __expf(dm - dn), fb = __expf(o0[u] - dn);
-            S2 = S2 * fa + o1[u] * fb;
-            S3 = S3 * fa * fa + o2[u] * fb * fb;
-            dm = dn;
-          }
-        }
-        const float T1 = t1c[(size_t)bh * Ck + j];
-        const float a = __expf(-dm);
-        E = fmaxf(0.f, a * a * T1 - 2.f * a * S2 + S3);
-        mu = sbar[((size_t)bh * Cq + i) * Ck + j] + dm;
+        cluster_error(part, t1c, ps, sbar, bh, i, j, Cq, Ck, maxp, E, mu);
         mloc = fmaxf(mloc, mu);
       }
       s_mu[j] = mu;
@@ -641,12 +960,7 @@ __global__ void __launch_bounds__(256) rt_select_kernel(const float* __restrict_
     const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
     for (int j = tid; j < Ck; j += 256) {
       const int nj = ko[j + 1] - ko[j];
-      float r = 0.f;
-      if (nj > 0) {
-        const double e = (double)s_e[j] * exp(2.0 * ((double)s_mu[j] - (double)M));
-        r = (float)(e / ((double)mi * (double)nj));
-      }
-      s_e[j] = r;
+      s_e[j] = nj > 0 ? cluster_ratio(s_e[j], s_mu[j], M, mi, nj) : 0.f;
     }
   }
   __syncthreads();
@@ -677,6 +991,129 @@ __global__ void __launch_bounds__(256) rt_select_kernel(const float* __restrict_
   // empty key clusters (sorted last with the all-ones key) are never taken
   for (int j = tid; j < Ck; j += 256)
     if (ko[j + 1] == ko[j]) mrow[j] = 0;
+}
+
+// Sum of an integer over the 16 lanes of each row (DPP butterfly, as
+// row16_sum); every lane of the row gets its row's sum.
+__device__ __forceinline__ int row16_sum_i(int v) {
+  v += __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, true);   // quad_perm [1,0,3,2]
+  v += __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, true);   // quad_perm [2,3,0,1]
+  v += __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, true);  // row_half_mirror
+  v += __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, true);  // row_mirror
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+  v = row16_sum_i(v);
+  return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) + __builtin_amdgcn_readlane(v, 32) +
+         __builtin_amdgcn_readlane(v, 48);
+}
+
+// The same selection with one wave per (batch, head, query cluster) when
+// C_k <= 64 RT_SEL_CPL: cluster j = lane + 64 e lives in lane registers, and
+// no sort is needed.  In the (r desc, j asc) order a cluster is taken while
+// the keys of the clusters before it sum to less than the budget; the last
+// one taken (the crossing cluster) is the one whose predecessors hold fewer
+// than the budget's keys and which itself brings them to at least the
+// budget.  Its sort key (the ratio part of desc_key, then j) is found bit by
+// bit, each bit by one count over the wave of the keys of the clusters
+// ordered before a candidate; every cluster ordered at or before it is taken.
+constexpr int RT_SEL_CPL = 8;
+constexpr int RT_SEL_JBITS = 9;  // bits of j < 64 RT_SEL_CPL
+__global__ void __launch_bounds__(256) rt_select_wave_kernel(
+    const float* __restrict__ part, const float* __restrict__ t1c, const int32_t* __restrict__ pstart,
+    const float* __restrict__ sbar, const int32_t* __restrict__ qoff, const int32_t* __restrict__ koff,
+    const float* __restrict__ scores_in, int Cq, int Ck, int maxp, double budget,
+    const int32_t* __restrict__ row_budget, float* __restrict__ scores_out, uint8_t* __restrict__ mask) {
+  const int lane = lane_id();
+  const int bh = blockIdx.y, i = blockIdx.x * 4 + wave_id();
+  if (i >= Cq) return;  // whole waves; the kernel has no workgroup barrier
+  const int32_t* qo = qoff + (size_t)bh * (Cq + 1);
+  const int32_t* ko = koff + (size_t)bh * (Ck + 1);
+  const int mi = qo[i + 1] - qo[i];
+  uint8_t* mrow = mask + ((size_t)bh * Cq + i) * Ck;
+  float* srow = scores_out ? scores_out + ((size_t)bh * Cq + i) * Ck : nullptr;
+  if (mi == 0) {
+    for (int j = lane; j < Ck; j += SV_WAVE) {
+      mrow[j] = 0;
+      if (srow) srow[j] = 0.f;
+    }
+    return;
+  }
+  int nj[RT_SEL_CPL];
+  float r[RT_SEL_CPL];
+#pragma unroll
+  for (int e = 0; e < RT_SEL_CPL; ++e) {
+    const int j = lane + SV_WAVE * e;
+    nj[e] = j < Ck ? ko[j + 1] - ko[j] : 0;
+  }
+  if (scores_in) {
+    const float* in = scores_in + ((size_t)bh * Cq + i) * Ck;
+#pragma unroll
+    for (int e = 0; e < RT_SEL_CPL; ++e) {
+      const int j = lane + SV_WAVE * e;
+      r[e] = j < Ck ? in[j] : 0.f;
+    }
+  } else {
+    const int32_t* ps = pstart + (size_t)bh * (Ck + 1);
+    float E[RT_SEL_CPL], mu[RT_SEL_CPL], mloc = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < RT_SEL_CPL; ++e) {
+      E[e] = 0.f;
+      mu[e] = -INFINITY;
+      if (nj[e] > 0) {
+        cluster_error(part, t1c, ps, sbar, bh, i, lane + SV_WAVE * e, Cq, Ck, maxp, E[e], mu[e]);
+        mloc = fmaxf(mloc, mu[e]);
+      }
+    }
+    const float M = wave_max_f(mloc);
+#pragma unroll
+    for (int e = 0; e < RT_SEL_CPL; ++e) r[e] = nj[e] > 0 ? cluster_ratio(E[e], mu[e], M, mi, nj[e]) : 0.f;
+  }
+  uint32_t kh[RT_SEL_CPL];  // ratio part of the sort key (empty clusters weigh nothing)
+  int tot = 0;
+#pragma unroll
+  for (int e = 0; e < RT_SEL_CPL; ++e) {
+    const int j = lane + SV_WAVE * e;
+    if (srow && j < Ck) srow[j] = r[e];
+    kh[e] = (uint32_t)(desc_key(r[e], j) >> 32);
+    tot += nj[e];
+  }
+  tot = wave_sum_i(tot);
+  const double bud = row_budget ? (double)row_budget[(size_t)bh * Cq + i] : budget;
+  // a count of keys c is below the budget iff c < ceil(budget)
+  const int cap = bud > (double)tot ? tot + 1 : (int)ceil(bud);
+  uint32_t H = 0xFFFFFFFFu, L = 0xFFFFFFFFu;  // crossing cluster: all taken when every prefix is below the budget
+  bool none = cap <= 0;
+  if (!none && tot >= cap) {
+    // H: the largest ratio key whose strictly smaller keys hold < cap keys
+    H = 0;
+    for (int b = 31; b >= 0; --b) {
+      const uint32_t c = H | (1u << b);
+      int n = 0;
+#pragma unroll
+      for (int e = 0; e < RT_SEL_CPL; ++e) n += kh[e] < c ? nj[e] : 0;
+      if (wave_sum_i(n) < cap) H = c;
+    }
+    int base = 0;
+#pragma unroll
+    for (int e = 0; e < RT_SEL_CPL; ++e) base += kh[e] < H ? nj[e] : 0;
+    base = wave_sum_i(base);
+    // L: among ratio key H, the largest j whose smaller indices hold < cap - base keys
+    L = 0;
+    for (int b = RT_SEL_JBITS - 1; b >= 0; --b) {
+      const uint32_t c = L | (1u << b);
+      int n = 0;
+#pragma unroll
+      for (int e = 0; e < RT_SEL_CPL; ++e) n += (kh[e] == H && (uint32_t)(lane + SV_WAVE * e) < c) ? nj[e] : 0;
+      if (base + wave_sum_i(n) < cap) L = c;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < RT_SEL_CPL; ++e) {
+    const int j = lane + SV_WAVE * e;
+    if (j < Ck)
+      mrow[j] = (!none && nj[e] > 0 && (kh[e] < H || (kh[e] == H && (uint32_t)j <= L))) ? 1 : 0;
+  }
 }
 
 // ---------------------------------------------------------------- host side
@@ -715,6 +1152,20 @@ static size_t sel_lds(int Ck) {
   return bytes;
 }
 
+// The greedy fill: a wave per query cluster while the key clusters fit in its
+// registers, else a workgroup per query cluster with a sort in LDS.
+static void launch_select(const float* part, const float* t1c, const int32_t* ps, const float* sbar,
+                          const int32_t* q_offsets, const int32_t* k_offsets, const float* scores_in, int Cq, int Ck,
+                          int BH, int maxp, double budget, const int32_t* row_budget, float* scores_out,
+                          uint8_t* mask, hipStream_t stream) {
+  if (Ck <= SV_WAVE * RT_SEL_CPL)
+    hipLaunchKernelGGL(rt_select_wave_kernel, dim3(cdiv(Cq, 4), BH), dim3(256), 0, stream, part, t1c, ps, sbar,
+                       q_offsets, k_offsets, scores_in, Cq, Ck, maxp, budget, row_budget, scores_out, mask);
+  else
+    hipLaunchKernelGGL(rt_select_kernel, dim3(Cq, BH), dim3(256), sel_lds(Ck), stream, part, t1c, ps, sbar, q_offsets,
+                       k_offsets, scores_in, Cq, Ck, maxp, budget, row_budget, scores_out, mask);
+}
+
 static void launch_sbar(const float* q_means, const float* k_means, int BH, int Cq, int Ck, int D, float scale,
                         float* sbar, hipStream_t stream) {
   const dim3 grid(cdiv(Ck, 64), cdiv(Cq, 16), BH);
@@ -740,31 +1191,36 @@ static int cu_count() {
 
 static void launch_probe(const RtPlan& p, const float* q_means, const void* k_perm, const void* v_perm, svgear_dtype dt,
                          const float* k_means, const float* v_means, const int32_t* k_offsets, int Cq, int Ck, int BH,
-                         int N, int D, float scale, bf16* qh, bf16* ql, int32_t* ps, int4* pinfo, float* part,
-                         float* t1, float* t1c, hipStream_t stream) {
+                         int N, int D, float scale, char* w, int32_t* ps, int4* pinfo, float* part, float* t1,
+                         float* t1c, hipStream_t stream) {
+  bf16* qh = reinterpret_cast<bf16*>(w + p.off_qhi);
+  bf16* ql = reinterpret_cast<bf16*>(w + p.off_qlo);
+  const float scale2 = scale * 1.4426950408889634f;
   if (D == 128)
     hipLaunchKernelGGL((rt_prep_kernel<128>), dim3(cdiv(p.Cqp * D, 256), BH), dim3(256), 0, stream, q_means, Cq, p.Cqp,
-                       scale * 1.4426950408889634f, qh, ql);
+                       scale2, qh, ql);
   else
     hipLaunchKernelGGL((rt_prep_kernel<64>), dim3(cdiv(p.Cqp * D, 256), BH), dim3(256), 0, stream, q_means, Cq, p.Cqp,
-                       scale * 1.4426950408889634f, qh, ql);
+                       scale2, qh, ql);
   hipLaunchKernelGGL(chunk_list_kernel, dim3(BH), dim3(1024), 0, stream, k_offsets, Ck, RT_PIECE, ps);
   hipLaunchKernelGGL(rt_pieces_kernel, dim3(cdiv(Ck, 256), BH), dim3(256), 0, stream, k_offsets, ps, Ck, p.maxp,
                      pinfo);
-  // workgroups per head: about RT_PROBE_WGS over the whole launch, each
-  // streaming several pieces (never more workgroups than pieces can exist)
   // workgroups per head: about RT_PROBE_PER_CU per compute unit over the
   // whole launch (one round of resident workgroups), never more than pieces
   const int G = std::max(1, std::min(p.maxp, RT_PROBE_PER_CU * cu_count() / BH));
-#define RT_PROBE(T, DD)                                                                                            \
-  hipLaunchKernelGGL((rt_probe_kernel<T, DD>), dim3(G, BH), dim3(RT_WAVES * 64), 0, stream, (const T*)k_perm,              \
-                     (const T*)v_perm, k_means, v_means, pinfo, ps, qh, ql, N, Cq, p.Cqp, Ck, p.maxp, part, t1)
   if (dt == SVGEAR_BF16) {
-    if (D == 128) RT_PROBE(bf16, 128); else RT_PROBE(bf16, 64);
-  } else {
-    if (D == 128) RT_PROBE(float, 128); else RT_PROBE(float, 64);
-  }
+#define RT_PROBE(DD)                                                                                                 \
+  hipLaunchKernelGGL((rt_probe_bf16_kernel<DD>), dim3(G, BH), dim3(RT_WAVES * 64), 0, stream, (const bf16*)k_perm,    \
+                     (const bf16*)v_perm, k_means, v_means, pinfo, ps, qh, ql, N, Cq, p.Cqp, Ck, p.maxp, part, t1)
+    if (D == 128) RT_PROBE(128); else RT_PROBE(64);
 #undef RT_PROBE
+  } else {
+#define RT_PROBE(DD)                                                                                                 \
+  hipLaunchKernelGGL((rt_probe_kernel<float, DD>), dim3(G, BH), dim3(RT_WAVES * 64), 0, stream, (const float*)k_perm, \
+                     (const float*)v_perm, k_means, v_means, pinfo, ps, qh, ql, N, Cq, p.Cqp, Ck, p.maxp, part, t1)
+    if (D == 128) RT_PROBE(128); else RT_PROBE(64);
+#undef RT_PROBE
+  }
   hipLaunchKernelGGL(rt_t1_kernel, dim3(cdiv(Ck, 256), BH), dim3(256), 0, stream, t1, ps, Ck, p.maxp, t1c);
 }
 
@@ -796,8 +1252,6 @@ extern "C" svgear_status svgear_route(const float* q_means, const int32_t* q_off
   st = check_ws("route", ws, ws_bytes, p.total);
   if (st != SVGEAR_OK) return st;
   char* w = static_cast<char*>(ws);
-  bf16* qh = reinterpret_cast<bf16*>(w + p.off_qhi);
-  bf16* ql = reinterpret_cast<bf16*>(w + p.off_qlo);
   float* sbar = reinterpret_cast<float*>(w + p.off_sbar);
   int32_t* ps = reinterpret_cast<int32_t*>(w + p.off_ps);
   int4* pinfo = reinterpret_cast<int4*>(w + p.off_pinfo);
@@ -807,11 +1261,11 @@ extern "C" svgear_status svgear_route(const float* q_means, const int32_t* q_off
   const double budget = (double)density * (double)N;
   if (!scores_in) {
     launch_sbar(q_means, k_means, B * H, Cq, Ck, D, scale, sbar, stream);
-    launch_probe(p, q_means, k_perm, v_perm, dt, k_means, v_means, k_offsets, Cq, Ck, B * H, N, D, scale, qh, ql, ps,
+    launch_probe(p, q_means, k_perm, v_perm, dt, k_means, v_means, k_offsets, Cq, Ck, B * H, N, D, scale, w, ps,
                  pinfo, part, t1, t1c, stream);
   }
-  hipLaunchKernelGGL(rt_select_kernel, dim3(Cq, B * H), dim3(256), sel_lds(Ck), stream, part, t1c, ps, sbar, q_offsets,
-                     k_offsets, scores_in, Cq, Ck, p.maxp, budget, nullptr, scores_out, mask);
+  launch_select(part, t1c, ps, sbar, q_offsets, k_offsets, scores_in, Cq, Ck, B * H, p.maxp, budget, nullptr,
+                scores_out, mask, stream);
   return check_launch("svgear_route");
 }
 
@@ -843,8 +1297,6 @@ extern "C" svgear_status svgear_route_topp(const float* q_means, const int32_t* 
   st = check_ws("route_topp", ws, ws_bytes, p.total);
   if (st != SVGEAR_OK) return st;
   char* w = static_cast<char*>(ws);
-  bf16* qh = reinterpret_cast<bf16*>(w + p.off_qhi);
-  bf16* ql = reinterpret_cast<bf16*>(w + p.off_qlo);
   float* sbar = reinterpret_cast<float*>(w + p.off_sbar);
   int32_t* ps = reinterpret_cast<int32_t*>(w + p.off_ps);
   int4* pinfo = reinterpret_cast<int4*>(w + p.off_pinfo);
@@ -858,10 +1310,10 @@ extern "C" svgear_status svgear_route_topp(const float* q_means, const int32_t* 
                      q_offsets, k_offsets, Cq, Ck, (double)top_p, probs_out, bud, error_ranked ? nullptr : mask);
   if (error_ranked) {
     if (need_probe)
-      launch_probe(p, q_means, k_perm, v_perm, dt, k_means, v_means, k_offsets, Cq, Ck, BH, N, D, scale, qh, ql, ps,
+      launch_probe(p, q_means, k_perm, v_perm, dt, k_means, v_means, k_offsets, Cq, Ck, BH, N, D, scale, w, ps,
                    pinfo, part, t1, t1c, stream);
-    hipLaunchKernelGGL(rt_select_kernel, dim3(Cq, BH), dim3(256), sel_lds(Ck), stream, part, t1c, ps, sbar, q_offsets, k_offsets,
-                       scores_in, Cq, Ck, p.maxp, 0.0, bud, scores_out, mask);
+    launch_select(part, t1c, ps, sbar, q_offsets, k_offsets, scores_in, Cq, Ck, BH, p.maxp, 0.0, bud, scores_out, mask,
+                  stream);
   }
   return check_launch("svgear_route_topp");
 }

@@ -319,6 +319,41 @@ def test_route_select_ties_and_empty(sv):
     np.testing.assert_array_equal(mask, orc.select(r[0, 0], np.diff(oq[0, 0]), np.diff(ok[0, 0]), 0.5, N))
 
 
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 128)])
+def test_route_degenerate_key_clusters_exact(sv, dtype, D):
+    """Key clusters whose members all equal their mean (singletons, clusters of
+    identical rows) lose nothing to compensation: e_ij = 0 for every query
+    cluster (FrontierCS blog, probe paragraph: the error of a block is the
+    gap between its centroid's stand-in and its keys).  The GPU's ratios for
+    them are exactly 0 (the oracle's are 0 up to fp64 rounding of its two
+    score products), and every other ratio matches the oracle."""
+    rng = np.random.default_rng(7 + D)
+    sizes = [1] * 5 + [3, 7, 16, 33, 40] + [int(n) for n in rng.integers(2, 60, 10)]
+    ok = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    N, Ck, Cq = int(ok[-1]), len(sizes), 5
+    rnd = lambda a: host(to_dev(a, dtype)).astype(np.float64)  # values exact in the input dtype
+    K = rng.standard_normal((N, D)) + 2.0 * rng.standard_normal(D)
+    V = rng.standard_normal((N, D)) + 2.0 * rng.standard_normal(D)
+    for j in range(5, 10):
+        K[ok[j]:ok[j + 1]] = K[ok[j]]
+        V[ok[j]:ok[j + 1]] = V[ok[j]]
+    K, V = rnd(K), rnd(V)
+    ident = np.arange(N)
+    kbar, vbar = orc.means(K, ident, ok), orc.means(V, ident, ok)
+    qbar = 1.5 * rng.standard_normal((Cq, D))
+    oq = np.linspace(0, N, Cq + 1).astype(np.int32)
+    sc = 1.0 / np.sqrt(D)
+    r4 = lambda a: a.reshape(1, 1, *a.shape)
+    scores, mask = sv.route(f32(r4(qbar)), i32(r4(oq)), to_dev(r4(K), dtype), to_dev(r4(V), dtype), f32(r4(kbar)),
+                            f32(r4(vbar)), i32(r4(ok)), sc, 0.3)
+    scores = host(scores)[0, 0].astype(np.float64)
+    r_o, _ = orc.route(qbar, oq, K, V, kbar, vbar, ok, sc, 0.3)
+    rowmax = r_o.max(axis=1, keepdims=True)
+    assert (r_o[:, :10] <= 1e-20 * rowmax).all()
+    assert (scores[:, :10] == 0).all(), scores[:, :10]
+    assert (np.abs(scores - r_o) <= 2e-3 * r_o + 1e-7 * rowmax + 1e-37).all()
+
+
 # ------------------------------------------------------------------ attention
 def attn_inputs(w, x, outs, mask=None):
     BH = w.B * w.H
