@@ -411,6 +411,28 @@ __global__ void __launch_bounds__(RT_WAVES * 64) __attribute__((amdgpu_waves_per
   }
 }
 
+// Exact split v = hi + mid + lo into bfloat16 (v - hi and v - hi - mid are
+// exact in fp32; the last remainder has at most 8 significant bits).
+__device__ __forceinline__ void split3_bf16(float v, bf16& hi, bf16& mid, bf16& lo) {
+  hi = (bf16)v;
+  const float r1 = v - (float)hi;
+  mid = (bf16)r1;
+  lo = (bf16)(r1 - (float)mid);
+}
+// Two bf16 in a 32-bit word (element 0 in the low half), their doubles (exact),
+// and a . b + c over the pair with exact products (v_dot2_f32_bf16).
+__device__ __forceinline__ uint32_t pack_bf2(bf16 a, bf16 b) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+__device__ __forceinline__ uint32_t twice_bf2(uint32_t p) {
+  const bf16 a = (bf16)(2.f * __uint_as_float(p << 16)), b = (bf16)(2.f * __uint_as_float(p & 0xFFFF0000u));
+  return pack_bf2(a, b);
+}
+typedef __bf16 rt_bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(rt_bf16x2, a), __builtin_bit_cast(rt_bf16x2, b), c, false);
+}
+
 // The probe for bfloat16 keys, without centring.  A bf16 key is exact, so the
 // two 16x16x32 products of a key against the hi and lo planes of scale *
 // log2(e) * q_bar give s_k = q2 . k (q2 = hi + lo, within 2^-17 of q_bar per
@@ -453,11 +475,14 @@ __global__ void __launch_bounds__(RT_WAVES * 64) __attribute__((amdgpu_waves_per
   __shared__ __attribute__((aligned(1024))) char sKx[TL::SLOTS < NT ? 16 * (NT - TL::SLOTS) : 16];
   __shared__ __attribute__((aligned(16))) float sW[2][32];
   __shared__ __attribute__((aligned(16))) float sVV[2][32];
-  __shared__ __attribute__((aligned(16))) float sVm[RT_PPW][D];  // v_bar of each piece's cluster
-  __shared__ float sVbsq[RT_PPW][16];                            // ||v_bar||^2 over each thread segment
+  // v_bar of each piece's cluster as an exact three-piece bf16 split (hi, mid,
+  // lo planes of coordinate pairs), and ||v_bar||^2 over each thread segment
+  __shared__ __attribute__((aligned(16))) uint32_t sVp[RT_PPW][3][D / 2];
+  __shared__ float sVbsq[RT_PPW][16];
   __shared__ float sSb[RT_WAVES][RT_PPW][16];                    // s'_j of each piece, per wave query column
   __shared__ int4 sInfo[RT_PPW];
-  __shared__ int2 sStream[RT_PPW * (RT_PIECE / 32)];
+  // sub-tile s: (piece slot, first row, the piece's last row, 1 if the piece's last sub-tile)
+  __shared__ int4 sStream[RT_PPW * (RT_PIECE / 32)];
   __shared__ int sNsub;
 
   const int bh = blockIdx.y, tid = threadIdx.x, lane = lane_id();
@@ -491,7 +516,19 @@ __global__ void __launch_bounds__(RT_WAVES * 64) __attribute__((amdgpu_waves_per
 #pragma unroll
     for (int u = 0; u < MSLOTS; ++u) {
       const int v = tid + NT * u, k = v / (D / 4), o = (v % (D / 4)) * 4;
-      if (k < npc) *reinterpret_cast<f32x4*>(&sVm[k][o]) = mv[u];
+      if (k < npc) {
+        uint32_t pc[3][2];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          bf16 a[3], c[3];
+          split3_bf16(mv[u][2 * t], a[0], a[1], a[2]);
+          split3_bf16(mv[u][2 * t + 1], c[0], c[1], c[2]);
+#pragma unroll
+          for (int pl = 0; pl < 3; ++pl) pc[pl][t] = pack_bf2(a[pl], c[pl]);
+        }
+#pragma unroll
+        for (int pl = 0; pl < 3; ++pl) *reinterpret_cast<uint2*>(&sVp[k][pl][o / 2]) = make_uint2(pc[pl][0], pc[pl][1]);
+      }
     }
   }
   if (w == 0) {
@@ -504,15 +541,25 @@ __global__ void __launch_bounds__(RT_WAVES * 64) __attribute__((amdgpu_waves_per
       if (lane >= o) x += y;
     }
     const int base = x - ns;
-    for (int u = 0; u < ns; ++u) sStream[base + u] = make_int2(lane, in.y + 32 * u);
+    for (int u = 0; u < ns; ++u) sStream[base + u] = make_int4(lane, in.y + 32 * u, in.z - 1, u == ns - 1);
     if (lane == SV_WAVE - 1) sNsub = x;
   }
   __syncthreads();
+  // ||v_bar||^2 = sum of hi^2 + 2 hi mid + 2 hi lo + mid^2 (the dropped terms
+  // are below 2^-24 relative), in the pair order of the per-key products
+  // below, so that for a v_bar exact in bf16 (mid = lo = 0) it repeats ||v||^2's
+  // sequence of products exactly
   for (int u = tid; u < npc * 16; u += NT) {
     const int k = u >> 4, sg = u & 15;
     float t = 0.f;
 #pragma unroll
-    for (int e = 0; e < DPT; ++e) t = fmaf(sVm[k][sg * DPT + e], sVm[k][sg * DPT + e], t);
+    for (int q = 0; q < DPT / 2; ++q) {
+      const uint32_t h = sVp[k][0][sg * DPT / 2 + q], m = sVp[k][1][sg * DPT / 2 + q], l = sVp[k][2][sg * DPT / 2 + q];
+      t = dot2_bf16(h, h, t);
+      t = dot2_bf16(h, twice_bf2(m), t);
+      t = dot2_bf16(h, twice_bf2(l), t);
+      t = dot2_bf16(m, m, t);
+    }
     sVbsq[k][sg] = t;
   }
   __syncthreads();
@@ -524,15 +571,15 @@ __global__ void __launch_bounds__(RT_WAVES * 64) __attribute__((amdgpu_waves_per
   // statistics are not used), so that the loads in flight are the same on
   // every path and the waits for them stay partial.
   auto kload = [&](int s, char* kt) {
-    const int2 st = sStream[min(s, nsub - 1)];
-    const int g = min(st.y + kq, sInfo[st.x].z - 1);
+    const int4 st = sStream[min(s, nsub - 1)];
+    const int g = min(st.y + kq, st.z);
     char* dst = tid < TL::SLOTS ? kt + 1024 * w : sKx + 1024 * (w - TL::SLOTS / 64);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rK, (__attribute__((address_space(3))) void*)dst, 16,
                                              (int)((uint32_t)g * TL::ROWB + kc * 16), 0, 0, 0);
   };
   auto fetch = [&](int s, RtSeg<bf16, DPT>& rv) {
-    const int2 st = sStream[min(s, nsub - 1)];
-    rv.load(vb + (size_t)min(st.y + kr, sInfo[st.x].z - 1) * D + d0);
+    const int4 st = sStream[min(s, nsub - 1)];
+    rv.load(vb + (size_t)min(st.y + kr, st.z) * D + d0);
   };
 
   for (int qb = 0; qb < Cqp; qb += QW) {
@@ -600,21 +647,25 @@ __global__ void __launch_bounds__(RT_WAVES * 64) __attribute__((amdgpu_waves_per
 
     auto step = [&](int s, auto bc) {
       constexpr int b = decltype(bc)::value;
-      const int2 st = sStream[s];
+      const int4 st = sStream[s];
       const int k = st.x;
       {
-        const bool ok = st.y + kr < sInfo[k].z;
+        const bool ok = st.y + kr <= st.z;
         float bvp = 0.f, vvp = 0.f;
         if (ok) {
+          // v_bar . v and ||v||^2 from exact bf16 pair products: a key equal
+          // to its (bf16-exact) mean gives bvp = vvp = ||v_bar||^2 bit for bit
+          typedef __attribute__((__vector_size__(DPT * 2))) uint32_t pv_t;
+          const pv_t hv = *reinterpret_cast<const pv_t*>(&sVp[k][0][d0 / 2]);
+          const pv_t mv = *reinterpret_cast<const pv_t*>(&sVp[k][1][d0 / 2]);
+          const pv_t lv = *reinterpret_cast<const pv_t*>(&sVp[k][2][d0 / 2]);
 #pragma unroll
-          for (int e0 = 0; e0 < DPT; e0 += 4) {
-            const f32x4 vb4 = *reinterpret_cast<const f32x4*>(&sVm[k][d0 + e0]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float vf = rv[b].at(e0 + e);
-              bvp = fmaf(vb4[e], vf, bvp);
-              vvp = fmaf(vf, vf, vvp);
-            }
+          for (int q = 0; q < DPT / 2; ++q) {
+            const uint32_t v2 = rv[b].v[q];
+            bvp = dot2_bf16(hv[q], v2, bvp);
+            bvp = dot2_bf16(mv[q], v2, bvp);
+            bvp = dot2_bf16(lv[q], v2, bvp);
+            vvp = dot2_bf16(v2, v2, vvp);
           }
           t1acc += sVbsq[k][seg] - 2.f * bvp + vvp;
         }
@@ -672,7 +723,7 @@ __global__ void __launch_bounds__(RT_WAVES * 64) __attribute__((amdgpu_waves_per
         s2 += t2;
         s3 += t3;
       }
-      if (s + 1 == nsub || sStream[s + 1].x != k) {
+      if (st.w) {
         const int pc = bx + (kb0 + k) * G;
         if (has_q) {
 #pragma unroll
