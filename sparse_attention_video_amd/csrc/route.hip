@@ -113,7 +113,8 @@ __global__ void __launch_bounds__(256) rt_pieces_kernel(const int32_t* __restric
   for (int pc = ps[j], r0 = lo; r0 < hi; ++pc, r0 += RT_PIECE) out[pc] = make_int4(j, r0, min(r0 + RT_PIECE, hi), 0);
 }
 
-// The probe.  A workgroup of RT_WAVES waves streams the pieces pc =
+// The probe for fp32 keys (bf16 keys take rt_probe_bf16_kernel below, which
+// needs no centring).  A workgroup of RT_WAVES waves streams the pieces pc =
 // blockIdx.x, blockIdx.x + gridDim.x, ... of one head, 32 keys (a sub-tile)
 // at a time; wave w owns query clusters 16 (RT_WAVES pass + w) .. + 15, whose
 // q_bar (hi and lo) it keeps in registers as the B operand of 16x16x32
