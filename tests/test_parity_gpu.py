@@ -319,6 +319,37 @@ def test_route_select_ties_and_empty(sv):
     np.testing.assert_array_equal(mask, orc.select(r[0, 0], np.diff(oq[0, 0]), np.diff(ok[0, 0]), 0.5, N))
 
 
+@pytest.mark.parametrize("Ck", [1, 63, 64, 65, 512, 513])
+def test_route_select_given_ratios_both_fill_kernels(sv, Ck):
+    """The greedy fill (FrontierCS blog, budget paragraph: clusters by ratio,
+    keys until the budget) from given float32 ratios, bit-exact against the
+    oracle on both fill kernels (a wave per query cluster while C_k <= 512, a
+    sorting workgroup beyond): tied and zero ratios, empty key and query
+    clusters, budgets from none to all."""
+    rng = np.random.default_rng(Ck)
+    Cq, B, H = 7, 1, 2
+    ksz = rng.integers(0, 40, (B * H, Ck)) * (rng.random((B * H, Ck)) > 0.15)
+    ksz[:, 0] = np.maximum(ksz[:, 0], 1)
+    N = int(ksz.sum(axis=1).max()) + 5
+    ksz[:, -1] += N - ksz.sum(axis=1)  # every head's sizes sum to N
+    ok = np.concatenate([np.zeros((B * H, 1), np.int64), np.cumsum(ksz, axis=1)], axis=1)
+    qsz = np.stack([np.diff(np.sort(np.concatenate([[0, N], rng.integers(0, N + 1, Cq - 1)]))) for _ in range(B * H)])
+    qsz[:, 2] = 0
+    qsz[:, 3] += N - qsz.sum(axis=1)
+    oq = np.concatenate([np.zeros((B * H, 1), np.int64), np.cumsum(qsz, axis=1)], axis=1)
+    r = rng.random((B * H, Cq, Ck)).astype(np.float32)
+    r[:, 0] = np.round(r[:, 0] * 4) / 4         # many ties
+    r[:, 1] = 0.0                                # all tied at zero
+    r[:, 4, : Ck // 2] = r[:, 4, Ck // 2:][:, : Ck // 2] if Ck > 1 else r[:, 4, :1]
+    kp = torch.zeros((B, H, N, 64), dtype=torch.float32, device="cuda")
+    for dens in (1e-9, 0.05, 0.3, 0.999, 1.0):
+        _, mask = sv.route(None, i32(oq.reshape(B, H, -1)), kp, None, None, None, i32(ok.reshape(B, H, -1)), 0.125,
+                           dens, scores_in=f32(r.reshape(B, H, Cq, Ck)))
+        mask = host(mask).reshape(B * H, Cq, Ck)
+        for h in range(B * H):
+            np.testing.assert_array_equal(mask[h], orc.select(r[h], qsz[h], ksz[h], dens, N), err_msg=f"density {dens}")
+
+
 @pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 64), ("f32", 128)])
 def test_route_degenerate_key_clusters_exact(sv, dtype, D):
     """Key clusters whose members all equal their mean (singletons, clusters of
