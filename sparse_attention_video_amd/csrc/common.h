@@ -21,7 +21,7 @@ __device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
 __device__ __forceinline__ float to_f32(float x) { return x; }
 __device__ __forceinline__ bf16 to_bf16(float x) { return (bf16)x; }  // round to nearest even
 
-// Split v = hi + lo + r with hi, lo bfloat16 and |r| <= 2^-18 |v| (v - hi is exact in fp32).
+// Split v = hi + lo + r with hi, lo bfloat16 and |r| <= 2^-17 |v| (v - hi is exact in fp32).
 __device__ __forceinline__ void split_bf16(float v, bf16& hi, bf16& lo) {
   hi = (bf16)v;
   lo = (bf16)(v - (float)hi);

@@ -22,6 +22,9 @@ namespace svg {
 
 constexpr int KM_EXTRA = 16;        // extra K slots of the distance GEMM (norms, offset)
 constexpr int KM_TOK_WG = 256;      // tokens per assign workgroup (4 waves x 64)
+// candidate pruning of the tracking rounds pays from a few hundred centroids
+// on (its bound matrix is C x C per head)
+constexpr int KM_PRUNE_MIN_C = 256, KM_PRUNE_MAX_C = 1024;
 constexpr int SORT_TILE = 4096;     // tokens per histogram / scatter tile
 constexpr int MEAN_ROWS = 256;      // rows per segment-sum chunk
 constexpr float PAD_NORM = 1e30f;   // squared norm given to padding centroids
@@ -53,7 +56,7 @@ inline __host__ __device__ int km_mcap(int N) {
 template <int D>
 __global__ void __launch_bounds__(256) km_prep_kernel(const float* __restrict__ cent, int C, int Cpad,
                                                       bf16* __restrict__ ops, uint32_t* __restrict__ nmax,
-                                                      int32_t* __restrict__ mtot) {
+                                                      int32_t* __restrict__ mtot, float* __restrict__ cnorm) {
   constexpr int EPL = D / SV_WAVE;  // elements per lane
   constexpr int RW = km_row<D>();
   __shared__ double s_max[4];
@@ -88,6 +91,7 @@ __global__ void __launch_bounds__(256) km_prep_kernel(const float* __restrict__ 
     }
     cc = wave_sum_d(cc);
     if (c < C) wmax = fmax(wmax, cc);
+    if (cnorm && lane == 0 && c < C) cnorm[(size_t)bh * Cpad + c] = (float)cc;  // ||c||^2 (fp64 sum, rounded once)
     if (lane < KM_EXTRA) {
       const float n = c < C ? (float)cc : PAD_NORM;
       const bf16 n_hi = (bf16)n;
@@ -113,6 +117,60 @@ __global__ void __launch_bounds__(256) km_prep_kernel(const float* __restrict__ 
 }
 
 // --------------------------------------------------------------------------
+// Lower bounds on squared centroid distances, lb[a][c] <= ||c_a - c_c||^2, for
+// the candidate pruning of the tracking rounds (Elkan's triangle-inequality
+// bound: a centroid c with ||c_a - c_c|| > 2 ||x - c_a|| is strictly farther
+// from x than c_a, so x's label cannot move to it).  A wave takes a 32 x 32
+// tile from the prep operand rows (-2c split hi/lo in bf16): P = Ah.Ch +
+// Ah.Cl + Al.Ch estimates 4 c_a.c_c, and P / 2 is within 5.4e-5 (n_a + n_c)
+// of 2 c_a.c_c (split remainders below 2^-17 of each element and the dropped
+// lo.lo product, 2^-15 per element; fp32 sums of 3 D products, 2.3e-5; n =
+// ||c||^2 from fp64 sums rounded once), so lb = n_a + n_c - P / 2 - 1e-4
+// (n_a + n_c).
+// --------------------------------------------------------------------------
+template <int D>
+__global__ void __launch_bounds__(256) km_cc_kernel(const bf16* __restrict__ ops, const float* __restrict__ cnorm,
+                                                    int C, int Cpad, float* __restrict__ lb) {
+  constexpr int RW = km_row<D>(), KS = D / 16;
+  const int bh = blockIdx.y, lane = lane_id(), w = wave_id();
+  const int nt = Cpad / 32, tile = blockIdx.x * 4 + w;
+  if (tile >= nt * nt) return;
+  const int a0 = (tile / nt) * 32, c0 = (tile % nt) * 32;
+  const int half = lane >> 5, col = lane & 31;
+  const bf16* ob = ops + (size_t)bh * Cpad * RW + 8 * half;
+  const bf16* ra = ob + (size_t)(a0 + col) * RW;
+  const bf16* rc = ob + (size_t)(c0 + col) * RW;
+  bf16x8 ah[KS], al[KS], ch[KS], cl[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    ah[ks] = *reinterpret_cast<const bf16x8*>(ra + 16 * ks);
+    al[ks] = *reinterpret_cast<const bf16x8*>(ra + D + KM_EXTRA + 16 * ks);
+    ch[ks] = *reinterpret_cast<const bf16x8*>(rc + 16 * ks);
+    cl[ks] = *reinterpret_cast<const bf16x8*>(rc + D + KM_EXTRA + 16 * ks);
+  }
+  f32x16 acc = {};
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    acc = mfma_bf16(ah[ks], ch[ks], acc);
+    acc = mfma_bf16(ah[ks], cl[ks], acc);
+    acc = mfma_bf16(al[ks], ch[ks], acc);
+  }
+  // lane: column c = c0 + col, rows a = a0 + c_row(r, half)
+  const float* nb = cnorm + (size_t)bh * Cpad;
+  const int c = c0 + col;
+  if (c >= C) return;
+  const float nc = nb[c];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int a = a0 + c_row(r, half);
+    if (a < C) {
+      const float sn = nb[a] + nc;
+      lb[((size_t)bh * C + a) * C + c] = sn - 0.5f * acc[r] - 1e-4f * sn;
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
 // assign: label[n] = argmin_c ||x_n - c||^2 (ties to the lowest index).
 //
 // Each wave owns 64 tokens as two 32-token MFMA B tiles held in registers;
@@ -129,13 +187,24 @@ __global__ void __launch_bounds__(256) km_prep_kernel(const float* __restrict__ 
 //   else                     -> exact fp64 scan of every centroid
 // The exact distances are summed by a fixed 64-lane butterfly.
 // --------------------------------------------------------------------------
-template <typename T, int D>
+//
+// PRUNE (tracking rounds, bf16): the workgroup takes 256 consecutive tokens of
+// the order sorted by their current labels (perm), and only the centroids
+// that can still be nearest to one of them: with R_a the largest distance
+// of the workgroup's tokens of label a to c_a (an fp32 upper bound), c stays
+// a candidate iff lb[a][c] <= 4 R_a^2 for some label a present; every other
+// centroid is strictly farther from each such token than its c_a.  The list
+// of candidates (ascending, in LDS) replaces 0 .. C-1: chunk rows are
+// gathered from it and keys carry list positions, mapped back at the end.
+template <typename T, int D, bool PRUNE = false>
 __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) km_assign_kernel(const T* __restrict__ x, const bf16* __restrict__ ops,
                                                         const uint32_t* __restrict__ nmax,
                                                         const float* __restrict__ cent, int N, int C, int Cpad, int ib,
                                                         int32_t* __restrict__ labels, int2* __restrict__ moved,
-                                                        int32_t* __restrict__ mtot, uint32_t* __restrict__ r2max) {
+                                                        int32_t* __restrict__ mtot, uint32_t* __restrict__ r2max,
+                                                        const int32_t* __restrict__ perm, const float* __restrict__ lb) {
   constexpr bool F32 = sizeof(T) == 4;
+  static_assert(!(PRUNE && F32), "candidate pruning is built for bf16 tokens");
   constexpr int KS = D / 16;
   constexpr int RW = km_row<D>();          // operand row (bf16 elements)
   constexpr int SR = RW + 8;               // LDS row stride: an odd multiple of 16 bytes
@@ -159,11 +228,17 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) 
   bf16x8 bext[2];
   float xx[2];
   int lold[2];  // previous labels (tracking rounds), loaded with the rows
+  int tokn[2];  // token index of this lane's column of tile t (N: none)
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const int n = tok0 + 32 * t + col;
+    const int pos = tok0 + 32 * t + col;
+    tokn[t] = pos < N ? (PRUNE ? perm[(size_t)bh * N + pos] : pos) : N;
+  }
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int n = tokn[t];
     const bool ok = n < N;
-    lold[t] = (moved && ok && half == 0) ? labels[(size_t)bh * N + n] : -1;
+    lold[t] = (moved && ok && (PRUNE || half == 0)) ? labels[(size_t)bh * N + n] : -1;
     float part = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -231,13 +306,66 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) 
   }
   const __amdgpu_buffer_rsrc_t rops =
       __builtin_amdgcn_make_buffer_rsrc((void*)ob, (short)0, Cpad * RW * 2, 0x00020000);
+  // candidate list (PRUNE): positions 0 .. nlist-1 hold centroid indices
+  // (chunk 0 reserves 32 positions for the own labels, so a list holds up
+  // to C + 31 positions; the caller's ib covers them)
+  __shared__ int s_cand[PRUNE ? KM_PRUNE_MAX_C + 32 : 1];
+  __shared__ uint32_t s_r2[PRUNE ? KM_TOK_WG : 1];
+  __shared__ int s_pos[PRUNE ? 64 : 1];
+  __shared__ int s_cnt[4];
+  __shared__ int s_cnt4[PRUNE ? KM_PRUNE_MAX_C / 256 : 1][4];
+  int nlist = C, nfirst = 0, a_lo = 0, a_hi = 0;
+  if constexpr (PRUNE) {
+    // labels of the workgroup's tokens span a_lo .. a_hi (sorted order)
+    const int p0 = blockIdx.x * KM_TOK_WG, p1 = min(N, p0 + KM_TOK_WG) - 1;
+    a_lo = labels[(size_t)bh * N + perm[(size_t)bh * N + p0]];
+    a_hi = labels[(size_t)bh * N + perm[(size_t)bh * N + p1]];
+    const bool narrow = a_hi - a_lo < 64;
+    s_r2[tid] = 0u;
+    __syncthreads();
+    if (narrow && half == 0)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        if (tokn[t] < N) s_r2[lold[t] - a_lo] = 1u;  // present labels
+    __syncthreads();
+    if (narrow && w == 0) {
+      // chunk 0 = the present labels, ascending; s_pos: label -> position
+      const bool pres = s_r2[lane] != 0u;
+      const uint64_t bal = ballot(pres);
+      const int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+      if (pres) s_cand[pos] = a_lo + lane;
+      s_pos[lane] = pos;
+      if (lane == 0) s_cnt[0] = __popcll(bal);
+    }
+    __syncthreads();
+    const int k = narrow ? s_cnt[0] : 33;
+    if (k <= 32) {
+      nfirst = k;
+      nlist = 32;  // chunk 0 for now; the other candidates follow its products
+      for (int q = k + tid; q < 32; q += 256) s_cand[q] = s_cand[0];
+    } else {
+      // no pruning for this workgroup: every centroid, in order
+      for (int c = tid; c < C; c += 256) s_cand[c] = c;
+      for (int q = C + tid; q < ((C + 31) & ~31); q += 256) s_cand[q] = s_cand[0];
+    }
+    __syncthreads();
+  }
   auto stage = [&](int c0, int buf) {
 #pragma unroll
     for (int k = 0; k < NJW; ++k)
-      if (4 * k + w < NJ)
+      if (4 * k + w < NJ) {
+        uint32_t go = goff[k];
+        int so = c0 * RW * 2;
+        if constexpr (PRUNE) {
+          // row r of the chunk is candidate c0 + r (pad bytes: its row start)
+          const int o = 1024 * (4 * k + w) + 16 * lane;
+          const int r = min(o / (2 * SR), 31), cb2 = o - r * (2 * SR);
+          go = (uint32_t)s_cand[c0 + r] * (uint32_t)(RW * 2) + (uint32_t)((o < CHB && cb2 < 2 * RW) ? cb2 : 0);
+          so = 0;
+        }
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rops, (__attribute__((address_space(3))) void*)(&s_ops[buf][512 * (4 * k + w)]), 16, (int)goff[k],
-            c0 * RW * 2, 0, 0);
+            rops, (__attribute__((address_space(3))) void*)(&s_ops[buf][512 * (4 * k + w)]), 16, (int)go, so, 0, 0);
+      }
   };
   // this wave's staging loads have landed (vector-memory count 0; the export
   // and LDS counts left at their maxima)
@@ -248,7 +376,6 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) 
   const float s_split = F32 ? 3.01f : 1.0f;
   const int kprod = D * (F32 ? 3 : 2) + KM_EXTRA;
   const float gam = (kprod * u) / (1.f - kprod * u);
-  const int nchunk = Cpad / 32;
   stage(0, 0);
   staged();
   __syncthreads();
@@ -340,12 +467,110 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) 
       key[1][0] = minkey(key[1][0], k1);
     }
   };
-  for (int ci = 0; ci < nchunk; ++ci) {
+  int ci0 = 0;
+  if constexpr (PRUNE) {
+    if (nfirst > 0) {
+      // chunk 0 holds the workgroup's own labels: each token's estimate V of
+      // ||x - c_a||^2 + off (a in chunk 0) bounds its distance to its own
+      // centroid, ||x - c_a||^2 <= V - off + 2 E0 (+ the rounding of ||x||^2
+      // and its split, below 3e-5 ||x||^2)
+      f32x16 acc0, acc1;
+      mma(0, acc0, acc1);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const f32x16& acc = t ? acc1 : acc0;
+        const int p = tokn[t] < N ? s_pos[lold[t] - a_lo] : 0;
+        const int hp = (p >> 2) & 1, rs = ((p >> 3) << 2) | (p & 3);
+        float v = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v = r == rs ? acc[r] : v;
+        const float vo = shfl_xor(v, 32);
+        const float V = half == hp ? v : vo;
+        const float offb = (float)(bf16)off[t];
+        const float u2 = fmaxf(0.f, V - offb + 2.f * E0[t] + 3e-5f * xx[t]) * (1.f + 1e-5f);
+        // (bit pattern + 1: present labels stay nonzero even at distance 0)
+        if (half == 0 && tokn[t] < N) atomicMax(&s_r2[lold[t] - a_lo], __float_as_uint(u2) + 1u);
+      }
+      __syncthreads();
+      // the other candidates, ascending, from position 32: thread tid tests
+      // centroids tid + 256 u against the own labels, 4 labels' bound loads
+      // in flight at a time
+      constexpr int CPT = KM_PRUNE_MAX_C / 256;
+      bool keep[CPT];
+#pragma unroll
+      for (int u = 0; u < CPT; ++u) keep[u] = false;
+      for (int i0 = 0; i0 < nfirst; i0 += 4) {
+        float thr[4];
+        const float* lrow[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int a = s_cand[i0 + jj < nfirst ? i0 + jj : 0];
+          thr[jj] = i0 + jj < nfirst ? 4.f * __uint_as_float(s_r2[a - a_lo] - 1u) * (1.f + 3e-5f) : -1.f;
+          lrow[jj] = lb + ((size_t)bh * C + a) * C;
+        }
+        float lv[4][CPT];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+          for (int u = 0; u < CPT; ++u) lv[jj][u] = lrow[jj][min(tid + 256 * u, C - 1)];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+#pragma unroll
+          for (int u = 0; u < CPT; ++u) keep[u] = keep[u] || lv[jj][u] <= thr[jj];
+      }
+      uint64_t bal[CPT];
+#pragma unroll
+      for (int u = 0; u < CPT; ++u) {
+        const int c = tid + 256 * u;
+        // (the own labels are already in chunk 0)
+        keep[u] = keep[u] && c < C && !(c >= a_lo && c <= a_hi && s_r2[c - a_lo] != 0u);
+        bal[u] = ballot(keep[u]);
+        if (lane == 0) s_cnt4[u][w] = __popcll(bal[u]);
+      }
+      __syncthreads();
+      int base = 32;
+#pragma unroll
+      for (int u = 0; u < CPT; ++u) {
+        int o = base;
+        for (int v = 0; v < w; ++v) o += s_cnt4[u][v];
+        if (keep[u])
+          s_cand[o + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal[u] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal[u], 0))] =
+              tid + 256 * u;
+        base += s_cnt4[u][0] + s_cnt4[u][1] + s_cnt4[u][2] + s_cnt4[u][3];
+      }
+      nlist = base;
+      for (int q = nlist + tid; q < ((nlist + 31) & ~31); q += 256) s_cand[q] = s_cand[0];
+      __syncthreads();
+      if (nlist > 32) stage(32, 1);
+      // chunk 0's keys; its positions past the own labels are padding
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (c_row(r, half) >= nfirst) {
+          acc0[r] = FLT_MAX;
+          acc1[r] = FLT_MAX;
+        }
+      keys(0, acc0, acc1);
+      if (nlist > 32) staged();
+      __syncthreads();
+      ci0 = 1;
+    }
+  }
+  const int nchunk = PRUNE ? (nlist + 31) / 32 : Cpad / 32;
+  for (int ci = ci0; ci < nchunk; ++ci) {
     const int buf = ci & 1;
     const bool more = ci + 1 < nchunk;
     if (more) stage((ci + 1) * 32, buf ^ 1);
     f32x16 acc0, acc1;
     mma(buf, acc0, acc1);
+    if (PRUNE && ci * 32 + 32 > nlist) {
+      // list positions past the last candidate (padding) never enter a list
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (ci * 32 + c_row(r, half) >= nlist) {
+          acc0[r] = FLT_MAX;
+          acc1[r] = FLT_MAX;
+        }
+    }
     keys(ci * 32, acc0, acc1);
     if (more) staged();
     __syncthreads();
@@ -373,6 +598,7 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) 
     const float k1v = key[t][0];
     const float W = 2.f * E0[t] + q * (2.f * k1v + 2.f * E0[t] + 1.f) * 2.5f;
     lab[t] = (int)(__float_as_uint(k1v) & imask);
+    if constexpr (PRUNE) lab[t] = s_cand[min(lab[t], nlist - 1)];  // list position -> centroid
     int nc = 1;
 #pragma unroll
     for (int k = 1; k < 4; ++k) nc += (key[t][k] - k1v <= W) ? 1 : 0;
@@ -393,12 +619,12 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) 
   uint64_t mvb[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    const int n_mine = tok0 + 32 * t + col;
+    const int n_mine = tokn[t];
     uint64_t todo = ballot(half == 0 && n_mine < N && ncand[t] > 1);
     while (todo) {
       const int src = __builtin_ctzll(todo);
       todo &= todo - 1;
-      const int n = tok0 + 32 * t + src;
+      const int n = __shfl(n_mine, src, SV_WAVE);
       const int nc = __shfl(ncand[t], src, SV_WAVE);
       float best = 0.f;
       int bidx = -1;
@@ -412,8 +638,9 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) 
         const uint32_t c1 = __float_as_uint(__shfl(key[t][1], src, SV_WAVE)) & imask;
         const uint32_t c2 = __float_as_uint(__shfl(key[t][2], src, SV_WAVE)) & imask;
         int c = (int)(grp == 0 ? c0 : grp == 1 ? c1 : c2);
-        const bool live = grp < nc && c < C;
+        const bool live = grp < nc && c < (PRUNE ? nlist : C);
         if (!live) c = 0;
+        if constexpr (PRUNE) c = s_cand[c];  // list position -> centroid
         const float* cr = cb + (size_t)c * D + gl * EPG;
         float part = 0.f;
 #pragma unroll
@@ -1103,8 +1330,12 @@ __global__ void __launch_bounds__(256) km_delta_kernel(const T* __restrict__ x, 
 // ---------------------------------------------------------------- host side
 struct KmPlan {
   int BH, Cpad, ib, ntiles, maxch;
-  size_t off_ops, off_nmax, off_counts, off_cs, off_partial, off_pfx, off_fx, off_fxcnt, off_moved, off_mtot, off_r2max, total;
+  size_t off_ops, off_nmax, off_counts, off_cs, off_partial, off_pfx, off_fx, off_fxcnt, off_moved, off_mtot, off_r2max;
+  size_t off_cnorm, off_lb, total;
+  bool prune;  // candidate pruning in the tracking rounds (bf16 tokens only)
+  int ibp;     // key index bits of the pruned assign (list positions < Cpad + 32)
 };
+
 
 static KmPlan km_plan(int B, int H, int N, int D, int C) {
   KmPlan p;
@@ -1126,6 +1357,10 @@ static KmPlan km_plan(int B, int H, int N, int D, int C) {
   p.off_moved = cv.used; cv.take<int2>((size_t)p.BH * KM_MSLOTS * km_mcap(N));
   p.off_mtot = cv.used; cv.take<int32_t>((size_t)p.BH * KM_MSLOTS);
   p.off_r2max = cv.used; cv.take<uint32_t>((size_t)p.BH * KM_MSLOTS);
+  p.prune = C >= KM_PRUNE_MIN_C && C <= KM_PRUNE_MAX_C;
+  p.ibp = bit_length((unsigned)(p.Cpad + 31));
+  p.off_cnorm = cv.used; if (p.prune) cv.take<float>((size_t)p.BH * p.Cpad);
+  p.off_lb = cv.used; if (p.prune) cv.take<float>((size_t)p.BH * C * C);
   p.total = cv.used;
   return p;
 }
@@ -1164,6 +1399,16 @@ static void launch_partial_sq(const void* x, const int32_t* perm, const int32_t*
                      cs, N, C, MEAN_ROWS, maxch, partial, (T*)nullptr, means);
 }
 
+// The pruned assign exists for bf16 tokens only.
+template <typename T, int D>
+static void launch_assign_pruned(const void* x, const bf16* ops, const uint32_t* nmax, const float* cent, int N,
+                                 int C, int Cpad, int ib, int32_t* labels, int2* moved, int32_t* mtot,
+                                 const int32_t* perm, const float* lb, int BH, hipStream_t st) {
+  if constexpr (sizeof(T) == 2)
+    hipLaunchKernelGGL((km_assign_kernel<T, D, true>), dim3(cdiv(N, KM_TOK_WG), BH), dim3(256), 0, st, (const T*)x,
+                       ops, nmax, cent, N, C, Cpad, ib, labels, moved, mtot, nullptr, perm, lb);
+}
+
 template <typename T, int D>
 static svgear_status kmeans_impl(const void* x, int BH, int N, int C, int iters, float* cent, int32_t* labels,
                                  int32_t* perm, int32_t* offsets, char* ws, const KmPlan& p, hipStream_t st) {
@@ -1178,6 +1423,10 @@ static svgear_status kmeans_impl(const void* x, int BH, int N, int C, int iters,
   int2* moved = reinterpret_cast<int2*>(ws + p.off_moved);
   int32_t* mtot = reinterpret_cast<int32_t*>(ws + p.off_mtot);
   uint32_t* r2max = reinterpret_cast<uint32_t*>(ws + p.off_r2max);
+  float* cnorm = reinterpret_cast<float*>(ws + p.off_cnorm);
+  float* lb = reinterpret_cast<float*>(ws + p.off_lb);
+  // candidate pruning of the tracking rounds (bf16 tokens, a few hundred centroids or more)
+  const bool prune = p.prune && sizeof(T) == 2;
   // The first KM_FULL_ROUNDS updates recompute every sum from the sorted
   // tokens (the first rounds move many tokens); the last of them leaves
   // exact fixed-point sums, and every later round updates those from the
@@ -1201,11 +1450,19 @@ static svgear_status kmeans_impl(const void* x, int BH, int N, int C, int iters,
   for (int it = 0; it < iters; ++it) {
     const bool track = it >= nfull;             // incremental round
     const bool setup = incr && it == nfull - 1;  // full round that sets up the fixed-point sums
+    const bool pr = prune && track;
+    if (pr) sort_labels();  // the tokens in the order of their current labels
     hipLaunchKernelGGL((km_prep_kernel<D>), dim3(cdiv(p.Cpad, KM_PREP_ROWS), BH), dim3(256), 0, st, cent, C, p.Cpad,
-                       ops, nmax, track ? mtot : nullptr);
-    hipLaunchKernelGGL((km_assign_kernel<T, D>), dim3(cdiv(N, KM_TOK_WG), BH), dim3(256), 0, st, (const T*)x, ops,
-                       nmax, cent, N, C, p.Cpad, p.ib, labels, track ? moved : nullptr, mtot,
-                       setup ? r2max : nullptr);
+                       ops, nmax, track ? mtot : nullptr, pr ? cnorm : nullptr);
+    if (pr) {
+      const int nt = p.Cpad / 32;
+      hipLaunchKernelGGL((km_cc_kernel<D>), dim3(cdiv(nt * nt, 4), BH), dim3(256), 0, st, ops, cnorm, C, p.Cpad, lb);
+      launch_assign_pruned<T, D>(x, ops, nmax, cent, N, C, p.Cpad, p.ibp, labels, moved, mtot, perm, lb, BH, st);
+    } else {
+      hipLaunchKernelGGL((km_assign_kernel<T, D>), dim3(cdiv(N, KM_TOK_WG), BH), dim3(256), 0, st, (const T*)x, ops,
+                         nmax, cent, N, C, p.Cpad, p.ib, labels, track ? moved : nullptr, mtot,
+                         setup ? r2max : nullptr, nullptr, nullptr);
+    }
     if (track) {
       hipLaunchKernelGGL((km_delta_kernel<T, D>), dim3(cdiv(C, kcl), BH), dim3(256), 0, st, (const T*)x, moved, mtot,
                          r2max, N, C, kcl, fx, fxcnt, cent, nmax);

@@ -135,6 +135,41 @@ def test_kmeans_multi_round_matches_lloyd(sv, name):
         assert (np.abs(cent[h] - mu).max(axis=1)[full] <= mean_bound(X[h], po, oo)[full] + 1e-6).all()
 
 
+@pytest.mark.parametrize("D,C,N", [(128, 300, 12000), (64, 256, 9000), (128, 1024, 20000)])
+def test_kmeans_pruned_rounds_match_lloyd(sv, D, C, N):
+    """From the fourth round on, bf16 k-means with a few hundred centroids or
+    more assigns each workgroup's tokens only against the centroids that the
+    triangle inequality leaves possible (the assignment step itself is
+    unchanged: the nearest centroid, SVG2 summary, "Semantic-Aware
+    Permutation via k-Means Clustering").  Eight rounds against the oracle's
+    Lloyd iterates with the first-divergence near-tie rule, and the centroids
+    as the means of the returned labels."""
+    w = scaled(WORKLOADS["tiny"], B=1, H=1, N=N, D=D, dtype="bf16", comps=C // 2, zipf=1.1, Cq=16, Ck=C,
+               seed=5, density=0.3)
+    x = layer_inputs(w)
+    X, C0 = x["k"][0], x["ck0"][0]
+    xd = to_dev(X.reshape(1, 1, N, D), "bf16")
+
+    def run(r):
+        cent = f32(C0.reshape(1, 1, C, D))
+        lab, _, _ = sv.kmeans(xd, cent, r)
+        return host(lab).reshape(-1), host(cent).reshape(C, D)
+
+    lab, cent = run(8)
+    Co, lo = orc.lloyd(X, C0, 8)
+    if (lab == lo).all():
+        po, oo = orc.permute(lo, C)
+        assert (np.abs(cent - Co).max(axis=1) <= mean_bound(X, po, oo) + 1e-6).all()
+        return
+    r, n = first_divergence(lambda rr: run(rr)[0], X, C0, 8)
+    assert r is not None, "final labels differ although every round agreed"
+    print(f"pruned k-means D={D} C={C}: labels first differ in round {r} at {n} near ties")
+    po, oo = orc.permute(lab, C)
+    full = np.diff(oo) > 0
+    mu = orc.means(X, po, oo)
+    assert (np.abs(cent - mu).max(axis=1)[full] <= mean_bound(X, po, oo)[full] + 1e-6).all()
+
+
 def test_kmeans_empty_cluster_keeps_centroid(sv):
     w, x = make("bf16-d64")
     X = x["q"]
