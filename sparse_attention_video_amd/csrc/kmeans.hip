@@ -202,7 +202,8 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) 
                                                         const float* __restrict__ cent, int N, int C, int Cpad, int ib,
                                                         int32_t* __restrict__ labels, int2* __restrict__ moved,
                                                         int32_t* __restrict__ mtot, uint32_t* __restrict__ r2max,
-                                                        const int32_t* __restrict__ perm, const float* __restrict__ lb) {
+                                                        const int32_t* __restrict__ perm, const float* __restrict__ lb,
+                                                        const int32_t* __restrict__ slab, int32_t* __restrict__ slab_new) {
   constexpr bool F32 = sizeof(T) == 4;
   static_assert(!(PRUNE && F32), "candidate pruning is built for bf16 tokens");
   constexpr int KS = D / 16;
@@ -238,7 +239,11 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) 
   for (int t = 0; t < 2; ++t) {
     const int n = tokn[t];
     const bool ok = n < N;
-    lold[t] = (moved && ok && (PRUNE || half == 0)) ? labels[(size_t)bh * N + n] : -1;
+    // (PRUNE: labels in the sorted order, read by position)
+    if constexpr (PRUNE)
+      lold[t] = ok ? slab[(size_t)bh * N + tok0 + 32 * t + col] : -1;
+    else
+      lold[t] = (moved && ok && half == 0) ? labels[(size_t)bh * N + n] : -1;
     float part = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -318,8 +323,8 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) 
   if constexpr (PRUNE) {
     // labels of the workgroup's tokens span a_lo .. a_hi (sorted order)
     const int p0 = blockIdx.x * KM_TOK_WG, p1 = min(N, p0 + KM_TOK_WG) - 1;
-    a_lo = labels[(size_t)bh * N + perm[(size_t)bh * N + p0]];
-    a_hi = labels[(size_t)bh * N + perm[(size_t)bh * N + p1]];
+    a_lo = slab[(size_t)bh * N + p0];
+    a_hi = slab[(size_t)bh * N + p1];
     const bool narrow = a_hi - a_lo < 64;
     s_r2[tid] = 0u;
     __syncthreads();
@@ -697,7 +702,12 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) 
       mvb[t] = ballot(lo != lnew);
       mv[t] = make_int2(n_mine, lo | (lnew << 16));
     }
-    if (mine) labels[(size_t)bh * N + n_mine] = lnew;
+    if (mine) {
+      if constexpr (PRUNE)
+        slab_new[(size_t)bh * N + tok0 + 32 * t + col] = lnew;  // by position (the sorted order)
+      else
+        labels[(size_t)bh * N + n_mine] = lnew;
+    }
   }
   if (moved) {
     // one reservation per wave in its sub-list; the order of the list is
@@ -885,11 +895,16 @@ __global__ void __launch_bounds__(1024) km_scan_kernel(int32_t* __restrict__ cou
 // --------------------------------------------------------------------------
 constexpr int KM_SCATTER_CPT = SVGEAR_MAX_CLUSTERS / 256;  // clusters per thread in the tile scan
 
-inline size_t km_scatter_lds(int C) { return (size_t)(5 * C + 2 * SORT_TILE) * sizeof(int32_t); }
+inline size_t km_scatter_lds(int C) { return (size_t)(5 * C + 3 * SORT_TILE) * sizeof(int32_t); }
 
+// With src_map, perm gets src_map[n] instead of n (regrouping a permuted
+// order: n is then a position of it); with slab_out, the labels in the new
+// order as well.
 __global__ void __launch_bounds__(256) km_scatter_kernel(const int32_t* __restrict__ labels,
                                                          const int32_t* __restrict__ tile_base, int N, int C,
-                                                         int ntiles, int ib, int32_t* __restrict__ perm) {
+                                                         int ntiles, int ib, int32_t* __restrict__ perm,
+                                                         const int32_t* __restrict__ src_map,
+                                                         int32_t* __restrict__ slab_out) {
   // [4][C] per-wave bases inside the tile | [C] tile position -> perm index
   // shift per cluster | [SORT_TILE] tokens and [SORT_TILE] destinations in
   // cluster order
@@ -898,6 +913,7 @@ __global__ void __launch_bounds__(256) km_scatter_kernel(const int32_t* __restri
   int32_t* shift = hw + 4 * C;
   int32_t* s_tok = shift + C;
   int32_t* s_dst = s_tok + SORT_TILE;
+  int32_t* s_lab = s_dst + SORT_TILE;
   const int bh = blockIdx.y, tile = blockIdx.x, lane = lane_id(), w = wave_id();
   const int32_t* lb = labels + (size_t)bh * N;
   int32_t* pb = perm + (size_t)bh * N;
@@ -980,6 +996,7 @@ __global__ void __launch_bounds__(256) km_scatter_kernel(const int32_t* __restri
       const int pos = mine[lab] + rank;
       s_tok[pos] = n;
       s_dst[pos] = pos + shift[lab];
+      s_lab[pos] = lab;
       if (rank == 0) mine[lab] = pos + (rk[i] >> 8);
     }
   }
@@ -989,7 +1006,11 @@ __global__ void __launch_bounds__(256) km_scatter_kernel(const int32_t* __restri
 #pragma unroll
   for (int r = 0; r < PER; ++r) {
     const int i = threadIdx.x + 256 * r;
-    if (i < nt) pb[s_dst[i]] = s_tok[i];
+    if (i < nt) {
+      const int v = s_tok[i];
+      pb[s_dst[i]] = src_map ? src_map[(size_t)bh * N + v] : v;
+      if (slab_out) slab_out[(size_t)bh * N + s_dst[i]] = s_lab[i];
+    }
   }
 }
 
@@ -1331,7 +1352,7 @@ __global__ void __launch_bounds__(256) km_delta_kernel(const T* __restrict__ x, 
 struct KmPlan {
   int BH, Cpad, ib, ntiles, maxch;
   size_t off_ops, off_nmax, off_counts, off_cs, off_partial, off_pfx, off_fx, off_fxcnt, off_moved, off_mtot, off_r2max;
-  size_t off_cnorm, off_lb, total;
+  size_t off_cnorm, off_lb, off_slab, off_slab2, off_perm2, total;
   bool prune;  // candidate pruning in the tracking rounds (bf16 tokens only)
   int ibp;     // key index bits of the pruned assign (list positions < Cpad + 32)
 };
@@ -1361,6 +1382,9 @@ static KmPlan km_plan(int B, int H, int N, int D, int C) {
   p.ibp = bit_length((unsigned)(p.Cpad + 31));
   p.off_cnorm = cv.used; if (p.prune) cv.take<float>((size_t)p.BH * p.Cpad);
   p.off_lb = cv.used; if (p.prune) cv.take<float>((size_t)p.BH * C * C);
+  p.off_slab = cv.used; if (p.prune) cv.take<int32_t>((size_t)p.BH * N);
+  p.off_slab2 = cv.used; if (p.prune) cv.take<int32_t>((size_t)p.BH * N);
+  p.off_perm2 = cv.used; if (p.prune) cv.take<int32_t>((size_t)p.BH * N);
   p.total = cv.used;
   return p;
 }
@@ -1403,10 +1427,18 @@ static void launch_partial_sq(const void* x, const int32_t* perm, const int32_t*
 template <typename T, int D>
 static void launch_assign_pruned(const void* x, const bf16* ops, const uint32_t* nmax, const float* cent, int N,
                                  int C, int Cpad, int ib, int32_t* labels, int2* moved, int32_t* mtot,
-                                 const int32_t* perm, const float* lb, int BH, hipStream_t st) {
+                                 const int32_t* perm, const float* lb, int32_t* slab, int BH, hipStream_t st) {
   if constexpr (sizeof(T) == 2)
     hipLaunchKernelGGL((km_assign_kernel<T, D, true>), dim3(cdiv(N, KM_TOK_WG), BH), dim3(256), 0, st, (const T*)x,
-                       ops, nmax, cent, N, C, Cpad, ib, labels, moved, mtot, nullptr, perm, lb);
+                       ops, nmax, cent, N, C, Cpad, ib, labels, moved, mtot, nullptr, perm, lb, slab, slab);
+}
+
+// labels[order[p]] = lab_by_pos[p]: token-order labels from an order grouped by label
+__global__ void __launch_bounds__(256) km_unsort_kernel(const int32_t* __restrict__ order,
+                                                        const int32_t* __restrict__ lab_by_pos, int N,
+                                                        int32_t* __restrict__ labels) {
+  const int bh = blockIdx.y, q = blockIdx.x * 256 + threadIdx.x;
+  if (q < N) labels[(size_t)bh * N + order[(size_t)bh * N + q]] = lab_by_pos[(size_t)bh * N + q];
 }
 
 template <typename T, int D>
@@ -1425,6 +1457,14 @@ static svgear_status kmeans_impl(const void* x, int BH, int N, int C, int iters,
   uint32_t* r2max = reinterpret_cast<uint32_t*>(ws + p.off_r2max);
   float* cnorm = reinterpret_cast<float*>(ws + p.off_cnorm);
   float* lb = reinterpret_cast<float*>(ws + p.off_lb);
+  // pruned rounds keep the tokens in an order grouped by label: pc[q] is the
+  // token at position q and sc[q] its label; each round updates sc in place
+  // and the next regroups (pc, sc) by it into the other pair of buffers
+  int32_t* pc = perm;
+  int32_t* sc = reinterpret_cast<int32_t*>(ws + p.off_slab);
+  int32_t* pn = reinterpret_cast<int32_t*>(ws + p.off_perm2);
+  int32_t* sn = reinterpret_cast<int32_t*>(ws + p.off_slab2);
+  bool grouped = false;
   // candidate pruning of the tracking rounds (bf16 tokens, a few hundred centroids or more)
   const bool prune = p.prune && sizeof(T) == 2;
   // The first KM_FULL_ROUNDS updates recompute every sum from the sorted
@@ -1445,23 +1485,36 @@ static svgear_status kmeans_impl(const void* x, int BH, int N, int C, int iters,
     hipLaunchKernelGGL(km_scan_kernel, dim3(BH), dim3(1024), 0, st, counts, N, C, p.ntiles, MEAN_ROWS, offsets, cs,
                        nmax);
     hipLaunchKernelGGL(km_scatter_kernel, dim3(p.ntiles, BH), dim3(256), km_scatter_lds(C), st, labels, counts, N,
-                       C, p.ntiles, p.ib, perm);
+                       C, p.ntiles, p.ib, perm, nullptr, nullptr);
   };
   for (int it = 0; it < iters; ++it) {
     const bool track = it >= nfull;             // incremental round
     const bool setup = incr && it == nfull - 1;  // full round that sets up the fixed-point sums
     const bool pr = prune && track;
-    if (pr) sort_labels();  // the tokens in the order of their current labels
+    if (pr) {
+      // the tokens grouped by their current labels, with those labels by position
+      const int32_t* src = grouped ? sc : labels;
+      hipLaunchKernelGGL(km_hist_kernel, dim3(p.ntiles, BH), dim3(256), 0, st, src, N, C, p.ntiles, counts);
+      hipLaunchKernelGGL(km_scan_kernel, dim3(BH), dim3(1024), 0, st, counts, N, C, p.ntiles, MEAN_ROWS, offsets,
+                         cs, nmax);
+      hipLaunchKernelGGL(km_scatter_kernel, dim3(p.ntiles, BH), dim3(256), km_scatter_lds(C), st, src, counts, N,
+                         C, p.ntiles, p.ib, grouped ? pn : pc, grouped ? pc : nullptr, grouped ? sn : sc);
+      if (grouped) {
+        std::swap(pc, pn);
+        std::swap(sc, sn);
+      }
+      grouped = true;
+    }
     hipLaunchKernelGGL((km_prep_kernel<D>), dim3(cdiv(p.Cpad, KM_PREP_ROWS), BH), dim3(256), 0, st, cent, C, p.Cpad,
                        ops, nmax, track ? mtot : nullptr, pr ? cnorm : nullptr);
     if (pr) {
       const int nt = p.Cpad / 32;
       hipLaunchKernelGGL((km_cc_kernel<D>), dim3(cdiv(nt * nt, 4), BH), dim3(256), 0, st, ops, cnorm, C, p.Cpad, lb);
-      launch_assign_pruned<T, D>(x, ops, nmax, cent, N, C, p.Cpad, p.ibp, labels, moved, mtot, perm, lb, BH, st);
+      launch_assign_pruned<T, D>(x, ops, nmax, cent, N, C, p.Cpad, p.ibp, labels, moved, mtot, pc, lb, sc, BH, st);
     } else {
       hipLaunchKernelGGL((km_assign_kernel<T, D>), dim3(cdiv(N, KM_TOK_WG), BH), dim3(256), 0, st, (const T*)x, ops,
                          nmax, cent, N, C, p.Cpad, p.ib, labels, track ? moved : nullptr, mtot,
-                         setup ? r2max : nullptr, nullptr, nullptr);
+                         setup ? r2max : nullptr, nullptr, nullptr, nullptr, nullptr);
     }
     if (track) {
       hipLaunchKernelGGL((km_delta_kernel<T, D>), dim3(cdiv(C, kcl), BH), dim3(256), 0, st, (const T*)x, moved, mtot,
@@ -1478,6 +1531,8 @@ static svgear_status kmeans_impl(const void* x, int BH, int N, int C, int iters,
       launch_finalize(partial, offsets, cs, BH, C, D, p.maxch, cent, 1, st);
     }
   }
+  if (grouped)  // the last labels back in token order
+    hipLaunchKernelGGL(km_unsort_kernel, dim3(cdiv(N, 256), BH), dim3(256), 0, st, pc, sc, N, labels);
   if (incr) sort_labels();  // perm and offsets of the last labels
   return check_launch("svgear_kmeans");
 }
