@@ -467,6 +467,54 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) 
       key[1][0] = minkey(key[1][0], k1);
     }
   };
+  // PRUNE: only keys within the tie window of a token's final best key k are
+  // ever used (the label, the refinement candidates, their count).  With kb
+  // the token's best key so far (both halves), k <= kb, and the window
+  // W(k) = 2 E0 + 2.5 q (2 k + 2 E0 + 1) grows with k, so an estimate V >
+  // thr = (kb + W(kb)) (1 + 4 q) gives a key (V with its low ib bits replaced,
+  // > V (1 - q)) above k + W(k) with room for the fp32 roundings: it cannot
+  // enter the window.  A tile whose 16 estimates lie above thr in every lane
+  // of the wave leaves the windowed part of the lists unchanged, and after
+  // chunk 0 (the own labels) that is the common case, so its insertion is
+  // skipped.
+  float thr[2] = {INFINITY, INFINITY};
+  auto set_thr = [&](int t) {
+    const float kb = fminf(key[t][0], shfl_xor(key[t][0], 32));
+    const float W = 2.f * E0[t] + q * (2.f * kb + 2.f * E0[t] + 1.f) * 2.5f;
+    thr[t] = (kb + W) * (1.f + 4.f * q);
+  };
+  auto keys_win = [&](int c0, const f32x16& acc0, const f32x16& acc1) {
+    float m0 = acc0[0], m1 = acc1[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) {
+      m0 = fminf(m0, acc0[r]);
+      m1 = fminf(m1, acc1[r]);
+    }
+    if (ballot(m0 <= thr[0])) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t idx = (uint32_t)(c0 + c_row(r, half));
+        const float k0 = __uint_as_float((__float_as_uint(acc0[r]) & ~imask) | idx);
+        key[0][3] = med3f(key[0][2], key[0][3], k0);
+        key[0][2] = med3f(key[0][1], key[0][2], k0);
+        key[0][1] = med3f(key[0][0], key[0][1], k0);
+        key[0][0] = minkey(key[0][0], k0);
+      }
+      set_thr(0);
+    }
+    if (ballot(m1 <= thr[1])) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t idx = (uint32_t)(c0 + c_row(r, half));
+        const float k1 = __uint_as_float((__float_as_uint(acc1[r]) & ~imask) | idx);
+        key[1][3] = med3f(key[1][2], key[1][3], k1);
+        key[1][2] = med3f(key[1][1], key[1][2], k1);
+        key[1][1] = med3f(key[1][0], key[1][1], k1);
+        key[1][0] = minkey(key[1][0], k1);
+      }
+      set_thr(1);
+    }
+  };
   int ci0 = 0;
   if constexpr (PRUNE) {
     if (nfirst > 0) {
@@ -550,6 +598,8 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) 
           acc1[r] = FLT_MAX;
         }
       keys(0, acc0, acc1);
+      set_thr(0);
+      set_thr(1);
       if (nlist > 32) staged();
       __syncthreads();
       ci0 = 1;
@@ -562,7 +612,7 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) 
     if (more) stage((ci + 1) * 32, buf ^ 1);
     f32x16 acc0, acc1;
     mma(buf, acc0, acc1);
-    if (PRUNE && ci * 32 + 32 > nlist) {
+    if (PRUNE && ci * 32 + 32 > nlist) [[unlikely]] {
       // list positions past the last candidate (padding) never enter a list
 #pragma unroll
       for (int r = 0; r < 16; ++r)
@@ -571,7 +621,10 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) 
           acc1[r] = FLT_MAX;
         }
     }
-    keys(ci * 32, acc0, acc1);
+    if constexpr (PRUNE)
+      keys_win(ci * 32, acc0, acc1);
+    else
+      keys(ci * 32, acc0, acc1);
     if (more) staged();
     __syncthreads();
   }
