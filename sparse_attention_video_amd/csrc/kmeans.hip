@@ -801,9 +801,19 @@ __global__ void __launch_bounds__(256) km_hist_kernel(const int32_t* __restrict_
     const int n = n0 + threadIdx.x + 256 * i;
     lab[i] = n < n1 ? lb[n] : -1;
   }
+  // a wave's 64 labels of a step are consecutive tokens: each run of equal
+  // labels adds its length once (labels grouped by value give few runs)
+  const int lane = lane_id();
 #pragma unroll
-  for (int i = 0; i < PER; ++i)
-    if (lab[i] >= 0) atomicAdd(&h[lab[i]], 1);
+  for (int i = 0; i < PER; ++i) {
+    const int l = lab[i];
+    const int prev = __shfl_up(l, 1, SV_WAVE);
+    const bool head = lane == 0 || prev != l;
+    const uint64_t heads = ballot(head);
+    const uint64_t later = heads & ~((2ull << lane) - 1ull);  // (lane 63: 2 << 63 wraps to 0)
+    const int len = (lane == 63 || later == 0ull ? 64 : __builtin_ctzll(later)) - lane;
+    if (head && l >= 0) atomicAdd(&h[l], len);
+  }
   __syncthreads();
   int32_t* cnt = counts + ((size_t)bh * ntiles + tile) * C;
   for (int c = threadIdx.x; c < C; c += 256) cnt[c] = h[c];
@@ -1051,14 +1061,26 @@ __global__ void __launch_bounds__(256) km_scatter_kernel(const int32_t* __restri
   __syncthreads();
   const int nt = min(N - tile * SORT_TILE, SORT_TILE);
   constexpr int PER = SORT_TILE / 256;
+  // every source read is issued before the first store (clamped entries
+  // past the tile's end are read and not stored)
+  int tv[PER], dv[PER];
 #pragma unroll
   for (int r = 0; r < PER; ++r) {
-    const int i = threadIdx.x + 256 * r;
-    if (i < nt) {
-      const int v = s_tok[i];
-      pb[s_dst[i]] = src_map ? src_map[(size_t)bh * N + v] : v;
-      if (slab_out) slab_out[(size_t)bh * N + s_dst[i]] = s_lab[i];
-    }
+    const int i = min(threadIdx.x + 256 * r, nt - 1);
+    tv[r] = s_tok[i];
+    dv[r] = s_dst[i];
+  }
+  if (src_map) {
+#pragma unroll
+    for (int r = 0; r < PER; ++r) tv[r] = src_map[(size_t)bh * N + tv[r]];
+  }
+#pragma unroll
+  for (int r = 0; r < PER; ++r)
+    if (threadIdx.x + 256 * r < nt) pb[dv[r]] = tv[r];
+  if (slab_out) {
+#pragma unroll
+    for (int r = 0; r < PER; ++r)
+      if (threadIdx.x + 256 * r < nt) slab_out[(size_t)bh * N + dv[r]] = s_lab[threadIdx.x + 256 * r];
   }
 }
 
