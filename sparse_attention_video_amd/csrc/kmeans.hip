@@ -191,7 +191,7 @@ __global__ void __launch_bounds__(256) km_cc_kernel(const bf16* __restrict__ ops
 // centroid is strictly farther from each such token than its c_a.  The list
 // of candidates (ascending, in LDS) replaces 0 .. C-1: chunk rows are
 // gathered from it and keys carry list positions, mapped back at the end.
-template <typename T, int D, bool PRUNE = false>
+template <typename T, int D, bool PRUNE = false, int CPT = 1>
 __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) km_assign_kernel(const T* __restrict__ x, const bf16* __restrict__ ops,
                                                         const uint32_t* __restrict__ nmax,
                                                         const float* __restrict__ cent, int N, int C, int Cpad, int ib,
@@ -230,6 +230,18 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) 
     const int pos = tok0 + 32 * t + col;
     tokn[t] = pos < N ? (PRUNE ? perm[(size_t)bh * N + pos] : pos) : N;
   }
+  if constexpr (!F32) {
+    // both tiles' rows are in flight before either is used (one memory
+    // latency, not two); a column past N reads row N - 1, whose results the
+    // kernel never stores (labels, moves and bounds skip such columns)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const size_t nr = (size_t)min(tokn[t], N - 1);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        bx[t][ks] = *reinterpret_cast<const bf16x8*>(xb + nr * D + 16 * ks + 8 * half);
+    }
+  }
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int n = tokn[t];
@@ -244,9 +256,7 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) 
     for (int ks = 0; ks < KS; ++ks) {
       const int d0 = 16 * ks + 8 * half;
       if constexpr (!F32) {
-        bf16x8 v = {};
-        if (ok) v = *reinterpret_cast<const bf16x8*>(xb + (size_t)n * D + d0);
-        bx[t][ks] = v;
+        const bf16x8 v = bx[t][ks];
 #pragma unroll
         for (int e = 0; e < 8; ++e) part += (float)v[e] * (float)v[e];
       } else {
@@ -309,11 +319,11 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) 
   // candidate list (PRUNE): positions 0 .. nlist-1 hold centroid indices
   // (chunk 0 reserves 32 positions for the own labels, so a list holds up
   // to C + 31 positions; the caller's ib covers them)
-  __shared__ int s_cand[PRUNE ? KM_PRUNE_MAX_C + 32 : 1];
+  __shared__ int s_cand[PRUNE ? 256 * CPT + 32 : 1];
   __shared__ uint32_t s_r2[PRUNE ? KM_TOK_WG : 1];
   __shared__ int s_pos[PRUNE ? 64 : 1];
   __shared__ int s_cnt[4];
-  __shared__ int s_cnt4[PRUNE ? KM_PRUNE_MAX_C / 256 : 1][4];
+  __shared__ int s_cnt4[PRUNE ? CPT : 1][4];
   int nlist = C, nfirst = 0, a_lo = 0, a_hi = 0;
   if constexpr (PRUNE) {
     // labels of the workgroup's tokens span a_lo .. a_hi (sorted order)
@@ -349,6 +359,17 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) 
       for (int q = C + tid; q < ((C + 31) & ~31); q += 256) s_cand[q] = s_cand[0];
     }
     __syncthreads();
+  }
+  // PRUNE: the bound rows of the first four own labels are read now, so their
+  // latency overlaps chunk 0's staging (the staging wait covers them too)
+  float lv0[4][PRUNE ? CPT : 1];
+  if constexpr (PRUNE) {
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const float* row = lb + ((size_t)bh * C + s_cand[jj < nfirst ? jj : 0]) * C;
+#pragma unroll
+      for (int u = 0; u < CPT; ++u) lv0[jj][u] = row[min(tid + 256 * u, C - 1)];
+    }
   }
   auto stage = [&](int c0, int buf) {
 #pragma unroll
@@ -543,7 +564,6 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) 
       // the other candidates, ascending, from position 32: thread tid tests
       // centroids tid + 256 u against the own labels, 4 labels' bound loads
       // in flight at a time
-      constexpr int CPT = KM_PRUNE_MAX_C / 256;
       bool keep[CPT];
 #pragma unroll
       for (int u = 0; u < CPT; ++u) keep[u] = false;
@@ -560,7 +580,7 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) 
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-          for (int u = 0; u < CPT; ++u) lv[jj][u] = lrow[jj][min(tid + 256 * u, C - 1)];
+          for (int u = 0; u < CPT; ++u) lv[jj][u] = i0 == 0 ? lv0[jj][u] : lrow[jj][min(tid + 256 * u, C - 1)];
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
@@ -1498,9 +1518,17 @@ template <typename T, int D>
 static void launch_assign_pruned(const void* x, const bf16* ops, const uint32_t* nmax, const float* cent, int N,
                                  int C, int Cpad, int ib, int32_t* labels, int2* moved, int32_t* mtot,
                                  const int32_t* perm, const float* lb, int32_t* slab, int BH, hipStream_t st) {
-  if constexpr (sizeof(T) == 2)
-    hipLaunchKernelGGL((km_assign_kernel<T, D, true>), dim3(cdiv(N, KM_TOK_WG), BH), dim3(256), 0, st, (const T*)x,
-                       ops, nmax, cent, N, C, Cpad, ib, labels, moved, mtot, nullptr, perm, lb, slab, slab);
+  // the candidate test takes CPT centroids per thread (C <= 256 CPT)
+  if constexpr (sizeof(T) == 2) {
+    if (C <= 512)
+      hipLaunchKernelGGL((km_assign_kernel<T, D, true, 2>), dim3(cdiv(N, KM_TOK_WG), BH), dim3(256), 0, st,
+                         (const T*)x, ops, nmax, cent, N, C, Cpad, ib, labels, moved, mtot, nullptr, perm, lb, slab,
+                         slab);
+    else
+      hipLaunchKernelGGL((km_assign_kernel<T, D, true, KM_PRUNE_MAX_C / 256>), dim3(cdiv(N, KM_TOK_WG), BH),
+                         dim3(256), 0, st, (const T*)x, ops, nmax, cent, N, C, Cpad, ib, labels, moved, mtot, nullptr,
+                         perm, lb, slab, slab);
+  }
 }
 
 // labels[order[p]] = lab_by_pos[p]: token-order labels from an order grouped by label
