@@ -225,10 +225,40 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) 
   float xx[2];
   int lold[2];  // previous labels (tracking rounds), loaded with the rows
   int tokn[2];  // token index of this lane's column of tile t (N: none)
+  // chunk staging straight from global memory into LDS (no registers): a
+  // chunk is 32 contiguous operand rows in global memory and 32 rows of
+  // stride SR in LDS.  Load j fills LDS bytes [1024 j, 1024 j + 1024) of the
+  // buffer, lane L the 16 bytes at o = 1024 j + 16 L: byte o % (2 SR) of row
+  // o / (2 SR).  Pad bytes (never read) take the chunk's first 16 bytes.
+  // The buffer form keeps the LDS-read waits of the products partial.
+  uint32_t goff[NJW];
+#pragma unroll
+  for (int k = 0; k < NJW; ++k) {
+    const int o = 1024 * (4 * k + w) + 16 * lane;
+    const int r = o / (2 * SR), cb = o - r * (2 * SR);
+    goff[k] = (o < CHB && cb < 2 * RW) ? (uint32_t)(r * 2 * RW + cb) : 0u;
+  }
+  const __amdgpu_buffer_rsrc_t rops =
+      __builtin_amdgcn_make_buffer_rsrc((void*)ob, (short)0, Cpad * RW * 2, 0x00020000);
+  // the largest centroid norm bound of the error window, read up front
+  const uint32_t nmax_bits = nmax[bh];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     const int pos = tok0 + 32 * t + col;
     tokn[t] = pos < N ? (PRUNE ? perm[(size_t)bh * N + pos] : pos) : N;
+  }
+  // previous labels (tracking rounds; PRUNE: by position in the sorted
+  // order), read unconditionally so that every path issues the same loads
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const bool ok = tokn[t] < N;
+    if constexpr (PRUNE) {
+      const int v = slab[(size_t)bh * N + min(tok0 + 32 * t + col, N - 1)];
+      lold[t] = ok ? v : -1;
+    } else {
+      const int v = labels[(size_t)bh * N + min(tokn[t], N - 1)];
+      lold[t] = (moved && ok && half == 0) ? v : -1;
+    }
   }
   if constexpr (!F32) {
     // both tiles' rows are in flight before either is used (one memory
@@ -246,11 +276,6 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) 
   for (int t = 0; t < 2; ++t) {
     const int n = tokn[t];
     const bool ok = n < N;
-    // (PRUNE: labels in the sorted order, read by position)
-    if constexpr (PRUNE)
-      lold[t] = ok ? slab[(size_t)bh * N + tok0 + 32 * t + col] : -1;
-    else
-      lold[t] = (moved && ok && half == 0) ? labels[(size_t)bh * N + n] : -1;
     float part = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -301,21 +326,6 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) 
 #pragma unroll
     for (int k = 0; k < 4; ++k) key[t][k] = FLT_MAX;
 
-  // chunk staging straight from global memory into LDS (no registers): a
-  // chunk is 32 contiguous operand rows in global memory and 32 rows of
-  // stride SR in LDS.  Load j fills LDS bytes [1024 j, 1024 j + 1024) of the
-  // buffer, lane L the 16 bytes at o = 1024 j + 16 L: byte o % (2 SR) of row
-  // o / (2 SR).  Pad bytes (never read) take the chunk's first 16 bytes.
-  // The buffer form keeps the LDS-read waits of the products partial.
-  uint32_t goff[NJW];
-#pragma unroll
-  for (int k = 0; k < NJW; ++k) {
-    const int o = 1024 * (4 * k + w) + 16 * lane;
-    const int r = o / (2 * SR), cb = o - r * (2 * SR);
-    goff[k] = (o < CHB && cb < 2 * RW) ? (uint32_t)(r * 2 * RW + cb) : 0u;
-  }
-  const __amdgpu_buffer_rsrc_t rops =
-      __builtin_amdgcn_make_buffer_rsrc((void*)ob, (short)0, Cpad * RW * 2, 0x00020000);
   // candidate list (PRUNE): positions 0 .. nlist-1 hold centroid indices
   // (chunk 0 reserves 32 positions for the own labels, so a list holds up
   // to C + 31 positions; the caller's ib covers them)
@@ -400,7 +410,7 @@ __global__ void __launch_bounds__(256, sizeof(T) == 2 ? (D == 128 ? 3 : 2) : 1) 
   stage(0, 0);
   staged();
   __syncthreads();
-  const float cm_pre = sqrtf(__uint_as_float(nmax[bh])) * (1.f + 1e-5f);
+  const float cm_pre = sqrtf(__uint_as_float(nmax_bits)) * (1.f + 1e-5f);
   float E0[2], off[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
