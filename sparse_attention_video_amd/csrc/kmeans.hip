@@ -1206,13 +1206,26 @@ __global__ void __launch_bounds__(256) km_partial_kernel(const T* __restrict__ x
       for (int e = 0; e < EPL; ++e) add(to_f32(tv[e]), e);
     }
   }
-  for (; p < r1; p += RPI) {
-    const int src = pb[p];
-    const u32x4 v = ld16(xb + (size_t)src * D + e0);
-    if constexpr (PERM) st16(xpb + (size_t)p * D + e0, v);
-    const T* tv = reinterpret_cast<const T*>(&v);
+  if (p < r1) {
+    // the last (fewer than 4) row steps, their loads in flight together:
+    // steps past r1 read row r1 - 1 again and are dropped
+    int src[4];
+    u32x4 v[4];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) add(to_f32(tv[e]), e);
+    for (int k = 0; k < 4; ++k) src[k] = pb[min(p + k * RPI, r1 - 1)];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = ld16(xb + (size_t)src[k] * D + e0);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      // every value is added (a dropped step adds one that contributes
+      // nothing), so no load can sink below the step's test
+      const bool ok = p + k * RPI < r1;
+      if constexpr (PERM)
+        if (ok) st16(xpb + (size_t)(p + k * RPI) * D + e0, v[k]);
+      const T* tv = reinterpret_cast<const T*>(&v[k]);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) add(ok ? to_f32(tv[e]) : (SQ ? mu[e] : 0.f), e);
+    }
   }
 #pragma unroll
   for (int e = 0; e < EPL; ++e) red[g * D + e0 + e] = acc[e];
@@ -1401,9 +1414,11 @@ __global__ void __launch_bounds__(256) km_delta_kernel(const T* __restrict__ x, 
       u32x4 v[UR];
 #pragma unroll
       for (int u = 0; u < UR; ++u) {
+        // every load is issued (an empty slot reads row 0, unused), so the
+        // UR rows are in flight together
         const int r = r0 + u * RPI + g;
         code[u] = r < nm ? s_m[r] : -1;
-        if (code[u] >= 0) v[u] = ld16(xb + (size_t)(code[u] & 0xffffff) * D + e0);
+        v[u] = ld16(xb + (size_t)(code[u] >= 0 ? code[u] & 0xffffff : 0) * D + e0);
       }
 #pragma unroll
       for (int u = 0; u < UR; ++u) {
