@@ -73,9 +73,9 @@ __global__ void __launch_bounds__(256) attn_kernel(const T* __restrict__ qp, con
   const int half = lane >> 5, col = lane & 31;
   const int32_t* ts = tstart + (size_t)bh * (Cq + 1);
   if ((int)blockIdx.x >= ts[Cq]) return;
-  if (tid == 0) sInfo[0] = upper_index(ts, Cq, blockIdx.x);
+  block_upper_index(ts, Cq, blockIdx.x, &sInfo[0]);
   __syncthreads();
-  const int ci = sInfo[0];
+  const int ci = min(max(sInfo[0], 0), Cq - 1);  // (in range even for a malformed table)
   const int32_t* qo = qoff + (size_t)bh * (Cq + 1);
   const int32_t* ko = koff + (size_t)bh * (Ck + 1);
   const int row0 = qo[ci] + ((int)blockIdx.x - ts[ci]) * AT_BM;
@@ -526,9 +526,9 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(const bf16* __restric
   if (bh >= BHn) return;
   const int32_t* ts = tstart + (size_t)bh * (Cq + 1);
   if (tile >= ts[Cq]) return;
-  if (tid == 0) sInfo[0] = upper_index(ts, Cq, tile);
+  block_upper_index(ts, Cq, tile, &sInfo[0]);
   __syncthreads();
-  const int ci = sInfo[0];
+  const int ci = min(max(sInfo[0], 0), Cq - 1);  // (in range even for a malformed table)
   const int32_t* qo = qoff + (size_t)bh * (Cq + 1);
   const int32_t* ko = koff + (size_t)bh * (Ck + 1);
   const int row0 = qo[ci] + (tile - ts[ci]) * AT_BM;

@@ -106,6 +106,17 @@ __device__ __forceinline__ float minkey(float a, float b) {
 }
 
 // Binary search: largest idx in [0, n) with starts[idx] <= v (starts[0] <= v assumed).
+// Workgroup form for starts in global memory, with starts[0] <= v <
+// starts[n]: exactly one i in [0, n) has starts[i] <= v < starts[i + 1]
+// (the last i with starts[i] <= v), and the thread that tests it writes it
+// to *out; every thread's loads are independent, so the lookup takes one
+// memory latency instead of log2 n.  The caller synchronises before reading
+// *out.
+__device__ __forceinline__ void block_upper_index(const int32_t* starts, int n, int v, int* out) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x)
+    if (starts[i] <= v && starts[i + 1] > v) *out = i;
+}
+
 __device__ __forceinline__ int upper_index(const int32_t* starts, int n, int v) {
   int lo = 0, hi = n - 1;
   while (lo < hi) {

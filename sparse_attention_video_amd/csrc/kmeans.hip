@@ -1162,9 +1162,9 @@ __global__ void __launch_bounds__(256) km_partial_kernel(const T* __restrict__ x
   const int bh = blockIdx.y, k = blockIdx.x;
   const int32_t* cs = chunk_start + (size_t)bh * (C + 1);
   if (k >= cs[C]) return;
-  if (threadIdx.x == 0) s_c = upper_index(cs, C, k);
+  block_upper_index(cs, C, k, &s_c);
   __syncthreads();
-  const int c = s_c;
+  const int c = min(max(s_c, 0), C - 1);  // (in range even for a malformed table)
   const int32_t* off = offsets + (size_t)bh * (C + 1);
   const int r0 = off[c] + (k - cs[c]) * rows;
   const int r1 = min(r0 + rows, off[c + 1]);
