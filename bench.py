@@ -34,9 +34,9 @@ METRIC = "ms per attention layer (cluster+route+sparse attn), 75.6k tok, 25% den
 # FETCH_SIZE / WRITE_SIZE calibrated against a 1 GiB device copy (FETCH x 2.0,
 # WRITE x 1.0); valid only for the attention source it was measured on.
 ATTN_TRAFFIC = {
-    "source_sha256": "121308afdd1ba5d3ba538f17214b64b3b30c4d719577a20c3ce6b0ada693ce0d",
+    "source_sha256": "6714f0ff0b7b000bfcee58c2919219f3f36ade41d3aaed1165a8e13cb20bf6ee",
     "workload": "wan",
-    "fetch_bytes": 41.72e9,
+    "fetch_bytes": 41.96e9,
     "write_bytes": 0.775e9,
 }
 PEAK_BF16_TFLOPS = 2500.0
