@@ -25,7 +25,7 @@ constexpr int KM_TOK_WG = 256;      // tokens per assign workgroup (4 waves x 64
 // candidate pruning of the tracking rounds pays from a few hundred centroids
 // on (its bound matrix is C x C per head)
 constexpr int KM_PRUNE_MIN_C = 256, KM_PRUNE_MAX_C = 1024;
-constexpr int SORT_TILE = 2048;     // tokens per histogram / scatter tile
+constexpr int SORT_TILE = 4096;     // tokens per histogram / scatter tile
 constexpr int MEAN_ROWS = 256;      // rows per segment-sum chunk
 constexpr float PAD_NORM = 1e30f;   // squared norm given to padding centroids
 constexpr int KM_PREP_ROWS = 32;    // centroid rows per prep workgroup
@@ -853,7 +853,7 @@ __global__ void __launch_bounds__(256) km_hist_kernel(const int32_t* __restrict_
 // scan: offsets (cluster starts), per-tile bases (in place over counts) and
 // the segment-sum chunk list.  One block of 1024 threads per (batch, head).
 // --------------------------------------------------------------------------
-constexpr int KM_SCAN_LDS = 32768;  // tile histograms of a head held in LDS (128 KB)
+constexpr int KM_SCAN_LDS = 16384;  // tile histograms of a head held in LDS (64 KB)
 
 __global__ void __launch_bounds__(1024) km_scan_kernel(int32_t* __restrict__ counts, int N, int C, int ntiles,
                                                        int rows, int32_t* __restrict__ offsets,
