@@ -135,7 +135,11 @@ def test_kmeans_multi_round_matches_lloyd(sv, name):
         assert (np.abs(cent[h] - mu).max(axis=1)[full] <= mean_bound(X[h], po, oo)[full] + 1e-6).all()
 
 
-@pytest.mark.parametrize("D,C,N", [(128, 300, 12000), (64, 256, 9000), (128, 1024, 20000)])
+# (the last three: ~3 tokens per cluster, so that workgroups span 64 or more
+# labels and take every centroid; ~8, around the 32-label limit of chunk 0;
+# a ragged size at D = 64)
+@pytest.mark.parametrize("D,C,N", [(128, 300, 12000), (64, 256, 9000), (128, 1024, 20000), (128, 1024, 3000),
+                                   (128, 512, 4096), (64, 300, 2500)])
 def test_kmeans_pruned_rounds_match_lloyd(sv, D, C, N):
     """From the fourth round on, bf16 k-means with a few hundred centroids or
     more assigns each workgroup's tokens only against the centroids that the
